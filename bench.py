@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the 3D-RoPE video-DiT attention layer on one MI355X.
+
+One step = one pass of the layer's hot path over one batch of synthetic
+inputs already resident in HBM: fused per-head RMSNorm + 3D-RoPE of q and k
+(vdit_rope_qk), then exact FULL softmax attention (vdit_attn_fwd), on the
+Wan-1.3B-shaped layer: latent grid 21 x 30 x 52 = 32760 tokens, 12 heads,
+head_dim 128, bf16, RoPE split 22/21/21 pairs.
+
+Prints ONE JSON line.  `value` is attention TFLOP/s over the whole step
+(matmul FLOPs 4 L^2 D H per layer; exps not counted).  `roofline` reports the
+attention kernel alone, timed with HIP events on the stream it runs on;
+`cpu_baseline` times the fp64 oracle on a bounded sample of query rows.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --workload N   (other workloads, for reference; one JSON line each)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "attention TFLOP/s and ms/layer on 1 MI355X (% of bf16 MFMA peak)"
+ATTN_SRC = os.path.join(ROOT, "video_diffusion_transformer_rmsnorm_amd", "csrc", "attn_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_wan13b_traffic.json")
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 --pmc summary,
+    or None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_rows: int, seed: int = 99):
+    """fp64 oracle on a bounded sample: rope over the whole grid (every key needs
+    it) plus attention of n_rows sampled query rows x all heads against all keys."""
+    import numpy as np
+    import oracle as O
+    import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v = WL.workload_inputs(w)
+    rows = WL.sample_rows(w.tokens, n_rows, seed)
+    t0 = time.perf_counter()
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    O.attention(wq[:, rows], wk, v.values)
+    dt = time.perf_counter() - t0
+    flops = WL.flops_full(len(rows), w.tokens, w.heads, w.head_dim)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} of {w.tokens} query rows x {w.heads} heads vs all {w.tokens} keys, "
+                      f"plus RMSNorm+RoPE of all tokens; {dt:.1f} s wall",
+            "seconds": dt}
+
+
+def bench_full(args):
+    import numpy as np
+    import torch
+    import video_diffusion_transformer_rmsnorm_amd as V
+    import workloads as WL
+
+    w = WL.WORKLOADS[2]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = WL.workload_inputs(w)
+
+    def up(t):
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    o = torch.empty_like(qd)
+    lse = torch.empty((1, w.heads, w.tokens), dtype=torch.float32, device=dev)
+    grid = V.make_grid(*w.grid, w.pairs)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        V.vdit_rope_qk(qd, kd, grid, q_out=qr, k_out=kr)
+        if ev is not None:
+            ev[1].record(stream)
+        V.vdit_attn_fwd(qr, kr, vd, o=o, lse=lse)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    flops = WL.flops_full(w.tokens, w.tokens, w.heads, w.head_dim)
+    rope_bytes = 2 * 2 * w.tokens * w.heads * w.head_dim * 2  # q,k read + write, bf16
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16 RNE)",
+        "config": {"workload": "wan1.3b_full_layer_21x30x52", "tokens": w.tokens, "heads": w.heads,
+                   "head_dim": w.head_dim, "rope_pairs": list(w.pairs), "mode": "full",
+                   "step": "rmsnorm+3d_rope(q,k) -> full attention", "parallelism": "none (1 GPU)"},
+        "attn_ms": round(attn_ms, 4),
+        "rope_ms": round(rope_ms, 4),
+        "pct_bf16_peak_step": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "rope_GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(), "kernel": "attn_mfma_kernel<128,2,4>",
+                     "algorithmic_flops_per_launch": flops},
+    }
+    return out, w
+
+
+def bench_other(args):
+    """Reference timings of the other workloads (not the headline line)."""
+    import numpy as np
+    import torch
+    import video_diffusion_transformer_rmsnorm_amd as V
+    import workloads as WL
+
+    w = WL.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = WL.workload_inputs(w)
+
+    def up(t):
+        if t.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(t.values.astype(np.float32)).to(dev)
+
+    qd, kd, vd = up(q), up(k), up(v)
+    grid = V.make_grid(*w.grid, w.pairs)
+    if w.mode == "ring":
+        q0, nq = w.q_range
+        qq = qd[:, q0:q0 + nq].contiguous()
+        kcs = [kd[:, s:s + n].contiguous() for s, n in w.kv_chunks]
+        vcs = [vd[:, s:s + n].contiguous() for s, n in w.kv_chunks]
+        flops = sum(WL.flops_full(nq, n, w.heads, w.head_dim) for _, n in w.kv_chunks)
+
+        def step():
+            V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs)
+    elif w.mode == "rolling":
+        kc = torch.zeros((w.n_slots, 1, w.tokens, w.kv_heads, w.head_dim), dtype=qd.dtype, device=dev)
+        vc = torch.zeros_like(kc)
+        for f in range(w.n_slots):
+            kc[f].copy_(kd[f:f + 1]); vc[f].copy_(vd[f:f + 1])
+        flops = WL.flops_full(w.tokens, w.tokens * w.n_slots, w.heads, w.head_dim)
+        frame = [w.n_slots]
+
+        def step():
+            f = frame[0]
+            V.vdit_rope_qk(qd[f % w.n_frames:f % w.n_frames + 1], None, grid, t_offset=f)
+            V.vdit_attn_fwd(qd[f % w.n_frames:f % w.n_frames + 1], kd[f % w.n_frames:f % w.n_frames + 1],
+                            vd[f % w.n_frames:f % w.n_frames + 1], mode="rolling", k_cache=kc, v_cache=vc, frame=f)
+            frame[0] += 1
+    elif w.mode == "hybrid":
+        s = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device=dev)
+        z = torch.zeros((1, w.kv_heads, w.head_dim), device=dev)
+        n_ch = WL.ceil_div(w.tokens, w.chunk_tokens)
+        flops = sum(WL.flops_full(min(w.chunk_tokens, w.tokens - c * w.chunk_tokens),
+                                  min(w.chunk_tokens, w.tokens - c * w.chunk_tokens), w.heads, w.head_dim)
+                    for c in range(n_ch))
+
+        def step():
+            s.zero_(); z.zero_()
+            V.vdit_attn_fwd(qd, kd, vd, mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=s, state_z=z)
+    else:
+        flops = WL.flops_full(w.tokens, w.tokens, w.heads, w.head_dim)
+
+        def step():
+            V.vdit_rope_qk(qd, kd, grid)
+            V.vdit_attn_fwd(qd, kd, vd)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic", "config": {"workload": w.name, "mode": w.mode, "reference_only": True}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="query rows of the oracle's timed sample")
+    ap.add_argument("--workload", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer's sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.workload != 2:
+        print(json.dumps(bench_other(args)), flush=True)
+        return
+    out, w = bench_full(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

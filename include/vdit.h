@@ -1,0 +1,213 @@
+/*
+ * vdit.h -- C ABI of a gfx950 (MI355X) library for the attention layer of
+ * Wan-style video diffusion transformers: per-head RMS-normalised queries and
+ * keys with channel-split 3D rotary position embedding, and exact multi-head
+ * softmax attention over a flattened T x H x W latent grid in four modes.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer unless marked (host).  The
+ *    caller owns all memory; the library never allocates or frees device
+ *    memory and keeps no global mutable state (thread-safe).
+ *  - Calls are asynchronous: they validate their arguments, enqueue kernels
+ *    on `stream` and return without synchronising.  A status of VDIT_OK
+ *    means "enqueued".
+ *  - Validation happens before any launch; a call that fails validation
+ *    writes nothing.  VDIT_ERR_INVALID_ARG: malformed arguments;
+ *    VDIT_ERR_UNSUPPORTED: well-formed but outside what the kernels handle
+ *    (for example head_dim other than 64 or 128); VDIT_ERR_HIP: a HIP call
+ *    or launch failed.  vdit_last_error() returns a message for the last
+ *    non-OK status of the calling thread.
+ *  - Tensors are row-major: q, k, v, o are [B, L, H, D] (D fastest);
+ *    log-sum-exp is [B, H, L] float32, natural log; an empty key set gives
+ *    LSE = -inf and O = 0.
+ *  - Device buffers must be 16-byte aligned.
+ *  - Element types: VDIT_BF16 (bfloat16, results rounded to nearest even) or
+ *    VDIT_F32.  Internal arithmetic is float32 in both cases.
+ */
+#ifndef VDIT_H
+#define VDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VDIT_ABI_VERSION 1
+
+typedef enum {
+  VDIT_OK = 0,
+  VDIT_ERR_INVALID_ARG = 1,
+  VDIT_ERR_UNSUPPORTED = 2,
+  VDIT_ERR_HIP = 3
+} vdit_status;
+
+typedef enum { VDIT_BF16 = 0, VDIT_F32 = 1 } vdit_dtype;
+
+/*
+ * Latent grid and rotary split.  Tokens are flattened t-major, then h, then
+ * w (FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder with
+ * Transformers, Sec. 3.1 writes latents as T' x H' x W').  The D/2 adjacent
+ * channel pairs (2p, 2p+1) are split in order into pairs_t, pairs_h, pairs_w
+ * pairs that rotate with the token's t, h and w coordinate respectively
+ * (3D-RoPE applied separately to the temporal and spatial axes, FlashDecoder
+ * Sec. 3.2 "Base Architecture").  Inside an axis block of P_a pairs, pair j
+ * has angular frequency theta^(-j / P_a) (RoFormer's 1D frequencies for a
+ * block of dimension 2 P_a).  pairs_t + pairs_h + pairs_w must equal
+ * head_dim / 2.
+ */
+typedef struct {
+  int32_t T, H, W;
+  int32_t pairs_t, pairs_h, pairs_w;
+  float theta; /* RoPE base, e.g. 10000 */
+} vdit_grid;
+
+/* vdit_rope_qk flags */
+#define VDIT_ROPE_NO_NORM 1u /* skip the RMSNorm, rotate only */
+
+/*
+ * vdit_rope_qk -- fused per-head RMSNorm + 3D-RoPE of queries and keys.
+ *
+ * For every token i of the slice, every head and both q and k:
+ *   y = x / sqrt(mean_d(x_d^2) + eps) * gain        (RMSNorm over head_dim,
+ *       Zhang & Sennrich, cited by FlashDecoder Sec. 3.2; skipped with
+ *       VDIT_ROPE_NO_NORM)
+ *   then each pair (y_2p, y_2p+1) is rotated by angle alpha = pos * omega_p:
+ *   (y0 cos a - y1 sin a, y0 sin a + y1 cos a).
+ * Token i has grid index n = token0 + i, so t = n / (H W) + t_offset,
+ * h = (n / W) mod H, w = n mod W.  t_offset lets a caller place a frame of a
+ * stream at any temporal position (FlashDecoder Sec. 4 "Long Video
+ * Decoding" assigns positions relative to the current window); angles are
+ * reduced in float64 so large positions keep full float32 accuracy.
+ *
+ * q_in, q_out: [B, L, n_heads, head_dim]; k_in, k_out: [B, L, n_kv_heads,
+ * head_dim]; dtype of all four.  q_out may equal q_in and k_out may equal
+ * k_in (in place); partial overlap is not allowed.  k_in/k_out may both be
+ * NULL (queries only) and likewise q_in/q_out.  q_gain, k_gain: [head_dim]
+ * float32 or NULL (gain 1).  eps >= 0.  grid (host) is read during the
+ * call only.  head_dim in {64, 128}; token0 + L <= T*H*W.
+ */
+vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                         int32_t B, int64_t L, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, vdit_dtype dtype, const vdit_grid* grid,
+                         int64_t token0, int64_t t_offset, const float* q_gain,
+                         const float* k_gain, float eps, uint32_t flags, hipStream_t stream);
+
+typedef enum {
+  VDIT_ATTN_FULL = 0,
+  VDIT_ATTN_RING = 1,
+  VDIT_ATTN_ROLLING = 2,
+  VDIT_ATTN_CHUNK_HYBRID = 3
+} vdit_attn_mode;
+
+/*
+ * Arguments of vdit_attn_fwd (host struct, read during the call only).
+ * Query head h reads key/value head h / (n_heads / n_kv_heads) (grouped-query
+ * attention, FlashDecoder Sec. 3.2).  Scores are s_ij = scale * q_i . k_j
+ * with scale <= 0 meaning 1/sqrt(head_dim).
+ *
+ * VDIT_ATTN_FULL: O = softmax(S) V over all Lkv keys, no mask.
+ *   q, o [B, Lq, n_heads, D]; k, v [B, Lkv, n_kv_heads, D]; lse optional.
+ *
+ * VDIT_ATTN_RING: one device's share of ring attention (ReGenVC:
+ *   End-to-End Real-Time Generative Video Coding at Ultra-Low Bitrate,
+ *   unified sequence parallelism paragraph): the key/value sequence arrives
+ *   as n_kv_chunks chunks, attended to in order; each chunk's partial is
+ *   folded into a float32 running partial in `workspace` with the
+ *   log-sum-exp merge of vdit_lse_merge, fused into the attention kernel's
+ *   epilogue, and the last chunk writes o (dtype) and lse.  k_chunks[c],
+ *   v_chunks[c] (host arrays of device pointers) are [B, chunk_len[c],
+ *   n_kv_heads, D]; chunk_len (host) must sum to Lkv; k and v are unused.
+ *   Equal to FULL over the concatenated chunks up to rounding order.
+ *
+ * VDIT_ATTN_ROLLING: frame-by-frame decode with a rolling KV cache of
+ *   n_slots frames (FlashDecoder Sec. 3.3).  k_cache, v_cache are
+ *   [n_slots, B, Lq, n_kv_heads, D]; frame f's keys/values live in slot
+ *   f mod n_slots.  If k and v are non-NULL they hold frame `frame`'s
+ *   [B, Lq, n_kv_heads, D] keys/values and are first copied into that slot;
+ *   if both are NULL the slot was already filled (for example by passing it
+ *   as k_out of vdit_rope_qk).  q (frame `frame`'s queries, Lq = tokens per
+ *   frame) then attends to the min(frame + 1, n_slots) most recent frames
+ *   with no mask; Lkv is ignored.  Rotating each frame once at insertion
+ *   with its absolute t gives the same scores as window-relative positions,
+ *   because rotary scores depend only on position differences.
+ *
+ * VDIT_ATTN_CHUNK_HYBRID: softmax attention inside chunks of chunk_tokens
+ *   tokens plus causal linear attention across chunks with running state
+ *   (MobileWan: Closing the Quality Gap for Mobile Video Diffusion, review
+ *   of Sec. 3.2).  Token i of chunk c gets
+ *     (sum_{j in c} e^{s_ij} v_j + phi(q_i)^T S_c) / (sum_{j in c} e^{s_ij} + phi(q_i)^T z_c)
+ *   with phi(x) = elu(x) + 1 on the (already normalised and rotated) q and k,
+ *   S_c = s_in + sum_{j before chunk c} phi(k_j) v_j^T, z_c = z_in + sum phi(k_j).
+ *   Self-attention: Lkv must equal Lq.  state_s [B, n_kv_heads, D, D] and
+ *   state_z [B, n_kv_heads, D] (float32) hold the incoming state (zero for a
+ *   new sequence) and receive the state after the last chunk, so calling
+ *   once per chunk equals one call over the whole sequence.  Needs
+ *   `workspace` of vdit_attn_workspace_bytes().
+ *
+ * lse: [B, n_heads, Lq] float32 or NULL.  o must not overlap q, k, v, the
+ * caches or the workspace.  workspace: device scratch of at least
+ * vdit_attn_workspace_bytes(args) bytes (may be NULL when that is 0);
+ * its contents need no initialisation and are clobbered.
+ */
+typedef struct {
+  int32_t mode;  /* vdit_attn_mode */
+  int32_t dtype; /* vdit_dtype of q, k, v, o, caches */
+  int32_t B, n_heads, n_kv_heads, head_dim;
+  int64_t Lq, Lkv;
+  float scale;
+  int32_t n_kv_chunks; /* RING */
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const void* const* k_chunks; /* RING (host array) */
+  const void* const* v_chunks; /* RING (host array) */
+  const int64_t* chunk_len;    /* RING (host array) */
+  void* k_cache;               /* ROLLING */
+  void* v_cache;               /* ROLLING */
+  int64_t frame;               /* ROLLING */
+  int32_t n_slots;             /* ROLLING */
+  int32_t reserved0;
+  int64_t chunk_tokens;        /* CHUNK_HYBRID */
+  float* state_s;              /* CHUNK_HYBRID */
+  float* state_z;              /* CHUNK_HYBRID */
+  void* workspace;
+  size_t workspace_bytes;
+} vdit_attn_args;
+
+/* Bytes of device workspace vdit_attn_fwd needs for these arguments
+ * (0 if none).  Returns (size_t)-1 for arguments that fail validation. */
+size_t vdit_attn_workspace_bytes(const vdit_attn_args* args /* host */);
+
+/* Enqueue one attention call (see vdit_attn_args).  head_dim in {64, 128}. */
+vdit_status vdit_attn_fwd(const vdit_attn_args* args /* host */, hipStream_t stream);
+
+/*
+ * vdit_lse_merge -- combine two attention partials over disjoint key sets:
+ *   L = ln(e^{L_a} + e^{L_b}),  O = e^{L_a - L} O_a + e^{L_b - L} O_b,
+ * the online-softmax combination of ring attention (ReGenVC, USP
+ * paragraph).  A partial with L = -inf has weight 0.  o_a, o_b: [B, L,
+ * n_heads, head_dim] of in_dtype; lse_a, lse_b: [B, n_heads, L] float32;
+ * o_out of out_dtype; lse_out may be NULL.  o_out may equal o_a (or o_b)
+ * when in_dtype == out_dtype, and lse_out may equal lse_a (or lse_b).
+ * head_dim in {64, 128}.
+ */
+vdit_status vdit_lse_merge(const void* o_a, const float* lse_a, const void* o_b,
+                           const float* lse_b, void* o_out, float* lse_out,
+                           vdit_dtype in_dtype, vdit_dtype out_dtype, int32_t B, int64_t L,
+                           int32_t n_heads, int32_t head_dim, hipStream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* vdit_last_error(void);
+
+/* VDIT_ABI_VERSION of the loaded library. */
+int32_t vdit_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VDIT_H */

@@ -1,0 +1,99 @@
+// Host-only test of the argument validation in validate.hpp (no HIP calls).
+// Built with g++ (optionally under AddressSanitizer / UBSan) by the CPU tests.
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "validate.hpp"
+
+using namespace vdit;
+
+static int failures = 0;
+#define EXPECT(cond, what)                                   \
+  do {                                                       \
+    if (!(cond)) {                                           \
+      std::printf("FAIL %s (line %d)\n", what, __LINE__);    \
+      ++failures;                                            \
+    }                                                        \
+  } while (0)
+
+static void* P(uintptr_t x) { return reinterpret_cast<void*>(x); }
+
+int main() {
+  GridArgs g{21, 30, 52, 22, 21, 21, 10000.f};
+  // good rope call
+  EXPECT(bool(check_rope(P(1ull << 30), P(2ull << 30), P(1ull << 30), P(2ull << 30), 1, 32760, 12, 12, 128, 0, &g, 0, 1e-6f)), "rope ok");
+  EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 10, 12, 12, 96, 0, &g, 0, 1e-6f).code == Check::unsupported, "head_dim 96 unsupported");
+  GridArgs bad = g; bad.pairs_w = 20;
+  EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 10, 12, 12, 128, 0, &bad, 0, 1e-6f).code == Check::invalid, "pair sum");
+  EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 10, 12, 12, 128, 0, nullptr, 0, 1e-6f).code == Check::invalid, "null grid");
+  EXPECT(check_rope(P(0x1001), nullptr, P(0x1001), nullptr, 1, 10, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "alignment");
+  EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 32761, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "beyond grid");
+  EXPECT(check_rope(P(0x1000), nullptr, P(0x1010), nullptr, 1, 10, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "partial overlap");
+  EXPECT(check_rope(P(0x1000), nullptr, nullptr, nullptr, 1, 10, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "q_out missing");
+  EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 10, 12, 12, 128, 0, &g, 0, -1.f).code == Check::invalid, "negative eps");
+
+  AttnArgs a{};
+  a.mode = 0; a.dtype = 0; a.B = 1; a.n_heads = 12; a.n_kv_heads = 12; a.head_dim = 128;
+  a.Lq = 100; a.Lkv = 100; a.q = P(1ull << 28); a.k = P(2ull << 28); a.v = P(3ull << 28); a.o = P(4ull << 28);
+  EXPECT(bool(check_attn(a)), "full ok");
+  AttnArgs b = a; b.n_kv_heads = 5;
+  EXPECT(check_attn(b).code == Check::invalid, "heads divisibility");
+  b = a; b.o = P((1ull << 28) + 0x100);
+  EXPECT(check_attn(b).code == Check::invalid, "o aliases q");
+  b = a; b.head_dim = 256;
+  EXPECT(check_attn(b).code == Check::unsupported, "head_dim 256");
+  b = a; b.mode = 7;
+  EXPECT(check_attn(b).code == Check::invalid, "mode");
+
+  // ring
+  const void* kc[2] = {P(5ull << 28), P(6ull << 28)};
+  const void* vc[2] = {P(7ull << 28), P(8ull << 28)};
+  int64_t lens[2] = {60, 40};
+  b = a; b.mode = 1; b.n_kv_chunks = 2; b.k_chunks = kc; b.v_chunks = vc; b.chunk_len = lens;
+  EXPECT(check_attn(b).code == Check::invalid, "ring workspace missing");
+  b.workspace = P(9ull << 28); b.workspace_bytes = ring_workspace_bytes(b);
+  EXPECT(bool(check_attn(b)), "ring ok");
+  lens[1] = 41;
+  EXPECT(check_attn(b).code == Check::invalid, "ring lengths must sum to Lkv");
+  lens[1] = 40;
+  b.workspace_bytes -= 1;
+  EXPECT(check_attn(b).code == Check::invalid, "ring workspace too small");
+
+  // rolling
+  b = a; b.mode = 2; b.n_slots = 5; b.frame = 3; b.k_cache = P(10ull << 28); b.v_cache = P(11ull << 28);
+  EXPECT(bool(check_attn(b)), "rolling ok");
+  b.n_slots = 0;
+  EXPECT(check_attn(b).code == Check::invalid, "rolling slots");
+  b.n_slots = 9;
+  EXPECT(check_attn(b).code == Check::unsupported, "rolling max slots");
+  b.n_slots = 5; b.frame = -1;
+  EXPECT(check_attn(b).code == Check::invalid, "rolling frame");
+  b.frame = 0; b.k = nullptr;
+  EXPECT(check_attn(b).code == Check::invalid, "rolling k/v pairing");
+
+  // hybrid
+  b = a; b.mode = 3; b.chunk_tokens = 30; b.state_s = reinterpret_cast<float*>(P(12ull << 28));
+  b.state_z = reinterpret_cast<float*>(P(13ull << 28));
+  EXPECT(check_attn(b).code == Check::invalid, "hybrid workspace missing");
+  b.workspace = P(14ull << 28); b.workspace_bytes = hybrid_layout(b).total;
+  EXPECT(bool(check_attn(b)), "hybrid ok");
+  HybridLayout hl = hybrid_layout(b);
+  EXPECT(hl.n_chunks == 4, "hybrid chunk count");
+  b.Lkv = 99;
+  EXPECT(check_attn(b).code == Check::invalid, "hybrid Lkv");
+  b.Lkv = 100; b.chunk_tokens = 0;
+  EXPECT(check_attn(b).code == Check::invalid, "hybrid chunk");
+
+  // merge
+  EXPECT(bool(check_merge(P(0x1000), (float*)P(0x2000), P(0x3000), (float*)P(0x4000), P(0x1000), (float*)P(0x2000), 0, 0, 1, 8, 2, 64)), "merge in place ok");
+  EXPECT(check_merge(P(0x1000), (float*)P(0x2000), P(0x3000), (float*)P(0x4000), P(0x1000), nullptr, 0, 1, 1, 8, 2, 64).code == Check::invalid, "merge in place dtype");
+  EXPECT(check_merge(P(0x1000), (float*)P(0x2000), P(0x3000), (float*)P(0x4000), P(0x1010), nullptr, 0, 0, 1, 8, 2, 64).code == Check::invalid, "merge partial overlap");
+
+  if (failures) {
+    std::printf("%d failures\n", failures);
+    return 1;
+  }
+  std::printf("validate_test ok\n");
+  return 0;
+}

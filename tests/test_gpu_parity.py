@@ -1,0 +1,392 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Inputs come from the seeded generators in ``workloads``; expected values from
+``oracle`` only.  Small cases span several tiles and ragged tails; the
+full-size workloads are checked on seeded samples of query rows (each row
+against every key) in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import video_diffusion_transformer_rmsnorm_amd as V
+import workloads as WL
+from parity import check, check_lse, from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def raw(shape, seed, dtype):
+    rng = np.random.default_rng(seed)
+    return WL.draw(shape, rng, dtype)
+
+
+def ws(dtype):
+    return "bf16" if dtype == torch.bfloat16 else "f32"
+
+
+# --------------------------------------------------------------------- rope --
+
+@pytest.mark.parametrize("dtype,D,pairs", [("bf16", 128, (22, 21, 21)), ("bf16", 64, (12, 10, 10)),
+                                           ("f32", 64, (12, 10, 10)), ("f32", 128, (20, 22, 22))])
+def test_rope_small_ragged(dtype, D, pairs):
+    grid = (3, 5, 7)
+    B, L, Hq, Hk = 2, 97, 3, 1
+    log(f"rope small {dtype} D={D} pairs={pairs} B={B} L={L}")
+    q = raw((B, L, Hq, D), 11, dtype); k = raw((B, L, Hk, D), 12, dtype)
+    qd, kd = to_dev(q), to_dev(k)
+    g = V.make_grid(*grid, pairs)
+    qo, ko = V.vdit_rope_qk(qd, kd, g, token0=5, t_offset=3)
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs, token0=5, t_offset=3)
+    check(qo, wq, dtype, "q"); check(ko, wk, dtype, "k")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_inplace_gain_nonorm_large_offset(dtype):
+    D, pairs, grid = 64, (12, 10, 10), (1, 34, 60)
+    L = 2040
+    log(f"rope in-place / gains / no-norm / t_offset {dtype}")
+    q = raw((1, L, 4, D), 21, dtype); k = raw((1, L, 2, D), 22, dtype)
+    rng = np.random.default_rng(23)
+    qg = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    kg = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    qd, kd = to_dev(q), to_dev(k)
+    g = V.make_grid(*grid, pairs)
+    V.vdit_rope_qk(qd, kd, g, q_out=qd, k_out=kd, t_offset=100003,
+                   q_gain=torch.from_numpy(qg).cuda(), k_gain=torch.from_numpy(kg).cuda())
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs, t_offset=100003, q_gain=qg, k_gain=kg)
+    check(qd, wq, dtype, "q in place"); check(kd, wk, dtype, "k in place")
+    qo, _ = V.vdit_rope_qk(to_dev(q), None, g, norm=False)
+    torch.cuda.synchronize()
+    wq2, _ = O.rope_qk(q.values, k.values, grid, pairs, norm=False)
+    check(qo, wq2, dtype, "q no-norm")
+
+
+def test_rope_full_size_wan13b():
+    w = WL.WORKLOADS[2]
+    log("rope full size 32760 x 12 x 128 bf16")
+    q, k, _ = WL.workload_inputs(w)
+    qo, ko = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*w.grid, w.pairs))
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    check(qo, wq, "bf16", "q"); check(ko, wk, "bf16", "k")
+
+
+# --------------------------------------------------------------- attention --
+
+@pytest.mark.parametrize("dtype,D,Lq,Lkv,Hq,Hk", [
+    ("bf16", 128, 300, 333, 4, 2), ("bf16", 64, 300, 333, 4, 4), ("bf16", 128, 1, 77, 2, 1),
+    ("bf16", 64, 513, 64, 2, 2), ("bf16", 128, 700, 1, 2, 2),
+    ("f32", 64, 130, 97, 2, 1), ("f32", 128, 65, 200, 2, 2),
+])
+def test_full_attention_small(dtype, D, Lq, Lkv, Hq, Hk):
+    log(f"full attention {dtype} D={D} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+    q = raw((2, Lq, Hq, D), 31, dtype); k = raw((2, Lkv, Hk, D), 32, dtype); v = raw((2, Lkv, Hk, D), 33, dtype)
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, k.values, v.values)
+    check(o, wo, dtype, "O"); check_lse(lse, wl, dtype, "LSE")
+
+
+def test_full_attention_empty_keys_and_scale():
+    log("full attention: no keys; explicit scale")
+    q = raw((1, 40, 2, 64), 41, "bf16")
+    kd = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = V.vdit_attn_fwd(to_dev(q), kd, kd)
+    torch.cuda.synchronize()
+    assert (from_dev(o) == 0).all() and np.isneginf(from_dev(lse)).all()
+    k = raw((1, 90, 2, 64), 42, "bf16"); v = raw((1, 90, 2, 64), 43, "bf16")
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), scale=0.3)
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, k.values, v.values, 0.3)
+    check(o, wo, "bf16", "O scale 0.3"); check_lse(lse, wl, "bf16", "LSE scale 0.3")
+
+
+@pytest.mark.parametrize("norm", [True, False])
+def test_tiny_workload_f32_end_to_end(norm):
+    w = WL.WORKLOADS[1]
+    log(f"tiny fp32 workload 72 tokens, norm={norm}")
+    q, k, v = WL.workload_inputs(w)
+    g = V.make_grid(*w.grid, w.pairs)
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), g, norm=norm)
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v), scale=1.0 / 8)
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs, norm=norm)
+    wo, wl = O.attention(wq, wk, v.values, 1.0 / 8)
+    check(qr, wq, "f32", "q roped"); check(o, wo, "f32", "O"); check_lse(lse, wl, "f32", "LSE")
+
+
+def _sampled_attention(qr64, kr64, v64, rows, scale=None):
+    o, l = O.attention(qr64[:, rows], kr64, v64, scale)
+    return o, l
+
+
+@pytest.mark.slow
+def test_wan13b_full_layer_sampled_rows():
+    w = WL.WORKLOADS[2]
+    log("Wan-1.3B layer 32760 x 12 x 128: rope + FULL attention, sampled rows")
+    q, k, v = WL.workload_inputs(w)
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*w.grid, w.pairs))
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v))
+    torch.cuda.synchronize()
+    rows = WL.sample_rows(w.tokens, 192, seed=7)
+    rows = np.unique(np.concatenate([rows, [0, 255, 256, w.tokens - 1]]))  # tile edges and the tail
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    wo, wl = _sampled_attention(wq, wk, v.values, rows)
+    check(from_dev(o)[:, rows], wo, "bf16", "O (sampled rows)")
+    check_lse(from_dev(lse)[:, :, rows], wl, "bf16", "LSE (sampled rows)")
+
+
+@pytest.mark.slow
+def test_wan13b_structured_inputs_sampled_rows():
+    w = WL.WORKLOADS[2]
+    log("Wan-1.3B layer with spatiotemporally smoothed inputs, sampled rows")
+    q, k, v = WL.workload_inputs(w, structured=True)
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*w.grid, w.pairs))
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v))
+    torch.cuda.synchronize()
+    rows = WL.sample_rows(w.tokens, 128, seed=8)
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    wo, wl = _sampled_attention(wq, wk, v.values, rows)
+    check(from_dev(o)[:, rows], wo, "bf16", "O (structured, sampled)")
+    check_lse(from_dev(lse)[:, :, rows], wl, "bf16", "LSE (structured, sampled)")
+
+
+def test_attention_deterministic():
+    log("determinism: two FULL runs bitwise equal")
+    q = raw((1, 600, 4, 128), 51, "bf16"); k = raw((1, 700, 4, 128), 52, "bf16"); v = raw((1, 700, 4, 128), 53, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o1, l1 = V.vdit_attn_fwd(qd, kd, vd)
+    o2, l2 = V.vdit_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --------------------------------------------------------------------- ring --
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ring_small_with_empty_chunk(dtype):
+    log(f"ring: 4 chunks incl. an empty one, {dtype}")
+    D = 128 if dtype == "bf16" else 64
+    q = raw((1, 280, 2, D), 61, dtype)
+    lens = [100, 0, 157, 65]
+    ks = [raw((1, n, 2, D), 62 + i, dtype) for i, n in enumerate(lens)]
+    vs = [raw((1, n, 2, D), 72 + i, dtype) for i, n in enumerate(lens)]
+    o, lse = V.vdit_attn_fwd(to_dev(q), mode="ring", k_chunks=[to_dev(x) for x in ks],
+                             v_chunks=[to_dev(x) for x in vs])
+    torch.cuda.synchronize()
+    K = np.concatenate([x.values for x in ks], axis=1); Vv = np.concatenate([x.values for x in vs], axis=1)
+    wo, wl = O.attention(q.values, K, Vv)
+    check(o, wo, dtype, "O ring"); check_lse(lse, wl, dtype, "LSE ring")
+    # reduction-order equivalence: ring == full on the concatenation
+    of, lf = V.vdit_attn_fwd(to_dev(q), torch.from_numpy(K.astype(np.float32)).to(o.dtype).cuda(),
+                             torch.from_numpy(Vv.astype(np.float32)).to(o.dtype).cuda())
+    torch.cuda.synchronize()
+    check(o, from_dev(of), dtype, "ring vs full (GPU)")
+
+
+@pytest.mark.slow
+def test_ring_shard_14b_sampled_rows():
+    w = WL.WORKLOADS[3]
+    log("14B-shaped shard: Q 15600, K/V 2 x 15600, 10 heads, ring of 2 + LSE merge, sampled rows")
+    q, k, v = WL.workload_inputs(w)
+    g = V.make_grid(*w.grid, w.pairs)
+    q0, q1 = w.q_range
+    qd = to_dev(q)[:, q0:q0 + q1].contiguous()
+    kd, vd = to_dev(k), to_dev(v)
+    qr, _ = V.vdit_rope_qk(qd, None, g, token0=q0)
+    kchunks = []
+    for (s, n) in w.kv_chunks:
+        _, kc = V.vdit_rope_qk(None, kd[:, s:s + n].contiguous(), g, token0=s)
+        kchunks.append(kc)
+    vchunks = [vd[:, s:s + n].contiguous() for (s, n) in w.kv_chunks]
+    o, lse = V.vdit_attn_fwd(qr, mode="ring", k_chunks=kchunks, v_chunks=vchunks)
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    rows = WL.sample_rows(q1, 160, seed=9)
+    wo, wl = O.attention(wq[:, q0 + rows], wk, v.values)
+    check(from_dev(o)[:, rows], wo, "bf16", "O ring (sampled)")
+    check_lse(from_dev(lse)[:, :, rows], wl, "bf16", "LSE ring (sampled)")
+
+
+# ------------------------------------------------------------------ merge --
+
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f32", "bf16"), ("f32", "f32")])
+def test_lse_merge(din, dout):
+    log(f"lse merge {din}->{dout}")
+    B, L, H, D = 2, 37, 3, 128
+    oa = raw((B, L, H, D), 81, din); ob = raw((B, L, H, D), 82, din)
+    rng = np.random.default_rng(83)
+    la = rng.standard_normal((B, H, L)).astype(np.float32) * 3
+    lb = rng.standard_normal((B, H, L)).astype(np.float32) * 3
+    la[0, 0, :5] = -np.inf
+    lb[0, 0, 3:8] = -np.inf
+    tdt = torch.bfloat16 if dout == "bf16" else torch.float32
+    oo, lo = V.vdit_lse_merge(to_dev(oa), torch.from_numpy(la).cuda(), to_dev(ob), torch.from_numpy(lb).cuda(),
+                              out_dtype=tdt)
+    torch.cuda.synchronize()
+    wo, wl = O.lse_merge(oa.values, la, ob.values, lb)
+    check(oo, wo, dout, "O merged", rel=False); check_lse(lo, wl, "f32", "LSE merged")
+    # in place into a
+    if din == dout:
+        ad = to_dev(oa); lad = torch.from_numpy(la).cuda()
+        V.vdit_lse_merge(ad, lad, to_dev(ob), torch.from_numpy(lb).cuda(), o_out=ad, lse_out=lad)
+        torch.cuda.synchronize()
+        check(ad, wo, dout, "O merged in place", rel=False); check_lse(lad, wl, "f32", "LSE in place")
+
+
+# ---------------------------------------------------------------- rolling --
+
+def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=False):
+    """Stream frames through rope (absolute t) + ROLLING attention; return outputs per frame."""
+    F, L, H, D = qf.values.shape
+    Hk = kf.values.shape[2]
+    dt = torch.bfloat16 if qf.dtype == "bf16" else torch.float32
+    kc = torch.zeros((n_slots, 1, L, Hk, D), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    g = V.make_grid(1, frame_grid[1], frame_grid[2], pairs)
+    qdev, kdev, vdev = to_dev(qf), to_dev(kf), to_dev(vf)
+    outs = {}
+    for f in range(frames):
+        qr, _ = V.vdit_rope_qk(qdev[f:f + 1], None, g, t_offset=f)
+        if prefill_slot:
+            slot = f % n_slots
+            V.vdit_rope_qk(None, kdev[f:f + 1], g, k_out=kc[slot], t_offset=f)
+            vc[slot].copy_(vdev[f:f + 1])
+            o, lse = V.vdit_attn_fwd(qr, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
+        else:
+            _, kr = V.vdit_rope_qk(None, kdev[f:f + 1], g, t_offset=f)
+            o, lse = V.vdit_attn_fwd(qr, kr, vdev[f:f + 1].contiguous(), mode="rolling", k_cache=kc,
+                                     v_cache=vc, frame=f)
+        outs[f] = (o, lse)
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("dtype,prefill", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_rolling_small_stream(dtype, prefill):
+    frame_grid, pairs, H, D, W, F = (1, 6, 7), (12, 10, 10), 2, 64, 3, 7
+    L = 42
+    log(f"rolling small stream {dtype} prefill={prefill} W={W} frames={F}")
+    rng = np.random.default_rng(91)
+    qf = WL.draw((F, L, H, D), rng, dtype); kf = WL.draw((F, L, H, D), rng, dtype); vf = WL.draw((F, L, H, D), rng, dtype)
+    outs = _rolling_run(qf, kf, vf, frame_grid, pairs, W, F, prefill)
+    for f in range(F):
+        wo, wl = O.rolling_frame(qf.values, kf.values, vf.values, f, W, frame_grid, pairs)
+        check(outs[f][0], wo, dtype, f"O frame {f}")
+        check_lse(outs[f][1], wl, dtype, f"LSE frame {f}")
+
+
+@pytest.mark.slow
+def test_rolling_decode_shape_sampled():
+    w = WL.WORKLOADS[4]
+    F = 8
+    log(f"rolling decode 2040 tokens x 16 heads x 64, 5 slots, {F} frames, sampled rows")
+    q, k, v = WL.workload_inputs(w)
+    sub = lambda t: WL.Tensor(t.values[:F], None if t.bits is None else t.bits[:F], t.dtype)
+    qf, kf, vf = sub(q), sub(k), sub(v)
+    outs = _rolling_run(qf, kf, vf, w.grid, w.pairs, w.n_slots, F)
+    rows = WL.sample_rows(w.tokens, 96, seed=10)
+    for f in (0, 3, 4, 7):
+        wo, wl = _rolling_oracle_rows(qf, kf, vf, f, w, rows)
+        check(from_dev(outs[f][0])[:, rows], wo, "bf16", f"O frame {f} (sampled)")
+        check_lse(from_dev(outs[f][1])[:, :, rows], wl, "bf16", f"LSE frame {f} (sampled)")
+
+
+def _rolling_oracle_rows(qf, kf, vf, f, w, rows):
+    """oracle.rolling_frame restricted to a sample of query rows (window-relative t)."""
+    win = list(O.rolling_window(f, w.n_slots))
+    f0 = win[0]
+    ks, vs = [], []
+    for u in win:
+        _, ku = O.rope_qk(kf.values[u][None], kf.values[u][None], w.grid, w.pairs, t_offset=u - f0)
+        ks.append(ku)
+        vs.append(vf.values[u][None])
+    qr, _ = O.rope_qk(qf.values[f][None], qf.values[f][None], w.grid, w.pairs, t_offset=f - f0)
+    return O.attention(qr[:, rows], np.concatenate(ks, 1), np.concatenate(vs, 1))
+
+
+# ----------------------------------------------------------------- hybrid --
+
+@pytest.mark.parametrize("dtype,D,L,C,Hq,Hk", [
+    ("bf16", 128, 300, 72, 2, 2), ("bf16", 64, 260, 64, 4, 2), ("bf16", 128, 50, 100, 2, 1),
+    ("f32", 64, 100, 24, 2, 1), ("f32", 128, 70, 16, 2, 2),
+])
+def test_hybrid_small(dtype, D, L, C, Hq, Hk):
+    log(f"chunk hybrid {dtype} D={D} L={L} chunk={C} Hq={Hq} Hk={Hk}")
+    q = raw((1, L, Hq, D), 101, dtype); k = raw((1, L, Hk, D), 102, dtype); v = raw((1, L, Hk, D), 103, dtype)
+    rng = np.random.default_rng(104)
+    s0 = (0.05 * rng.standard_normal((1, Hk, D, D))).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((1, Hk, D))).astype(np.float32)
+    sd = torch.from_numpy(s0).cuda(); zd = torch.from_numpy(z0).cuda()
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), mode="hybrid", chunk_tokens=C,
+                             state_s=sd, state_z=zd)
+    torch.cuda.synchronize()
+    wo, wl, ws_, wz = O.hybrid_recurrent(q.values, k.values, v.values, C, s0=s0, z0=z0)
+    check(o, wo, dtype, "O hybrid"); check_lse(lse, wl, dtype, "LSE hybrid")
+    # state: float32 accumulation of many terms -> relative check
+    gs, gz = from_dev(sd), from_dev(zd)
+    rs = np.linalg.norm(gs - ws_) / np.linalg.norm(ws_)
+    rz = np.linalg.norm(gz - wz) / np.linalg.norm(wz)
+    log(f"  state relF s={rs:.3e} z={rz:.3e}")
+    assert rs <= 1e-5 and rz <= 1e-5
+
+
+def test_hybrid_chunkwise_calls_equal_one_call():
+    log("chunk hybrid: one call per chunk == one call")
+    D, L, C, H = 128, 256, 64, 2
+    q = raw((1, L, H, D), 111, "bf16"); k = raw((1, L, H, D), 112, "bf16"); v = raw((1, L, H, D), 113, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    s1 = torch.zeros((1, H, D, D), device="cuda"); z1 = torch.zeros((1, H, D), device="cuda")
+    o1, _ = V.vdit_attn_fwd(qd, kd, vd, mode="hybrid", chunk_tokens=C, state_s=s1, state_z=z1)
+    s2 = torch.zeros_like(s1); z2 = torch.zeros_like(z1)
+    parts = []
+    for c0 in range(0, L, C):
+        sl = slice(c0, c0 + C)
+        oc, _ = V.vdit_attn_fwd(qd[:, sl].contiguous(), kd[:, sl].contiguous(), vd[:, sl].contiguous(),
+                                mode="hybrid", chunk_tokens=C, state_s=s2, state_z=z2)
+        parts.append(oc)
+    torch.cuda.synchronize()
+    o2 = torch.cat(parts, dim=1)
+    assert torch.equal(o1, o2), float((o1.float() - o2.float()).abs().max())
+    assert torch.equal(s1, s2) and torch.equal(z1, z2)
+
+
+@pytest.mark.slow
+def test_hybrid_5b_full():
+    w = WL.WORKLOADS[5]
+    log("chunk hybrid 12090 x 24 x 128, chunks of 1170: rope + hybrid vs oracle (all rows)")
+    q, k, v = WL.workload_inputs(w)
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*w.grid, w.pairs))
+    sd = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device="cuda")
+    zd = torch.zeros((1, w.kv_heads, w.head_dim), device="cuda")
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v), mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=sd, state_z=zd)
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    o_s, l_s, o_l, l_l = O.hybrid_partials(wq, wk, v.values, w.chunk_tokens)
+    wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
+    check(o, wo, "bf16", "O hybrid (all rows)")
+    check_lse(lse, wl, "bf16", "LSE hybrid")
+    fk = O.phi(wk)
+    ws_ = np.einsum("blhd,blhe->bhde", fk, v.values)
+    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
+    log(f"  state relF={rs:.3e}")
+    # the oracle's rotated k is unrounded float64 while the library's k is the
+    # bf16-rounded output of vdit_rope_qk: the state inherits that rounding
+    assert rs <= 1e-2
+
+
+# ----------------------------------------------------------------- errors --
+
+def test_invalid_arguments_raise():
+    log("invalid arguments raise VditError")
+    q = torch.zeros((1, 10, 3, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 10, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(V.VditError):
+        V.vdit_attn_fwd(q, k, k)  # 3 heads over 2 kv heads
+    qq = torch.zeros((1, 10, 2, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(V.VditError):
+        V.vdit_attn_fwd(qq, qq, qq)

@@ -1,0 +1,274 @@
+// abi.cpp -- the extern "C" boundary of libvdit: validation, mode dispatch
+// and error reporting.  Declared in include/vdit.h.
+#include "vdit.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "validate.hpp"
+#include "vdit_internal.hpp"
+
+static_assert(sizeof(vdit_attn_args) == sizeof(vdit::AttnArgs), "vdit_attn_args layout mirror");
+static_assert(offsetof(vdit_attn_args, workspace_bytes) == offsetof(vdit::AttnArgs, workspace_bytes),
+              "vdit_attn_args layout mirror");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vdit_status fail(vdit_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+vdit_status from_check(const vdit::CheckResult& r) {
+  if (r) return VDIT_OK;
+  return fail(r.code == vdit::Check::unsupported ? VDIT_ERR_UNSUPPORTED : VDIT_ERR_INVALID_ARG, r.msg);
+}
+
+vdit_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return VDIT_OK;
+  return fail(VDIT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+const vdit::AttnArgs& mirror(const vdit_attn_args* a) {
+  return *reinterpret_cast<const vdit::AttnArgs*>(a);
+}
+
+float softmax_scale(const vdit::AttnArgs& a) {
+  return a.scale > 0.f ? a.scale : 1.0f / std::sqrt(float(a.head_dim));
+}
+
+vdit::AttnLaunch base_launch(const vdit::AttnArgs& a) {
+  vdit::AttnLaunch p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = a.q;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.Lq = a.Lq;
+  p.B = a.B;
+  p.Hq = a.n_heads;
+  p.Hk = a.n_kv_heads;
+  p.D = a.head_dim;
+  p.scale = softmax_scale(a);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.epi = vdit::kEpiPlain;
+  return p;
+}
+
+hipError_t launch_attn(const vdit::AttnLaunch& p, int dtype, hipStream_t s) {
+  return dtype == VDIT_BF16 ? vdit::launch_attn_bf16(p, s) : vdit::launch_attn_f32(p, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vdit_last_error(void) { return g_last_error.c_str(); }
+
+int32_t vdit_abi_version(void) { return VDIT_ABI_VERSION; }
+
+vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* k_out, int32_t B,
+                         int64_t L, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                         vdit_dtype dtype, const vdit_grid* grid, int64_t token0, int64_t t_offset,
+                         const float* q_gain, const float* k_gain, float eps, uint32_t flags,
+                         hipStream_t stream) {
+  static_assert(sizeof(vdit_grid) == sizeof(vdit::GridArgs), "vdit_grid layout mirror");
+  const auto* g = reinterpret_cast<const vdit::GridArgs*>(grid);
+  if (auto r = vdit::check_rope(q_in, k_in, q_out, k_out, B, L, n_heads, n_kv_heads, head_dim,
+                                int(dtype), g, token0, eps);
+      !r)
+    return from_check(r);
+  if ((q_gain && (reinterpret_cast<uintptr_t>(q_gain) & 15)) ||
+      (k_gain && (reinterpret_cast<uintptr_t>(k_gain) & 15)))
+    return fail(VDIT_ERR_INVALID_ARG, "gain pointers must be 16-byte aligned");
+  if (flags & ~uint32_t(VDIT_ROPE_NO_NORM)) return fail(VDIT_ERR_INVALID_ARG, "unknown rope flags");
+  vdit::RopeLaunch p;
+  p.q_in = q_in;
+  p.k_in = k_in;
+  p.q_out = q_out;
+  p.k_out = k_out;
+  p.q_gain = q_gain;
+  p.k_gain = k_gain;
+  p.L = L;
+  p.token0 = token0;
+  p.t_offset = t_offset;
+  p.B = B;
+  p.Hq = n_heads;
+  p.Hk = n_kv_heads;
+  p.D = head_dim;
+  p.T = g->T;
+  p.H = g->H;
+  p.W = g->W;
+  p.pairs_t = g->pairs_t;
+  p.pairs_h = g->pairs_h;
+  p.pairs_w = g->pairs_w;
+  p.theta = g->theta;
+  p.eps = eps;
+  p.norm = (flags & VDIT_ROPE_NO_NORM) ? 0 : 1;
+  p.dtype = int32_t(dtype);
+  return from_hip(vdit::launch_rope(p, stream), "vdit_rope_qk launch");
+}
+
+size_t vdit_attn_workspace_bytes(const vdit_attn_args* args) {
+  if (!args) return size_t(-1);
+  const vdit::AttnArgs& a = mirror(args);
+  if (auto r = vdit::check_attn_shape(a); !r) {
+    g_last_error = r.msg;
+    return size_t(-1);
+  }
+  return vdit::attn_workspace_bytes(a);
+}
+
+vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
+  if (!args) return fail(VDIT_ERR_INVALID_ARG, "args is NULL");
+  const vdit::AttnArgs& a = mirror(args);
+  if (auto r = vdit::check_attn(a); !r) return from_check(r);
+  const size_t es = vdit::esize(a.dtype);
+  const int64_t D = a.head_dim;
+  const bool empty_q = (a.B == 0 || a.Lq == 0);
+
+  switch (a.mode) {
+    case VDIT_ATTN_FULL: {
+      if (empty_q) return VDIT_OK;
+      vdit::AttnLaunch p = base_launch(a);
+      if (a.Lkv > 0) {
+        p.nseg = 1;
+        p.seg[0] = {a.k, a.v, a.Lkv, a.Lkv * a.n_kv_heads * D};
+      }
+      return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(FULL) launch");
+    }
+    case VDIT_ATTN_RING: {
+      if (empty_q) return VDIT_OK;
+      const int n = a.n_kv_chunks;
+      auto seg_of = [&](int c) -> vdit::KvSeg {
+        return {a.k_chunks[c], a.v_chunks[c], a.chunk_len[c], a.chunk_len[c] * a.n_kv_heads * D};
+      };
+      if (n == 1) {
+        vdit::AttnLaunch p = base_launch(a);
+        if (a.chunk_len[0] > 0) {
+          p.nseg = 1;
+          p.seg[0] = seg_of(0);
+        }
+        return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(RING) launch");
+      }
+      char* ws = static_cast<char*>(a.workspace);
+      float* part_o = reinterpret_cast<float*>(ws);
+      float* part_lse = reinterpret_cast<float*>(
+          ws + vdit::align256(size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(D) * 4));
+      for (int c = 0; c < n; ++c) {
+        vdit::AttnLaunch p = base_launch(a);
+        if (a.chunk_len[c] > 0) {
+          p.nseg = 1;
+          p.seg[0] = seg_of(c);
+        }
+        p.epi = vdit::kEpiRing;
+        p.part_o = part_o;
+        p.part_lse = part_lse;
+        p.has_prev = c > 0;
+        p.final_out = c == n - 1;
+        if (auto st = from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(RING) launch"); st != VDIT_OK)
+          return st;
+      }
+      return VDIT_OK;
+    }
+    case VDIT_ATTN_ROLLING: {
+      if (empty_q) return VDIT_OK;
+      const size_t slot_elems = size_t(a.B) * size_t(a.Lq) * size_t(a.n_kv_heads) * size_t(D);
+      const int64_t slot = a.frame % a.n_slots;
+      char* kc = static_cast<char*>(a.k_cache);
+      char* vc = static_cast<char*>(a.v_cache);
+      if (a.k && a.k != kc + slot * slot_elems * es) {
+        if (auto st = from_hip(hipMemcpyAsync(kc + slot * slot_elems * es, a.k, slot_elems * es,
+                                              hipMemcpyDeviceToDevice, stream),
+                               "vdit_attn_fwd(ROLLING) k copy");
+            st != VDIT_OK)
+          return st;
+      }
+      if (a.v && a.v != vc + slot * slot_elems * es) {
+        if (auto st = from_hip(hipMemcpyAsync(vc + slot * slot_elems * es, a.v, slot_elems * es,
+                                              hipMemcpyDeviceToDevice, stream),
+                               "vdit_attn_fwd(ROLLING) v copy");
+            st != VDIT_OK)
+          return st;
+      }
+      const int64_t nvalid = a.frame + 1 < a.n_slots ? a.frame + 1 : a.n_slots;
+      vdit::AttnLaunch p = base_launch(a);
+      p.nseg = int32_t(nvalid);
+      for (int64_t i = 0; i < nvalid; ++i) {
+        const int64_t f = a.frame - nvalid + 1 + i;  // oldest first
+        const int64_t sl = f % a.n_slots;
+        p.seg[i] = {kc + sl * slot_elems * es, vc + sl * slot_elems * es, a.Lq, a.Lq * a.n_kv_heads * D};
+      }
+      return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(ROLLING) launch");
+    }
+    case VDIT_ATTN_CHUNK_HYBRID: {
+      const vdit::HybridLayout lay = vdit::hybrid_layout(a);
+      char* ws = static_cast<char*>(a.workspace);
+      vdit::HybridStateLaunch hs;
+      std::memset(&hs, 0, sizeof(hs));
+      hs.k = a.k;
+      hs.v = a.v;
+      hs.s_in = a.state_s;
+      hs.z_in = a.state_z;
+      hs.s_out = a.state_s;
+      hs.z_out = a.state_z;
+      hs.ds = reinterpret_cast<float*>(ws + lay.off_ds);
+      hs.dz = reinterpret_cast<float*>(ws + lay.off_dz);
+      hs.sc = ws + lay.off_sc;
+      hs.zc = reinterpret_cast<float*>(ws + lay.off_zc);
+      hs.L = a.Lq;
+      hs.chunk = a.chunk_tokens;
+      hs.n_chunks = lay.n_chunks;
+      hs.nsplit = lay.nsplit;
+      hs.B = a.B;
+      hs.Hk = a.n_kv_heads;
+      hs.D = a.head_dim;
+      hs.dtype = a.dtype;
+      if (auto st = from_hip(vdit::launch_hybrid_state(hs, stream), "vdit_attn_fwd(CHUNK_HYBRID) state");
+          st != VDIT_OK)
+        return st;
+      if (empty_q) return VDIT_OK;
+      vdit::AttnLaunch p = base_launch(a);
+      p.epi = vdit::kEpiHybrid;
+      p.chunk = a.chunk_tokens;
+      p.n_chunks = lay.n_chunks;
+      p.st = ws + lay.off_sc;
+      p.zc = reinterpret_cast<const float*>(ws + lay.off_zc);
+      p.hk = a.k;
+      p.hv = a.v;
+      p.nseg = 1;
+      return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(CHUNK_HYBRID) launch");
+    }
+  }
+  return fail(VDIT_ERR_INVALID_ARG, "unknown attention mode");
+}
+
+vdit_status vdit_lse_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                           void* o_out, float* lse_out, vdit_dtype in_dtype, vdit_dtype out_dtype,
+                           int32_t B, int64_t L, int32_t n_heads, int32_t head_dim,
+                           hipStream_t stream) {
+  if (auto r = vdit::check_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, int(in_dtype),
+                                 int(out_dtype), B, L, n_heads, head_dim);
+      !r)
+    return from_check(r);
+  vdit::MergeLaunch p;
+  p.o_a = o_a;
+  p.lse_a = lse_a;
+  p.o_b = o_b;
+  p.lse_b = lse_b;
+  p.o_out = o_out;
+  p.lse_out = lse_out;
+  p.L = L;
+  p.B = B;
+  p.H = n_heads;
+  p.D = head_dim;
+  p.in_dtype = int32_t(in_dtype);
+  p.out_dtype = int32_t(out_dtype);
+  return from_hip(vdit::launch_merge(p, stream), "vdit_lse_merge launch");
+}
+
+}  // extern "C"

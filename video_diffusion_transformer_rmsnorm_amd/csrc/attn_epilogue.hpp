@@ -1,0 +1,39 @@
+// attn_epilogue.hpp -- per-row finishing arithmetic shared by the attention
+// kernels: turning a running (max, sum, unnormalised accumulator) into
+// (O, LSE), and the log-sum-exp merge of two partials.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace vdit {
+
+// Natural-log LSE of a softmax partial whose scores were tracked in log2
+// units: m2 = running max of scale*log2(e)*s, l = sum 2^(that - m2).
+__device__ __forceinline__ float partial_lse(float m2, float l) {
+  return l > 0.f ? m2 * kLn2 + logf(l) : -INFINITY;
+}
+
+// Weights of two partials (la, lb natural-log LSEs) in their merge, and the
+// merged LSE.  A -inf partial gets weight 0; two -inf partials give 0, 0, -inf.
+struct MergeW {
+  float wa, wb, lse;
+};
+__device__ __forceinline__ MergeW merge_weights(float la, float lb) {
+  MergeW w;
+  const float mx = fmaxf(la, lb);
+  if (mx == -INFINITY) {
+    w.wa = 0.f; w.wb = 0.f; w.lse = -INFINITY;
+    return w;
+  }
+  const float ea = expf(la - mx), eb = expf(lb - mx);
+  const float s = ea + eb;
+  w.wa = ea / s;
+  w.wb = eb / s;
+  w.lse = mx + logf(s);
+  return w;
+}
+
+// phi(x) = elu(x) + 1
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+}  // namespace vdit

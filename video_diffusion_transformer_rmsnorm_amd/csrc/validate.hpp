@@ -1,0 +1,323 @@
+// validate.hpp -- argument validation for the vdit C ABI.
+//
+// Header-only and free of HIP calls so that a plain host compiler can build
+// it for CPU-only tests.  Every check runs before any launch; on failure the
+// caller writes nothing and reports the returned message.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+namespace vdit {
+
+enum class Check { ok = 0, invalid = 1, unsupported = 2 };
+
+struct CheckResult {
+  Check code = Check::ok;
+  std::string msg;
+  static CheckResult good() { return {}; }
+  static CheckResult bad(const std::string& m) { return {Check::invalid, m}; }
+  static CheckResult unsup(const std::string& m) { return {Check::unsupported, m}; }
+  explicit operator bool() const { return code == Check::ok; }
+};
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+inline size_t esize(int dtype) { return dtype == 1 ? 4 : 2; }
+
+inline CheckResult check_dtype(int dtype) {
+  if (dtype != 0 && dtype != 1) return CheckResult::bad("dtype must be VDIT_BF16 (0) or VDIT_F32 (1)");
+  return CheckResult::good();
+}
+
+inline CheckResult check_head_dim(int32_t D) {
+  if (D <= 0 || (D & 1)) return CheckResult::bad("head_dim must be a positive even number");
+  if (D != 64 && D != 128) return CheckResult::unsup("head_dim must be 64 or 128");
+  return CheckResult::good();
+}
+
+inline CheckResult check_heads(int32_t Hq, int32_t Hk) {
+  if (Hq <= 0 || Hk <= 0) return CheckResult::bad("n_heads and n_kv_heads must be positive");
+  if (Hq % Hk != 0) return CheckResult::bad("n_heads must be a multiple of n_kv_heads");
+  return CheckResult::good();
+}
+
+struct GridArgs {
+  int32_t T, H, W, pairs_t, pairs_h, pairs_w;
+  float theta;
+};
+
+inline CheckResult check_rope(const void* q_in, const void* k_in, const void* q_out,
+                              const void* k_out, int32_t B, int64_t L, int32_t Hq, int32_t Hk,
+                              int32_t D, int dtype, const GridArgs* g, int64_t token0,
+                              float eps) {
+  if (auto r = check_dtype(dtype); !r) return r;
+  if (auto r = check_head_dim(D); !r) return r;
+  if (!g) return CheckResult::bad("grid is NULL");
+  if (B < 0 || L < 0) return CheckResult::bad("B and L must be non-negative");
+  if ((q_in == nullptr) != (q_out == nullptr))
+    return CheckResult::bad("q_in and q_out must both be set or both be NULL");
+  if ((k_in == nullptr) != (k_out == nullptr))
+    return CheckResult::bad("k_in and k_out must both be set or both be NULL");
+  if (q_in && Hq <= 0) return CheckResult::bad("n_heads must be positive when q is given");
+  if (k_in && Hk <= 0) return CheckResult::bad("n_kv_heads must be positive when k is given");
+  if (g->T <= 0 || g->H <= 0 || g->W <= 0) return CheckResult::bad("grid T, H, W must be positive");
+  if (g->pairs_t < 0 || g->pairs_h < 0 || g->pairs_w < 0)
+    return CheckResult::bad("rotary pair counts must be non-negative");
+  if (int64_t(g->pairs_t) + g->pairs_h + g->pairs_w != D / 2)
+    return CheckResult::bad("pairs_t + pairs_h + pairs_w must equal head_dim / 2");
+  if (!(g->theta > 1.0f)) return CheckResult::bad("theta must be > 1");
+  if (!(eps >= 0.0f)) return CheckResult::bad("eps must be >= 0");
+  if (token0 < 0) return CheckResult::bad("token0 must be >= 0");
+  const int64_t cells = int64_t(g->T) * g->H * g->W;
+  if (token0 + L > cells) return CheckResult::bad("token0 + L exceeds the T*H*W grid");
+  for (const void* p : {q_in, k_in, q_out, k_out})
+    if (p && !aligned16(p)) return CheckResult::bad("tensor pointers must be 16-byte aligned");
+  const size_t es = esize(dtype);
+  const size_t nq = q_in ? size_t(B) * size_t(L) * size_t(Hq) * size_t(D) * es : 0;
+  const size_t nk = k_in ? size_t(B) * size_t(L) * size_t(Hk) * size_t(D) * es : 0;
+  if (q_in && q_out != q_in && overlaps(q_in, nq, q_out, nq))
+    return CheckResult::bad("q_out partially overlaps q_in");
+  if (k_in && k_out != k_in && overlaps(k_in, nk, k_out, nk))
+    return CheckResult::bad("k_out partially overlaps k_in");
+  if (q_out && k_out && overlaps(q_out, nq, k_out, nk))
+    return CheckResult::bad("q_out overlaps k_out");
+  return CheckResult::good();
+}
+
+// Mirror of vdit_attn_args with plain types (kept layout-identical).
+struct AttnArgs {
+  int32_t mode, dtype, B, n_heads, n_kv_heads, head_dim;
+  int64_t Lq, Lkv;
+  float scale;
+  int32_t n_kv_chunks;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const void* const* k_chunks;
+  const void* const* v_chunks;
+  const int64_t* chunk_len;
+  void* k_cache;
+  void* v_cache;
+  int64_t frame;
+  int32_t n_slots;
+  int32_t reserved0;
+  int64_t chunk_tokens;
+  float* state_s;
+  float* state_z;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+constexpr int kMaxRingChunks = 64;
+constexpr int kMaxSlots = 8;  // rolling-window frames handled in one launch
+
+// Workspace layout of the chunk-hybrid mode (byte offsets from the workspace
+// base, each region 256-byte aligned):
+//   dS   [n_chunks][nsplit][B][Hk][D][D] float32   per-split chunk state deltas (transposed: [d_out][d_in])
+//   dz   [n_chunks][nsplit][B][Hk][D]    float32
+//   S_c  [n_chunks][B][Hk][D][D]         float32 (F32 path) or 2 x bf16 hi/lo (BF16 path), transposed
+//   z_c  [n_chunks][B][Hk][D]            float32
+struct HybridLayout {
+  int64_t n_chunks = 0;
+  int nsplit = 1;
+  size_t off_ds = 0, off_dz = 0, off_sc = 0, off_zc = 0, total = 0;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int hybrid_nsplit(int64_t chunk_tokens) {
+  // enough token splits that every chunk state delta is spread over several
+  // workgroups, but each split still covers >= 128 tokens
+  int64_t s = chunk_tokens / 128;
+  if (s < 1) s = 1;
+  if (s > 8) s = 8;
+  return int(s);
+}
+
+inline HybridLayout hybrid_layout(const AttnArgs& a) {
+  HybridLayout h;
+  const int64_t L = a.Lq, C = a.chunk_tokens;
+  const size_t D = size_t(a.head_dim), B = size_t(a.B), Hk = size_t(a.n_kv_heads);
+  h.n_chunks = C > 0 ? (L + C - 1) / C : 0;
+  h.nsplit = hybrid_nsplit(C);
+  const size_t nc = size_t(h.n_chunks), ns = size_t(h.nsplit);
+  size_t off = 0;
+  h.off_ds = off; off = align256(off + nc * ns * B * Hk * D * D * 4);
+  h.off_dz = off; off = align256(off + nc * ns * B * Hk * D * 4);
+  h.off_sc = off; off = align256(off + nc * B * Hk * D * D * 4);  // f32, or hi+lo bf16 (same bytes)
+  h.off_zc = off; off = align256(off + nc * B * Hk * D * 4);
+  h.total = off;
+  return h;
+}
+
+inline size_t ring_workspace_bytes(const AttnArgs& a) {
+  if (a.n_kv_chunks <= 1) return 0;
+  const size_t o = size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * 4;
+  const size_t l = size_t(a.B) * size_t(a.n_heads) * size_t(a.Lq) * 4;
+  return align256(o) + align256(l);
+}
+
+inline CheckResult check_attn(const AttnArgs& a) {
+  if (auto r = check_dtype(a.dtype); !r) return r;
+  if (auto r = check_head_dim(a.head_dim); !r) return r;
+  if (auto r = check_heads(a.n_heads, a.n_kv_heads); !r) return r;
+  if (a.B < 0 || a.Lq < 0 || a.Lkv < 0) return CheckResult::bad("B, Lq, Lkv must be non-negative");
+  if (a.mode < 0 || a.mode > 3) return CheckResult::bad("unknown attention mode");
+  if (!(a.scale == a.scale)) return CheckResult::bad("scale is NaN");
+  const size_t es = esize(a.dtype);
+  const size_t D = size_t(a.head_dim);
+  const size_t nq = size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * D * es;
+  const bool empty_q = (a.B == 0 || a.Lq == 0);
+  if (!empty_q) {
+    if (!a.q || !a.o) return CheckResult::bad("q and o must be non-NULL");
+    if (!aligned16(a.q) || !aligned16(a.o)) return CheckResult::bad("q and o must be 16-byte aligned");
+  }
+  if (a.lse && !aligned16(a.lse)) return CheckResult::bad("lse must be 16-byte aligned");
+  if (!empty_q && overlaps(a.q, nq, a.o, nq)) return CheckResult::bad("o overlaps q");
+  switch (a.mode) {
+    case 0: {  // FULL
+      if (a.Lkv > 0 && !empty_q) {
+        if (!a.k || !a.v) return CheckResult::bad("k and v must be non-NULL");
+        if (!aligned16(a.k) || !aligned16(a.v)) return CheckResult::bad("k and v must be 16-byte aligned");
+        const size_t nk = size_t(a.B) * size_t(a.Lkv) * size_t(a.n_kv_heads) * D * es;
+        if (overlaps(a.o, nq, a.k, nk) || overlaps(a.o, nq, a.v, nk))
+          return CheckResult::bad("o overlaps k or v");
+      }
+      break;
+    }
+    case 1: {  // RING
+      if (a.n_kv_chunks < 1) return CheckResult::bad("RING needs n_kv_chunks >= 1");
+      if (a.n_kv_chunks > kMaxRingChunks) return CheckResult::unsup("too many ring chunks (max 64)");
+      if (!a.k_chunks || !a.v_chunks || !a.chunk_len)
+        return CheckResult::bad("RING needs k_chunks, v_chunks and chunk_len");
+      int64_t sum = 0;
+      for (int c = 0; c < a.n_kv_chunks; ++c) {
+        if (a.chunk_len[c] < 0) return CheckResult::bad("chunk_len must be non-negative");
+        sum += a.chunk_len[c];
+        if (a.chunk_len[c] > 0 && !empty_q) {
+          if (!a.k_chunks[c] || !a.v_chunks[c]) return CheckResult::bad("RING chunk pointer is NULL");
+          if (!aligned16(a.k_chunks[c]) || !aligned16(a.v_chunks[c]))
+            return CheckResult::bad("RING chunk pointers must be 16-byte aligned");
+        }
+      }
+      if (sum != a.Lkv) return CheckResult::bad("chunk_len must sum to Lkv");
+      const size_t need = ring_workspace_bytes(a);
+      if (need && !empty_q) {
+        if (!a.workspace || a.workspace_bytes < need)
+          return CheckResult::bad("RING workspace too small (see vdit_attn_workspace_bytes)");
+        if (!aligned16(a.workspace)) return CheckResult::bad("workspace must be 16-byte aligned");
+        if (overlaps(a.workspace, need, a.o, nq)) return CheckResult::bad("workspace overlaps o");
+      }
+      break;
+    }
+    case 2: {  // ROLLING
+      if (a.n_slots < 1) return CheckResult::bad("ROLLING needs n_slots >= 1");
+      if (a.n_slots > kMaxSlots) return CheckResult::unsup("ROLLING supports at most 8 slots");
+      if (a.frame < 0) return CheckResult::bad("frame must be >= 0");
+      if (!empty_q) {
+        if (!a.k_cache || !a.v_cache) return CheckResult::bad("ROLLING needs k_cache and v_cache");
+        if (!aligned16(a.k_cache) || !aligned16(a.v_cache))
+          return CheckResult::bad("caches must be 16-byte aligned");
+        if ((a.k == nullptr) != (a.v == nullptr))
+          return CheckResult::bad("ROLLING: k and v must both be set or both be NULL");
+        const size_t nc = size_t(a.n_slots) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_kv_heads) * D * es;
+        if (overlaps(a.o, nq, a.k_cache, nc) || overlaps(a.o, nq, a.v_cache, nc))
+          return CheckResult::bad("o overlaps a cache");
+        if (overlaps(a.k_cache, nc, a.v_cache, nc)) return CheckResult::bad("k_cache overlaps v_cache");
+      }
+      break;
+    }
+    case 3: {  // CHUNK_HYBRID
+      if (a.chunk_tokens < 1) return CheckResult::bad("CHUNK_HYBRID needs chunk_tokens >= 1");
+      if (a.Lkv != a.Lq) return CheckResult::bad("CHUNK_HYBRID is self-attention: Lkv must equal Lq");
+      if (!a.state_s || !a.state_z) return CheckResult::bad("CHUNK_HYBRID needs state_s and state_z");
+      if (!aligned16(a.state_s) || !aligned16(a.state_z))
+        return CheckResult::bad("state buffers must be 16-byte aligned");
+      if (!empty_q) {
+        if (!a.k || !a.v) return CheckResult::bad("k and v must be non-NULL");
+        if (!aligned16(a.k) || !aligned16(a.v)) return CheckResult::bad("k and v must be 16-byte aligned");
+        const size_t need = hybrid_layout(a).total;
+        if (!a.workspace || a.workspace_bytes < need)
+          return CheckResult::bad("CHUNK_HYBRID workspace too small (see vdit_attn_workspace_bytes)");
+        if (!aligned16(a.workspace)) return CheckResult::bad("workspace must be 16-byte aligned");
+        if (overlaps(a.workspace, need, a.o, nq)) return CheckResult::bad("workspace overlaps o");
+      }
+      break;
+    }
+  }
+  return CheckResult::good();
+}
+
+inline size_t attn_workspace_bytes(const AttnArgs& a) {
+  switch (a.mode) {
+    case 1: return ring_workspace_bytes(a);
+    case 3: return hybrid_layout(a).total;
+    default: return 0;
+  }
+}
+
+// Workspace check that ignores the workspace fields themselves (used by
+// vdit_attn_workspace_bytes, which is called before a workspace exists).
+inline CheckResult check_attn_shape(const AttnArgs& a) {
+  AttnArgs b = a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  b.q = b.k = b.v = nullptr;
+  b.o = nullptr;
+  b.lse = nullptr;
+  b.k_cache = b.v_cache = nullptr;
+  b.Lq = a.Lq;
+  if (auto r = check_dtype(b.dtype); !r) return r;
+  if (auto r = check_head_dim(b.head_dim); !r) return r;
+  if (auto r = check_heads(b.n_heads, b.n_kv_heads); !r) return r;
+  if (b.B < 0 || b.Lq < 0 || b.Lkv < 0) return CheckResult::bad("B, Lq, Lkv must be non-negative");
+  if (b.mode < 0 || b.mode > 3) return CheckResult::bad("unknown attention mode");
+  if (b.mode == 1 && (b.n_kv_chunks < 1 || b.n_kv_chunks > kMaxRingChunks))
+    return CheckResult::bad("RING needs 1 <= n_kv_chunks <= 64");
+  if (b.mode == 3 && b.chunk_tokens < 1) return CheckResult::bad("CHUNK_HYBRID needs chunk_tokens >= 1");
+  return CheckResult::good();
+}
+
+inline CheckResult check_merge(const void* o_a, const float* lse_a, const void* o_b,
+                               const float* lse_b, const void* o_out, const float* lse_out,
+                               int in_dtype, int out_dtype, int32_t B, int64_t L, int32_t H,
+                               int32_t D) {
+  if (auto r = check_dtype(in_dtype); !r) return r;
+  if (auto r = check_dtype(out_dtype); !r) return r;
+  if (auto r = check_head_dim(D); !r) return r;
+  if (B < 0 || L < 0 || H <= 0) return CheckResult::bad("B, L must be >= 0 and n_heads > 0");
+  if (B == 0 || L == 0) return CheckResult::good();
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return CheckResult::bad("merge pointers must be non-NULL");
+  for (const void* p : {o_a, static_cast<const void*>(lse_a), o_b, static_cast<const void*>(lse_b), o_out})
+    if (!aligned16(p)) return CheckResult::bad("merge pointers must be 16-byte aligned");
+  if (lse_out && !aligned16(lse_out)) return CheckResult::bad("lse_out must be 16-byte aligned");
+  const size_t nin = size_t(B) * size_t(L) * size_t(H) * size_t(D) * esize(in_dtype);
+  const size_t nout = size_t(B) * size_t(L) * size_t(H) * size_t(D) * esize(out_dtype);
+  const size_t nl = size_t(B) * size_t(L) * size_t(H) * 4;
+  for (const void* in : {o_a, o_b}) {
+    if (in == o_out) {
+      if (in_dtype != out_dtype) return CheckResult::bad("in-place merge needs in_dtype == out_dtype");
+    } else if (overlaps(in, nin, o_out, nout)) {
+      return CheckResult::bad("o_out partially overlaps an input");
+    }
+  }
+  if (lse_out) {
+    for (const float* in : {lse_a, lse_b})
+      if (in != lse_out && overlaps(in, nl, lse_out, nl))
+        return CheckResult::bad("lse_out partially overlaps an input");
+    if (overlaps(lse_out, nl, o_out, nout)) return CheckResult::bad("lse_out overlaps o_out");
+  }
+  return CheckResult::good();
+}
+
+}  // namespace vdit

@@ -1,0 +1,108 @@
+// vdit_internal.hpp -- kernel parameter blocks and launcher entry points
+// shared between the C ABI (abi.cpp) and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace vdit {
+
+constexpr int kMaxSeg = 8;
+
+// A run of keys/values: element (b, j, hk, d) of a segment lives at
+// base + b * bstride + (j * Hk + hk) * D + d.
+struct KvSeg {
+  const void* k;
+  const void* v;
+  int64_t len;
+  int64_t bstride;  // elements between batches
+};
+
+enum Epilogue : int32_t {
+  kEpiPlain = 0,   // write normalised O (+ LSE)
+  kEpiRing = 1,    // fold into / out of a float32 running partial
+  kEpiHybrid = 2,  // merge with the linear-attention partial of the chunk
+};
+
+struct AttnLaunch {
+  const void* q;
+  void* o;
+  float* lse;
+  int64_t Lq;
+  int32_t B, Hq, Hk, D;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  int32_t nseg;
+  int32_t epi;
+  KvSeg seg[kMaxSeg];
+  // ring epilogue
+  float* part_o;     // [B, Lq, Hq, D] float32 running partial
+  float* part_lse;   // [B, Hq, Lq]
+  int32_t has_prev;  // part_* hold the partial of the earlier chunks
+  int32_t final_out; // write o / lse (else write part_*)
+  // chunk-hybrid (self-attention over q's own sequence, chunks of `chunk`)
+  int64_t chunk;
+  int64_t n_chunks;
+  const void* st;    // per chunk state S_c^T [n_chunks][B][Hk][D][D]: bf16 hi,lo pairs or float32
+  const float* zc;   // [n_chunks][B][Hk][D]
+  const void* hk;    // key / value base of the whole sequence (hybrid)
+  const void* hv;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s);
+hipError_t launch_attn_f32(const AttnLaunch& p, hipStream_t s);
+
+struct RopeLaunch {
+  const void* q_in;
+  const void* k_in;
+  void* q_out;
+  void* k_out;
+  const float* q_gain;
+  const float* k_gain;
+  int64_t L;
+  int64_t token0;
+  int64_t t_offset;
+  int32_t B, Hq, Hk, D;
+  int32_t T, H, W;
+  int32_t pairs_t, pairs_h, pairs_w;
+  float theta;
+  float eps;
+  int32_t norm;
+  int32_t dtype;
+};
+hipError_t launch_rope(const RopeLaunch& p, hipStream_t s);
+
+struct MergeLaunch {
+  const void* o_a;
+  const float* lse_a;
+  const void* o_b;
+  const float* lse_b;
+  void* o_out;
+  float* lse_out;
+  int64_t L;
+  int32_t B, H, D;
+  int32_t in_dtype, out_dtype;
+};
+hipError_t launch_merge(const MergeLaunch& p, hipStream_t s);
+
+struct HybridStateLaunch {
+  const void* k;       // [B, L, Hk, D]
+  const void* v;
+  const float* s_in;   // [B, Hk, D, D]  (d_in, d_out)
+  const float* z_in;   // [B, Hk, D]
+  float* s_out;        // may equal s_in
+  float* z_out;
+  float* ds;           // [n_chunks][nsplit][B][Hk][D][D] transposed (d_out, d_in)
+  float* dz;           // [n_chunks][nsplit][B][Hk][D]
+  void* sc;            // per-chunk state, transposed, bf16 hi/lo pairs or float32
+  float* zc;
+  int64_t L, chunk, n_chunks;
+  int32_t nsplit;
+  int32_t B, Hk, D;
+  int32_t dtype;       // of k, v; also selects the S_c format
+};
+hipError_t launch_hybrid_state(const HybridStateLaunch& p, hipStream_t s);
+
+}  // namespace vdit
