@@ -146,7 +146,7 @@ def bench_full(args):
         "rope_GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(), "kernel": "attn_mfma_kernel<128,2,4>",
+                     "traffic": measured_traffic(), "kernel": "attn_mfma_kernel<128,4>",
                      "algorithmic_flops_per_launch": flops},
     }
     return out, w
@@ -180,10 +180,10 @@ def bench_other(args):
         def step():
             V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs)
     elif w.mode == "rolling":
-        kc = torch.zeros((w.n_slots, 1, w.tokens, w.kv_heads, w.head_dim), dtype=qd.dtype, device=dev)
+        kc = torch.zeros((1, w.n_slots, w.tokens, w.kv_heads, w.head_dim), dtype=qd.dtype, device=dev)
         vc = torch.zeros_like(kc)
         for f in range(w.n_slots):
-            kc[f].copy_(kd[f:f + 1]); vc[f].copy_(vd[f:f + 1])
+            kc[:, f].copy_(kd[f:f + 1]); vc[:, f].copy_(vd[f:f + 1])
         flops = WL.flops_full(w.tokens, w.tokens * w.n_slots, w.heads, w.head_dim)
         frame = [w.n_slots]
 

@@ -124,15 +124,15 @@ typedef enum {
  *
  * VDIT_ATTN_ROLLING: frame-by-frame decode with a rolling KV cache of
  *   n_slots frames (FlashDecoder Sec. 3.3).  k_cache, v_cache are
- *   [n_slots, B, Lq, n_kv_heads, D]; frame f's keys/values live in slot
+ *   [B, n_slots, Lq, n_kv_heads, D]; frame f's keys/values live in slot
  *   f mod n_slots.  If k and v are non-NULL they hold frame `frame`'s
  *   [B, Lq, n_kv_heads, D] keys/values and are first copied into that slot;
  *   if both are NULL the slot was already filled (for example by passing it
- *   as k_out of vdit_rope_qk).  q (frame `frame`'s queries, Lq = tokens per
- *   frame) then attends to the min(frame + 1, n_slots) most recent frames
- *   with no mask; Lkv is ignored.  Rotating each frame once at insertion
- *   with its absolute t gives the same scores as window-relative positions,
- *   because rotary scores depend only on position differences.
+ *   as k_out of vdit_rope_qk when B = 1).  q (frame `frame`'s queries,
+ *   Lq = tokens per frame) then attends to the min(frame + 1, n_slots) most
+ *   recent frames with no mask; Lkv is ignored.  Rotating each frame once at
+ *   insertion with its absolute t gives the same scores as window-relative
+ *   positions, because rotary scores depend only on position differences.
  *
  * VDIT_ATTN_CHUNK_HYBRID: softmax attention inside chunks of chunk_tokens
  *   tokens plus causal linear attention across chunks with running state

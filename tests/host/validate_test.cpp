@@ -65,8 +65,8 @@ int main() {
   EXPECT(bool(check_attn(b)), "rolling ok");
   b.n_slots = 0;
   EXPECT(check_attn(b).code == Check::invalid, "rolling slots");
-  b.n_slots = 9;
-  EXPECT(check_attn(b).code == Check::unsupported, "rolling max slots");
+  b.n_slots = 64;
+  EXPECT(bool(check_attn(b)), "rolling many slots");
   b.n_slots = 5; b.frame = -1;
   EXPECT(check_attn(b).code == Check::invalid, "rolling frame");
   b.frame = 0; b.k = nullptr;

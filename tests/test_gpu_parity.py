@@ -245,7 +245,7 @@ def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=Fa
     F, L, H, D = qf.values.shape
     Hk = kf.values.shape[2]
     dt = torch.bfloat16 if qf.dtype == "bf16" else torch.float32
-    kc = torch.zeros((n_slots, 1, L, Hk, D), dtype=dt, device="cuda")
+    kc = torch.zeros((1, n_slots, L, Hk, D), dtype=dt, device="cuda")
     vc = torch.zeros_like(kc)
     g = V.make_grid(1, frame_grid[1], frame_grid[2], pairs)
     qdev, kdev, vdev = to_dev(qf), to_dev(kf), to_dev(vf)
@@ -254,8 +254,8 @@ def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=Fa
         qr, _ = V.vdit_rope_qk(qdev[f:f + 1], None, g, t_offset=f)
         if prefill_slot:
             slot = f % n_slots
-            V.vdit_rope_qk(None, kdev[f:f + 1], g, k_out=kc[slot], t_offset=f)
-            vc[slot].copy_(vdev[f:f + 1])
+            V.vdit_rope_qk(None, kdev[f:f + 1], g, k_out=kc[:, slot], t_offset=f)
+            vc[:, slot].copy_(vdev[f:f + 1])
             o, lse = V.vdit_attn_fwd(qr, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
         else:
             _, kr = V.vdit_rope_qk(None, kdev[f:f + 1], g, t_offset=f)

@@ -174,7 +174,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
 
     full:    k, v [B,Lkv,Hk,D].
     ring:    k_chunks, v_chunks lists of [B,len_c,Hk,D]; workspace allocated if not given.
-    rolling: k_cache, v_cache [n_slots,B,Lq,Hk,D]; k, v = this frame's keys/values or None
+    rolling: k_cache, v_cache [B,n_slots,Lq,Hk,D]; k, v = this frame's keys/values or None
              (slot already filled); frame = stream index.
     hybrid:  k, v [B,L,Hk,D]; chunk_tokens; state_s [B,Hk,D,D], state_z [B,Hk,D] float32 (in/out).
     """
@@ -205,7 +205,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
         hk = k_cache.shape[3]
         a = _attn_args(q, k, v, mode, o, lse, scale, n_kv_heads or hk, 0)
         a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
-        a.n_slots = k_cache.shape[0]
+        a.n_slots = k_cache.shape[1]
         a.frame = frame
     elif mode == "hybrid":
         hk = k.shape[2]

@@ -177,32 +177,30 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
     }
     case VDIT_ATTN_ROLLING: {
       if (empty_q) return VDIT_OK;
-      const size_t slot_elems = size_t(a.B) * size_t(a.Lq) * size_t(a.n_kv_heads) * size_t(D);
+      // cache [B, n_slots, Lq, Hk, D]: frame f lives in slot f mod n_slots
+      const size_t frame_elems = size_t(a.Lq) * size_t(a.n_kv_heads) * size_t(D);  // one batch, one slot
       const int64_t slot = a.frame % a.n_slots;
       char* kc = static_cast<char*>(a.k_cache);
       char* vc = static_cast<char*>(a.v_cache);
-      if (a.k && a.k != kc + slot * slot_elems * es) {
-        if (auto st = from_hip(hipMemcpyAsync(kc + slot * slot_elems * es, a.k, slot_elems * es,
-                                              hipMemcpyDeviceToDevice, stream),
-                               "vdit_attn_fwd(ROLLING) k copy");
+      const size_t pitch = size_t(a.n_slots) * frame_elems * es;
+      for (int which = 0; which < 2; ++which) {
+        const void* src = which ? a.v : a.k;
+        char* dst = (which ? vc : kc) + size_t(slot) * frame_elems * es;
+        if (!src || src == dst) continue;
+        if (auto st = from_hip(hipMemcpy2DAsync(dst, pitch, src, frame_elems * es, frame_elems * es, size_t(a.B),
+                                                hipMemcpyDeviceToDevice, stream),
+                               "vdit_attn_fwd(ROLLING) cache insert");
             st != VDIT_OK)
           return st;
       }
-      if (a.v && a.v != vc + slot * slot_elems * es) {
-        if (auto st = from_hip(hipMemcpyAsync(vc + slot * slot_elems * es, a.v, slot_elems * es,
-                                              hipMemcpyDeviceToDevice, stream),
-                               "vdit_attn_fwd(ROLLING) v copy");
-            st != VDIT_OK)
-          return st;
-      }
+      // Frames 0..frame sit in slots 0..frame until the ring is full, after
+      // which every slot is valid: the valid keys of each batch are always
+      // the contiguous prefix of min(frame + 1, n_slots) slots.  Softmax
+      // attention does not depend on key order, so they are one segment.
       const int64_t nvalid = a.frame + 1 < a.n_slots ? a.frame + 1 : a.n_slots;
       vdit::AttnLaunch p = base_launch(a);
-      p.nseg = int32_t(nvalid);
-      for (int64_t i = 0; i < nvalid; ++i) {
-        const int64_t f = a.frame - nvalid + 1 + i;  // oldest first
-        const int64_t sl = f % a.n_slots;
-        p.seg[i] = {kc + sl * slot_elems * es, vc + sl * slot_elems * es, a.Lq, a.Lq * a.n_kv_heads * D};
-      }
+      p.nseg = 1;
+      p.seg[0] = {kc, vc, nvalid * a.Lq, int64_t(a.n_slots) * a.Lq * a.n_kv_heads * D};
       return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(ROLLING) launch");
     }
     case VDIT_ATTN_CHUNK_HYBRID: {

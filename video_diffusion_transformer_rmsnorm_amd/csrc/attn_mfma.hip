@@ -10,58 +10,101 @@
 // Closing the Quality Gap for Mobile Video Diffusion, review of Sec. 3.2).
 //
 // gfx950 design
-//  * Transposed scores.  Each wavefront owns QB blocks of 32 queries and
-//    computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the queries sit on
-//    the MFMA N axis (one query per lane column), keys on M.  A lane then
-//    holds 16 keys of one query per 32x32 block, so the softmax row max is a
-//    reduction inside the lane plus one exchange with lane^32, and the row
-//    rescale factor of the output is a per-lane scalar.
+//  * Transposed scores.  Each wavefront owns 32 queries and computes
+//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the queries sit on the MFMA
+//    N axis (one query per lane column), keys on M.  A lane holds 16 keys of
+//    one query per 32x32 block, so the softmax row max is a reduction inside
+//    the lane plus one exchange with lane^32, and the output rescale factor
+//    is a per-lane scalar.
 //  * Key permutation.  The K rows fed to the MFMA A operand are permuted
-//    (bits 2 and 3 of the row index swapped) so that the S^T accumulator
-//    registers 8h..8h+7 of a lane hold 8 consecutive keys.  Converted to
-//    bf16 they are directly the B operand of O^T = V^T P^T -- no shuffles
-//    between the two matrix products.
-//  * Q stays in registers for the whole kernel; K and V tiles of 64 keys
-//    are double-buffered in LDS (K row-major, V transposed to V^T[d][key]
-//    while it is written), both XOR-swizzled so the 16-byte operand reads
-//    of a wavefront are bank-conflict free.  The next tile's global loads
-//    are issued before the current tile's math and land in LDS after it:
-//    one barrier per tile.
-//  * Online softmax in log2 units (scale*log2(e) folded into one FMA before
-//    v_exp_f32); the running sum stays per lane and is combined with lane^32
-//    once at the end.
-//  * Workgroup ids are remapped so each of the 8 XCDs walks a contiguous
-//    range of (head, query-tile) work and its L2 serves one head's K/V.
+//    (bits 2 and 3 of the row index swapped) so that accumulator registers
+//    8h..8h+7 of a lane hold 8 consecutive keys: converted to bf16 they are
+//    directly the B operand of O^T = V^T P^T.
+//  * K/V tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4
+//    (no staging registers, no LDS store instructions).  Each 16-byte chunk
+//    of a row is placed at an XOR-swizzled position chosen by the source
+//    address, so the operand reads are bank-conflict free.  V stays
+//    row-major in LDS; the transposed V^T operand is read with
+//    ds_read_b64_tr_b16 (two reads per 16-key step).
+//  * Software pipeline over tiles with separate K and V double buffers: in
+//    iteration j the wavefront runs the softmax of tile j while the matrix
+//    cores compute S^T of tile j+1, then O^T += V_j^T P_j^T; K_{j+2} and
+//    V_{j+1} stream into the free buffers meanwhile.  One barrier per tile.
+//    Two wavefronts share each SIMD (<= 256 VGPRs), so one's exp/max work
+//    overlaps the other's matrix products.
+//  * Online softmax in log2 units with a lazy rescale: the running max only
+//    moves when a row's tile max exceeds it by more than 8 (so p <= 2^8),
+//    which skips the output rescale on almost every tile.
+//  * All LDS addresses are precomputed per lane; tile and buffer offsets are
+//    instruction immediates (the loop is unrolled by two over the buffer
+//    parity).  Workgroup ids are remapped so each XCD walks a contiguous
+//    range of (head, query-tile) work.
+#include <type_traits>
+
 #include "attn_epilogue.hpp"
 #include "vdit_internal.hpp"
+
+#ifndef VDIT_ATTN_WPE
+#define VDIT_ATTN_WPE 2
+#endif
+#ifndef VDIT_ATTN_SCHED
+#define VDIT_ATTN_SCHED 1
+#endif
+#ifndef VDIT_ATTN_VALU_PER_MFMA
+#define VDIT_ATTN_VALU_PER_MFMA 6
+#endif
 
 namespace vdit {
 namespace {
 
-constexpr int kBN = 64;  // keys per LDS tile
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kBN = 64;        // keys per tile
+constexpr float kLazy = 8.0f;  // rescale threshold of the running max (log2 units)
+
+// 16 bytes per lane from a buffer resource straight into LDS at M0 + 16*lane.
+// (The builtin only exists for the device pass; the host pass sees an empty
+// body, as it never runs kernel code.)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, lds_void* dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ int swap_bits23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// 16-bit element e (0..7) of a 16-byte vector
-__device__ __forceinline__ uint32_t elem16(const uint4& u, int e) {
-  const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+// Chunk swizzle of K rows: a bijection of row % 16 onto the chunk XOR mask so
+// that 16 lanes reading 16 different rows at one logical chunk hit 16
+// distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+// Chunk swizzle of V rows: the 4 rows one transposed read touches (rows
+// 4i..4i+3, 64 bytes each) land in distinct quarters of the 256-byte bank space.
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-template <int D, int QB, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void attn_mfma_kernel(AttnLaunch p, int64_t total) {
-  constexpr int NT = 64 * NW;
-  constexpr int WQ = 32 * QB;       // queries per wavefront
-  constexpr int BM = NW * WQ;       // queries per workgroup
-  constexpr int NCH = D / 8;        // 16-byte chunks per K row
+// second launch bound: workgroups per CU, i.e. VDIT_ATTN_WPE wavefronts per SIMD
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_kernel(AttnLaunch p, int64_t total) {
+  constexpr int BM = 32 * NW;       // queries per workgroup
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
-  constexpr int KPT = kBN * NCH / NT;  // keys per thread when loading a tile
-  constexpr int TILE = kBN * D;     // bf16 elements of one K (or V^T) tile
-  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "tile load mapping");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];
+  constexpr int ROWB = 2 * D;       // bytes per key row
+  constexpr int TILE_B = kBN * ROWB;
+  constexpr int RPI = 1024 / ROWB;  // rows per direct-load instruction
+  constexpr int IPW = kBN / RPI / NW;  // direct-load instructions per wavefront per tile
+  static_assert(IPW >= 1 && RPI * CPR == 64, "tile load mapping");
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_B];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -71,8 +114,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_kernel(AttnLaunch p, int
   const int64_t lid = xcd_remap(blockIdx.x, total);
   const bool hybrid = p.epi == kEpiHybrid;
   int64_t q_begin, q_end, chunk_id = 0;
-  int h, b, nseg;
-  KvSeg hseg;  // the chunk's own keys (hybrid)
+  int h, b;
+  KvSeg sg;  // the keys/values this workgroup attends to
   if (!hybrid) {
     const int64_t tiles = (p.Lq + BM - 1) / BM;
     const int64_t qt = lid % tiles, rest = lid / tiles;
@@ -80,7 +123,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_kernel(AttnLaunch p, int
     b = int(rest / p.Hq);
     q_begin = qt * BM;
     q_end = min(p.Lq, q_begin + BM);
-    nseg = p.nseg;
+    sg = p.seg[0];
+    if (p.nseg == 0) sg.len = 0;
   } else {
     const int64_t tpc = (p.chunk + BM - 1) / BM;
     const int64_t t = lid % tpc, rest = lid / tpc;
@@ -93,274 +137,298 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_kernel(AttnLaunch p, int
     q_begin = c0 + t * BM;
     q_end = min(c1, q_begin + BM);
     if (q_begin >= q_end) return;
-    nseg = 1;
-    hseg.k = static_cast<const uint16_t*>(p.hk) + c0 * p.Hk * D;
-    hseg.v = static_cast<const uint16_t*>(p.hv) + c0 * p.Hk * D;
-    hseg.len = c1 - c0;
-    hseg.bstride = p.Lq * p.Hk * D;
+    sg.k = static_cast<const uint16_t*>(p.hk) + c0 * p.Hk * D;
+    sg.v = static_cast<const uint16_t*>(p.hv) + c0 * p.Hk * D;
+    sg.len = c1 - c0;
+    sg.bstride = p.Lq * p.Hk * D;
   }
-  // segment descriptors are read from the kernel argument block (uniform)
-  auto seg_at = [&](int si) -> KvSeg { return hybrid ? hseg : p.seg[si]; };
   const int hk = h / (p.Hq / p.Hk);
+  const int64_t rs = int64_t(p.Hk) * ROWB;  // bytes between consecutive keys
 
   // ------------------------------------------------------------ Q in VGPRs --
-  bf16x8 Qr[QB][KS];
-  const int64_t qw0 = q_begin + wave * WQ;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int64_t qrow = qw0 + 32 * qb + r;
+  bf16x8 Qr[KS];
+  const int64_t qw0 = q_begin + wave * 32;
+  {
+    const int64_t qrow = qw0 + r;
     const bool ok = qrow < q_end;
     const uint16_t* src = static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.Lq + (ok ? qrow : q_begin)) * p.Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g);
       if (!ok) u = make_uint4(0, 0, 0, 0);
-      Qr[qb][ks] = __builtin_bit_cast(bf16x8, u);
+      Qr[ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
 
-  f32x16 O[DB][QB];
+  // ---------------------------------------------------- per-lane addresses --
+  // direct loads: instruction u of this wavefront fills tile rows
+  // lrow0 + u*RPI + lane/CPR, reading the chunk the swizzle puts at the lane's slot
+  const int lrow0 = wave * IPW * RPI + lane / CPR;
+  uint32_t koff[IPW], voff[IPW];
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int row = lrow0 + u * RPI;
+    const int slot = lane % CPR;
+    koff[u] = uint32_t(row) * uint32_t(rs) + uint32_t((slot ^ swz_k<D>(row)) * 16);
+    voff[u] = uint32_t(row) * uint32_t(rs) + uint32_t((slot ^ swz_v<D>(row)) * 16);
+  }
+  // K operand of S^T: row 32kb + swap23(r), logical chunk 2ks + g
+  uint32_t kaddr[KS];
+  {
+    const int row = swap_bits23(r);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = uint32_t(row * ROWB + (((2 * ks + g) ^ swz_k<D>(row)) * 16));
+  }
+  // V^T operand via transposed reads: in each 16-lane group, source lane
+  // s = 4*rho + q reads row (16kk + 8g + 4h + rho), channels d0 + 4q .. +3
+  // with d0 = 32db + 16*((lane/16)&1); the destination lane gets 4 keys of
+  // channel d0 + lane%16.
+  uint32_t vaddr[DB];
+  {
+    const int s16 = lane & 15, rho = s16 >> 2, q4 = s16 & 3;
+    const int rowo = 8 * g + rho;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * q4;
+      const int chunk = d >> 3;
+      vaddr[db] = uint32_t(rowo * ROWB + ((chunk ^ swz_v<D>(rowo)) * 16) + (d & 7) * 2);
+    }
+  }
+
+  // ---------------------------------------------------------- tile issue --
+  const int len = int(sg.len);
+  const int ntiles = (len + kBN - 1) / kBN;
+  const char* kbase = reinterpret_cast<const char*>(sg.k) + (int64_t(b) * sg.bstride + int64_t(hk) * D) * 2;
+  const char* vbase = reinterpret_cast<const char*>(sg.v) + (int64_t(b) * sg.bstride + int64_t(hk) * D) * 2;
+  // Tile `tile` of K or V -> LDS buffer via buffer_load_dwordx4 ... lds.  The
+  // buffer resource starts at the tile and covers only the keys that exist,
+  // so rows past the end of the sequence read as zeros (their scores are
+  // masked to -inf): no special tail path and no 64-bit address VGPRs.
+  auto issue = [&](int tile, bool is_v, int buf) {
+    const int j0 = tile * kBN;
+    const char* tb = (is_v ? vbase : kbase) + int64_t(j0) * rs;
+    int64_t avail = int64_t(len - 1 - j0) * rs + ROWB;  // bytes of existing keys from the tile start
+    avail = avail < 0x7fffffff ? avail : 0x7fffffff;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(tb), (short)0, __builtin_amdgcn_readfirstlane(int(avail)), 0x00020000);
+    char* lb = lds + (is_v ? 2 + buf : buf) * TILE_B + wave * IPW * 1024;
+#pragma unroll
+    for (int u = 0; u < IPW; ++u)
+      buffer_load_lds16(rsrc, (lds_void*)(lb + u * 1024), is_v ? voff[u] : koff[u]);
+  };
+
+  f32x16 O[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) O[db][qb][i] = 0.f;
-  float m2[QB], lsum[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m2[qb] = -INFINITY; lsum[qb] = 0.f; }
-
-  // ------------------------------------------------------ tile bookkeeping --
-  int ntiles = 0;
-  for (int s = 0; s < nseg; ++s) ntiles += int((seg_at(s).len + kBN - 1) / kBN);
-
-  const int lrow0 = KPT * (tid / NCH);  // first key row this thread loads
-  const int lch = tid % NCH;            // 16-byte chunk (8 channels) it loads
-  uint4 kreg[KPT], vreg[KPT];
-
-  auto load_tile = [&](int si, int64_t j0) {
-    const KvSeg sg = seg_at(si);
-    const int64_t nv = sg.len - j0;
-    const uint16_t* kb = static_cast<const uint16_t*>(sg.k) + int64_t(b) * sg.bstride + int64_t(hk) * D + lch * 8;
-    const uint16_t* vb = static_cast<const uint16_t*>(sg.v) + int64_t(b) * sg.bstride + int64_t(hk) * D + lch * 8;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int key = lrow0 + u;
-      if (key < nv) {
-        const int64_t off = (j0 + key) * p.Hk * D;
-        kreg[u] = *reinterpret_cast<const uint4*>(kb + off);
-        vreg[u] = *reinterpret_cast<const uint4*>(vb + off);
-      } else {
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    uint16_t* Kl = lds + buf * 2 * TILE;
-    uint16_t* Vl = Kl + TILE;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int key = lrow0 + u;
-      const int phys = lch ^ (swap_bits23(key & 31) & (NCH - 1));
-      *reinterpret_cast<uint4*>(Kl + key * D + phys * 8) = kreg[u];
-    }
-    // V^T[d][key]: KPT consecutive keys of one channel per store
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = lch * 8 + e;
-      const int phys = (lrow0 >> 3) ^ ((d + (d >> 3)) & 7);
-      uint16_t* dst = Vl + d * kBN + phys * 8 + (lrow0 & 7);
-      if constexpr (KPT == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = elem16(vreg[0], e) | (elem16(vreg[1], e) << 16);
-      } else if constexpr (KPT == 4) {
-        uint2 w;
-        w.x = elem16(vreg[0], e) | (elem16(vreg[1], e) << 16);
-        w.y = elem16(vreg[2], e) | (elem16(vreg[3], e) << 16);
-        *reinterpret_cast<uint2*>(dst) = w;
-      } else {
-        uint4 w;
-        w.x = elem16(vreg[0], e) | (elem16(vreg[1], e) << 16);
-        w.y = elem16(vreg[2], e) | (elem16(vreg[3], e) << 16);
-        w.z = elem16(vreg[4], e) | (elem16(vreg[5], e) << 16);
-        w.w = elem16(vreg[6], e) | (elem16(vreg[7], e) << 16);
-        *reinterpret_cast<uint4*>(dst) = w;
-      }
-    }
-  };
-
+    for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
+  float m2 = -INFINITY, lsum = 0.f;
   const float c2 = p.scale_log2;
-  int cur_s = 0;
-  int64_t cur_j = 0;
-  int64_t cur_len = 0;
-  if (ntiles > 0) {
-    while (seg_at(cur_s).len == 0) ++cur_s;
-    cur_len = seg_at(cur_s).len;
-    load_tile(cur_s, cur_j);
-    store_tile(0);
-  }
-  __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int nv = int(min<int64_t>(kBN, cur_len - cur_j));
-    // next tile
-    int nxt_s = cur_s;
-    int64_t nxt_j = cur_j + kBN;
-    int64_t nxt_len = cur_len;
-    if (t + 1 < ntiles) {
-      if (nxt_j >= nxt_len) {
-        nxt_j = 0;
-        ++nxt_s;
-        while (seg_at(nxt_s).len == 0) ++nxt_s;
-        nxt_len = seg_at(nxt_s).len;
-      }
-      load_tile(nxt_s, nxt_j);
-    }
-
-    const uint16_t* Kl = lds + (t & 1) * 2 * TILE;
-    const uint16_t* Vl = Kl + TILE;
-
-    // S^T = K Q^T for two 32-key blocks
-    f32x16 S[2][QB];
+  // S^T of the tile in K buffer `buf` (unmasked)
+  auto qk = [&](int buf, f32x16* S) {
+    const char* Kl = lds + buf * TILE_B;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[kb][qb][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + swap_bits23(r);
-        const int phys = (2 * ks + g) ^ (swap_bits23(row & 31) & (NCH - 1));
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + row * D + phys * 8);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[qb][ks], S[kb][qb], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + kaddr[ks] + kb * 32 * ROWB);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[ks], S[kb], 0, 0, 0);
       }
-    }
+  };
+
+  // mask keys >= nv of a tail tile, then the tile row max -> lazy rescale
+  auto row_max = [&](f32x16* S, int nv) {
     if (nv < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key >= nv) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) S[kb][qb][i] = -INFINITY;
-          }
+          if (key >= nv) S[kb][i] = -INFINITY;
         }
     }
-
-    // online softmax (log2 units), P^T in bf16 as the next B operands
-    bf16x8 P[2][QB][2];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][qb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m2[qb], mx * c2);
-      const float alpha = fast_exp2(m2[qb] - mn);
-      m2[qb] = mn;
-      lsum[qb] *= alpha;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mcand = mx * c2;
+    const bool grow = mcand > m2 + kLazy;
+    if (__ballot(grow)) {
+      const float mn = grow ? mcand : m2;
+      const float alpha = fast_exp2(m2 - mn);
+      m2 = mn;
+      lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) O[db][qb][i] *= alpha;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x8 pv;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float e = fast_exp2(fmaf(S[kb][qb][8 * hh + j], c2, -mn));
-            ls += e;
-            pv[j] = static_cast<__bf16>(e);
-          }
-          P[kb][qb][hh] = pv;
-        }
-      lsum[qb] += ls;
+        for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
     }
+  };
 
-    // O^T += V^T P^T
+  // p = 2^(s*c2 - m2) -> P (bf16 B operands); row sum as a shallow tree
+  auto exps = [&](const f32x16* S, bf16x8 (*P)[2]) {
+    const float mn = m2;
+    float part[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(S[kb][8 * hh + j], c2, -mn));
+        bf16x8 pv8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv8[j] = static_cast<__bf16>(e[j]);
+        P[kb][hh] = pv8;
+        part[2 * kb + hh] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
+    lsum += (part[0] + part[1]) + (part[2] + part[3]);
+    // materialise the sum here: otherwise the compiler sinks these adds into
+    // the next tile and keeps all 32 exponentials live across the PV MFMAs
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(lsum));  // (a VGPR constraint exists only in the device pass)
+#endif
+  };
+
+  // O^T += V^T P^T with V from V buffer `buf`
+  auto pv = [&](int buf, bf16x8 (*P)[2]) {
+    const char* Vl = lds + (2 + buf) * TILE_B;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = 32 * db + r;
-        const int phys = (2 * kk + g) ^ ((d + (d >> 3)) & 7);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vl + d * kBN + phys * 8);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[kk >> 1][qb][kk & 1], O[db][qb], 0, 0, 0);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk) * ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk + 4) * ROWB));
+        const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kk >> 1][kk & 1], O[db], 0, 0, 0);
       }
-    }
+  };
 
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
+  // Instruction interleave of one tile's math block: the QK^T MFMAs of the
+  // next tile are spread through the exp/convert VALU work of this tile (the
+  // wavefront issues in order, so VALU work only overlaps the matrix cores
+  // when it sits between MFMAs), then the PV MFMAs with their V reads.
+  // Instruction interleave of one tile's math, in two regions.  Region A: the
+  // QK^T MFMAs of the next tile spread through this tile's exp/convert VALU
+  // work (a wavefront issues in order, so VALU work overlaps the matrix
+  // cores only when it sits between MFMAs), K operand reads one step ahead.
+  // Region B: the PV MFMAs with their transposed V reads two steps ahead.
+  auto schedule_a = [&]() {
+#if VDIT_ATTN_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VDIT_ATTN_VALU_PER_MFMA, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
+  };
+  auto schedule_b = [&]() {
+#if VDIT_ATTN_SCHED
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+#endif
+  };
+
+  auto wait_and_sync = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur_s = nxt_s;
-    cur_j = nxt_j;
-    cur_len = nxt_len;
+  };
+
+  if (ntiles > 0) {
+    // prologue: K_0, V_0, K_1 in flight; S^T of tile 0
+    issue(0, false, 0);
+    issue(0, true, 0);
+    if (ntiles > 1) issue(1, false, 1);
+    wait_and_sync();
+    f32x16 S[2];
+    qk(0, S);
+    __syncthreads();
+
+    auto iteration = [&](int t, auto parity) {
+      constexpr int P0 = decltype(parity)::value;
+      // stream K_{t+2} into K buffer P0 and V_{t+1} into V buffer 1-P0
+      if (t + 2 < ntiles) issue(t + 2, false, P0);
+      if (t + 1 < ntiles) issue(t + 1, true, 1 - P0);
+      row_max(S, min(kBN, len - t * kBN));
+      // math block: exps of tile t || S^T of tile t+1 (computed on the last
+      // tile too, on stale LDS data, and discarded), then O^T += V^T P^T
+      f32x16 Sn[2];
+      qk(1 - P0, Sn);
+      bf16x8 P[2][2];
+      exps(S, P);
+      schedule_a();
+      __builtin_amdgcn_sched_barrier(0);
+      pv(P0, P);
+      schedule_b();
+      S[0] = Sn[0];
+      S[1] = Sn[1];
+      wait_and_sync();
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      iteration(t, std::integral_constant<int, 0>{});
+      iteration(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntiles) iteration(t, std::integral_constant<int, 0>{});
   }
 
   // -------------------------------------------------------------- epilogue --
-  float inv[QB], lse_s[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lsum[qb] + __shfl_xor(lsum[qb], 32);
-    inv[qb] = lt > 0.f ? 1.f / lt : 0.f;
-    lse_s[qb] = partial_lse(m2[qb], lt);
-  }
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_s = partial_lse(m2, lt);
+  const int64_t q = qw0 + r;
 
   if (p.epi == kEpiPlain || p.epi == kEpiRing) {
+    if (q >= q_end) return;
+    const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
+    const int64_t lrowi = (int64_t(b) * p.Hq + h) * p.Lq + q;
+    float wa = 0.f, wb = inv, lse_out = lse_s;
+    const bool merge_prev = p.epi == kEpiRing && p.has_prev;
+    if (merge_prev) {
+      const MergeW w = merge_weights(p.part_lse[lrowi], lse_s);
+      wa = w.wa;
+      wb = w.wb * inv;
+      lse_out = w.lse;
+    }
+    const bool to_part = p.epi == kEpiRing && !p.final_out;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int64_t q = qw0 + 32 * qb + r;
-      if (q >= q_end) continue;
-      const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
-      const int64_t lrow = (int64_t(b) * p.Hq + h) * p.Lq + q;
-      float wa = 0.f, wb = inv[qb], lse_out = lse_s[qb];
-      const bool merge_prev = p.epi == kEpiRing && p.has_prev;
-      if (merge_prev) {
-        const MergeW w = merge_weights(p.part_lse[lrow], lse_s[qb]);
-        wa = w.wa;
-        wb = w.wb * inv[qb];
-        lse_out = w.lse;
-      }
-      const bool to_part = p.epi == kEpiRing && !p.final_out;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * g;
+        float y[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = 32 * db + 8 * i4 + 4 * g;
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = O[db][qb][4 * i4 + e] * wb;
-          if (merge_prev) {
-            const float4 pv = *reinterpret_cast<const float4*>(p.part_o + orow + d);
-            y[0] = fmaf(wa, pv.x, y[0]); y[1] = fmaf(wa, pv.y, y[1]);
-            y[2] = fmaf(wa, pv.z, y[2]); y[3] = fmaf(wa, pv.w, y[3]);
-          }
-          if (to_part) {
-            *reinterpret_cast<float4*>(p.part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
-          } else {
-            uint2 w;
-            w.x = pack_bf16x2(y[0], y[1]);
-            w.y = pack_bf16x2(y[2], y[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
-          }
+        for (int e = 0; e < 4; ++e) y[e] = O[db][4 * i4 + e] * wb;
+        if (merge_prev) {
+          const float4 pv4 = *reinterpret_cast<const float4*>(p.part_o + orow + d);
+          y[0] = fmaf(wa, pv4.x, y[0]); y[1] = fmaf(wa, pv4.y, y[1]);
+          y[2] = fmaf(wa, pv4.z, y[2]); y[3] = fmaf(wa, pv4.w, y[3]);
         }
-      if (g == 0) {
-        if (to_part) p.part_lse[lrow] = lse_out;
-        else if (p.lse) p.lse[lrow] = lse_out;
+        if (to_part) {
+          *reinterpret_cast<float4*>(p.part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
+        } else {
+          uint2 w;
+          w.x = pack_bf16x2(y[0], y[1]);
+          w.y = pack_bf16x2(y[2], y[3]);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
+        }
       }
+    if (g == 0) {
+      if (to_part) p.part_lse[lrowi] = lse_out;
+      else if (p.lse) p.lse[lrowi] = lse_out;
     }
     return;
   }
@@ -372,65 +440,48 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_kernel(AttnLaunch p, int
   const uint16_t* st_hi = static_cast<const uint16_t*>(p.st) + sidx * D * D;
   const uint16_t* st_lo = st_hi + plane;
   const float* z = p.zc + sidx * D;
-  float den[QB];
-  bf16x8 Fq[QB][KS];
+  bf16x8 Fq[KS];
+  float dn = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float dn = 0.f;
+  for (int ks = 0; ks < KS; ++ks) {
+    const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
+    const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
+    const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+    bf16x8 f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
-      const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
-      const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
-      bf16x8 f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = phi_elu1(static_cast<float>(Qr[qb][ks][j]));
-        dn = fmaf(x, zz[j], dn);
-        f[j] = static_cast<__bf16>(x);
-      }
-      Fq[qb][ks] = f;
+    for (int j = 0; j < 8; ++j) {
+      const float x = phi_elu1(static_cast<float>(Qr[ks][j]));
+      dn = fmaf(x, zz[j], dn);
+      f[j] = static_cast<__bf16>(x);
     }
-    den[qb] = dn + __shfl_xor(dn, 32);
+    Fq[ks] = f;
   }
-  MergeW w[QB];
-  float inv_den[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lse_l = den[qb] > 0.f ? logf(den[qb]) : -INFINITY;
-    w[qb] = merge_weights(lse_s[qb], lse_l);
-    inv_den[qb] = den[qb] > 0.f ? 1.f / den[qb] : 0.f;
-  }
+  const float den = dn + __shfl_xor(dn, 32);
+  const float lse_l = den > 0.f ? logf(den) : -INFINITY;
+  const MergeW w = merge_weights(lse_s, lse_l);
+  const float inv_den = den > 0.f ? 1.f / den : 0.f;
+  const float ws = w.wa * inv, wl = w.wb * inv_den;
+  const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    f32x16 A[QB];
+    f32x16 A;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) A[qb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) A[i] = 0.f;
     const int dout = 32 * db + r;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 ah = *reinterpret_cast<const bf16x8*>(st_hi + dout * D + 16 * ks + 8 * g);
       const bf16x8 al = *reinterpret_cast<const bf16x8*>(st_lo + dout * D + 16 * ks + 8 * g);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        A[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, Fq[qb][ks], A[qb], 0, 0, 0);
-        A[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, Fq[qb][ks], A[qb], 0, 0, 0);
-      }
+      A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, Fq[ks], A, 0, 0, 0);
+      A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, Fq[ks], A, 0, 0, 0);
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int64_t q = qw0 + 32 * qb + r;
-      if (q >= q_end) continue;
-      const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
-      const float ws = w[qb].wa * inv[qb], wl = w[qb].wb * inv_den[qb];
+    if (q < q_end) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = 32 * db + 8 * i4 + 4 * g;
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = ws * O[db][qb][4 * i4 + e] + wl * A[qb][4 * i4 + e];
+        for (int e = 0; e < 4; ++e) y[e] = ws * O[db][4 * i4 + e] + wl * A[4 * i4 + e];
         uint2 u;
         u.x = pack_bf16x2(y[0], y[1]);
         u.y = pack_bf16x2(y[2], y[3]);
@@ -438,37 +489,30 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_kernel(AttnLaunch p, int
       }
     }
   }
-  if (p.lse && g == 0) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int64_t q = qw0 + 32 * qb + r;
-      if (q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = w[qb].lse;
-    }
-  }
+  if (p.lse && g == 0 && q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = w.lse;
 }
 
-template <int D, int QB, int NW>
+template <int D, int NW>
 hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
-  constexpr int BM = NW * 32 * QB;
+  constexpr int BM = NW * 32;
   int64_t total;
   if (p.epi == kEpiHybrid) total = ((p.chunk + BM - 1) / BM) * p.n_chunks * p.Hq * p.B;
   else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, QB, NW>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
-  // Large query sets: 64 queries per wavefront (each K/V operand read from
-  // LDS feeds two MFMAs).  Small ones (one frame of a stream, short chunks):
-  // 32 per wavefront so the grid still covers the 256 CUs.
+  // 128 queries per workgroup (4 wavefronts); problems too small to fill the
+  // 256 CUs twice over use 64-query workgroups.
   const int64_t rows = (p.epi == kEpiHybrid ? p.chunk : p.Lq);
-  const int64_t work256 = ((rows + 255) / 256) * p.Hq * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1);
-  const bool big = work256 >= 512;
-  if (p.D == 128) return big ? launch_cfg<128, 2, 4>(p, s) : launch_cfg<128, 1, 4>(p, s);
-  return big ? launch_cfg<64, 2, 4>(p, s) : launch_cfg<64, 1, 4>(p, s);
+  const int64_t wg128 = ((rows + 127) / 128) * p.Hq * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1);
+  const bool big = wg128 >= 512;
+  if (p.D == 128) return big ? launch_cfg<128, 4>(p, s) : launch_cfg<128, 2>(p, s);
+  return big ? launch_cfg<64, 4>(p, s) : launch_cfg<64, 2>(p, s);
 }
 
 }  // namespace vdit

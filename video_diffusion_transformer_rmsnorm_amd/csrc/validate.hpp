@@ -119,7 +119,6 @@ struct AttnArgs {
 };
 
 constexpr int kMaxRingChunks = 64;
-constexpr int kMaxSlots = 8;  // rolling-window frames handled in one launch
 
 // Workspace layout of the chunk-hybrid mode (byte offsets from the workspace
 // base, each region 256-byte aligned):
@@ -222,7 +221,6 @@ inline CheckResult check_attn(const AttnArgs& a) {
     }
     case 2: {  // ROLLING
       if (a.n_slots < 1) return CheckResult::bad("ROLLING needs n_slots >= 1");
-      if (a.n_slots > kMaxSlots) return CheckResult::unsup("ROLLING supports at most 8 slots");
       if (a.frame < 0) return CheckResult::bad("frame must be >= 0");
       if (!empty_q) {
         if (!a.k_cache || !a.v_cache) return CheckResult::bad("ROLLING needs k_cache and v_cache");
