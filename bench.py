@@ -224,6 +224,22 @@ def bench_other(args):
             "data": "synthetic", "config": {"workload": w.name, "mode": w.mode, "reference_only": True}}
 
 
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of a profiler run: each launch reads and
+    writes exactly nbytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,11 +249,16 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows of the oracle's timed sample")
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the layer's sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.workload != 2:
         print(json.dumps(bench_other(args)), flush=True)
         return

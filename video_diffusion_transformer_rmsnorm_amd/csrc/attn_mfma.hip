@@ -51,7 +51,13 @@
 #define VDIT_ATTN_SCHED 1
 #endif
 #ifndef VDIT_ATTN_VALU_PER_MFMA
-#define VDIT_ATTN_VALU_PER_MFMA 6
+#define VDIT_ATTN_VALU_PER_MFMA 4
+#endif
+#ifndef VDIT_ATTN_KPREF
+#define VDIT_ATTN_KPREF 3  // K operand reads issued ahead of their MFMA
+#endif
+#ifndef VDIT_ATTN_VPREF
+#define VDIT_ATTN_VPREF 2  // V^T operand read pairs issued ahead of their MFMA
 #endif
 
 namespace vdit {
@@ -72,6 +78,15 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, l
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
 #endif
+}
+
+// Value of lane l ^ 32 (the other 32-lane half), via v_permlane32_swap on
+// (x, x): of the two results one is this lane's own x and the other the
+// partner's, so pick the one that differs (equal bits: either is correct).
+__device__ __forceinline__ float other_half(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0] == u ? r[1] : r[0]);
 }
 
 __device__ __forceinline__ int swap_bits23(int x) {
@@ -100,14 +115,24 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
   constexpr int ROWB = 2 * D;       // bytes per key row
-  constexpr int TILE_B = kBN * ROWB;
-  constexpr int RPI = 1024 / ROWB;  // rows per direct-load instruction
-  constexpr int IPW = kBN / RPI / NW;  // direct-load instructions per wavefront per tile
+  constexpr int TILE_B = kBN * ROWB;  // V tile bytes
+  constexpr int RPI = 1024 / ROWB;  // V rows per direct-load instruction
+  constexpr int IPW = kBN / RPI / NW;  // V direct-load instructions per wavefront per tile
   static_assert(IPW >= 1 && RPI * CPR == 64, "tile load mapping");
-  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_B];  // K0 K1 V0 V1
+  // K rows are padded by one 16-byte chunk: rows land 16 bytes apart in the
+  // bank space (conflict-free operand reads) and every operand address is a
+  // per-lane base plus a compile-time offset.
+  constexpr int KCPR = CPR + 1;                 // chunk slots per padded K row
+  constexpr int KROWB = 16 * KCPR;
+  constexpr int KTILE_B = kBN * KROWB;
+  constexpr int KI = KTILE_B / 1024;            // K direct-load instructions per tile
+  constexpr int KIW = (KI + NW - 1) / NW;       // ... per wavefront (at most)
+  static_assert(KTILE_B % 1024 == 0, "padded K tile is whole 1 KB blocks");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * KTILE_B + 2 * TILE_B];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 5, r = lane & 31;
 
   // ---------------------------------------------------------------- work --
@@ -161,24 +186,25 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   }
 
   // ---------------------------------------------------- per-lane addresses --
-  // direct loads: instruction u of this wavefront fills tile rows
-  // lrow0 + u*RPI + lane/CPR, reading the chunk the swizzle puts at the lane's slot
+  // direct loads.  K: instruction u (= wave + NW*i) fills padded slots
+  // 64u + lane, i.e. row s / KCPR, chunk s % KCPR (the pad slot re-reads the
+  // row's last chunk).  V: instruction u of this wavefront fills rows
+  // lrow0 + u*RPI + lane/CPR, reading the chunk the swizzle puts at the slot.
+  uint32_t koff[KIW], voff[IPW];
+#pragma unroll
+  for (int i = 0; i < KIW; ++i) {
+    const int slot = 64 * (wave + NW * i) + lane;
+    const int row = slot / KCPR, col = min(slot % KCPR, CPR - 1);
+    koff[i] = uint32_t(row) * uint32_t(rs) + uint32_t(col * 16);
+  }
   const int lrow0 = wave * IPW * RPI + lane / CPR;
-  uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int u = 0; u < IPW; ++u) {
     const int row = lrow0 + u * RPI;
-    const int slot = lane % CPR;
-    koff[u] = uint32_t(row) * uint32_t(rs) + uint32_t((slot ^ swz_k<D>(row)) * 16);
-    voff[u] = uint32_t(row) * uint32_t(rs) + uint32_t((slot ^ swz_v<D>(row)) * 16);
+    voff[u] = uint32_t(row) * uint32_t(rs) + uint32_t(((lane % CPR) ^ swz_v<D>(row)) * 16);
   }
-  // K operand of S^T: row 32kb + swap23(r), logical chunk 2ks + g
-  uint32_t kaddr[KS];
-  {
-    const int row = swap_bits23(r);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kaddr[ks] = uint32_t(row * ROWB + (((2 * ks + g) ^ swz_k<D>(row)) * 16));
-  }
+  // K operand of S^T: row 32kb + swap23(r), chunk 2ks + g
+  const uint32_t kaddr = uint32_t(swap_bits23(r) * KROWB + g * 16);
   // V^T operand via transposed reads: in each 16-lane group, source lane
   // s = 4*rho + q reads row (16kk + 8g + 4h + rho), channels d0 + 4q .. +3
   // with d0 = 32db + 16*((lane/16)&1); the destination lane gets 4 keys of
@@ -211,10 +237,18 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     avail = avail < 0x7fffffff ? avail : 0x7fffffff;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(tb), (short)0, __builtin_amdgcn_readfirstlane(int(avail)), 0x00020000);
-    char* lb = lds + (is_v ? 2 + buf : buf) * TILE_B + wave * IPW * 1024;
+    if (is_v) {
+      char* lb = lds + 2 * KTILE_B + buf * TILE_B + wave * IPW * 1024;
 #pragma unroll
-    for (int u = 0; u < IPW; ++u)
-      buffer_load_lds16(rsrc, (lds_void*)(lb + u * 1024), is_v ? voff[u] : koff[u]);
+      for (int u = 0; u < IPW; ++u) buffer_load_lds16(rsrc, (lds_void*)(lb + u * 1024), voff[u]);
+    } else {
+      char* lb = lds + buf * KTILE_B;
+#pragma unroll
+      for (int i = 0; i < KIW; ++i) {
+        const int u = wave + NW * i;
+        if (u < KI) buffer_load_lds16(rsrc, (lds_void*)(lb + u * 1024), koff[i]);
+      }
+    }
   };
 
   f32x16 O[DB];
@@ -227,7 +261,7 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
 
   // S^T of the tile in K buffer `buf` (unmasked)
   auto qk = [&](int buf, f32x16* S) {
-    const char* Kl = lds + buf * TILE_B;
+    const char* Kl = lds + buf * KTILE_B + kaddr;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -236,13 +270,30 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + kaddr[ks] + kb * 32 * ROWB);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + ks * 32 + kb * 32 * KROWB);
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[ks], S[kb], 0, 0, 0);
       }
   };
 
   // mask keys >= nv of a tail tile, then the tile row max -> lazy rescale
-  auto row_max = [&](f32x16* S, int nv) {
+  // lane-local max of a tile's 32 scores (a 4-level max3 tree)
+  auto lane_max = [&](const f32x16* S) -> float {
+    float a[11];
+#pragma unroll
+    for (int j = 0; j < 10; ++j) {
+      const int i0 = 3 * j, i1 = 3 * j + 1, i2 = 3 * j + 2;
+      a[j] = fmaxf(fmaxf(S[i0 >> 4][i0 & 15], S[i1 >> 4][i1 & 15]), S[i2 >> 4][i2 & 15]);
+    }
+    a[10] = fmaxf(S[1][14], S[1][15]);
+    const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+    const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
+    return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
+  };
+
+  // row max of tile scores S (lane max mx precomputed on unmasked scores):
+  // mask the keys >= nv of a tail tile, combine the two lane halves, then the
+  // lazy rescale
+  auto row_max = [&](f32x16* S, float mx, int nv) {
     if (nv < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -251,13 +302,9 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
           const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
           if (key >= nv) S[kb][i] = -INFINITY;
         }
+      mx = lane_max(S);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, other_half(mx));
     const float mcand = mx * c2;
     const bool grow = mcand > m2 + kLazy;
     if (__ballot(grow)) {
@@ -299,7 +346,7 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
 
   // O^T += V^T P^T with V from V buffer `buf`
   auto pv = [&](int buf, bf16x8 (*P)[2]) {
-    const char* Vl = lds + (2 + buf) * TILE_B;
+    const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -322,7 +369,7 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   // Region B: the PV MFMAs with their transposed V reads two steps ahead.
   auto schedule_a = [&]() {
 #if VDIT_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, VDIT_ATTN_KPREF, 0);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -333,11 +380,12 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   };
   auto schedule_b = [&]() {
 #if VDIT_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VDIT_ATTN_VPREF, 1);
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);
     }
 #endif
   };
@@ -355,6 +403,7 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     wait_and_sync();
     f32x16 S[2];
     qk(0, S);
+    float mx = lane_max(S);
     __syncthreads();
 
     auto iteration = [&](int t, auto parity) {
@@ -362,16 +411,21 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
       // stream K_{t+2} into K buffer P0 and V_{t+1} into V buffer 1-P0
       if (t + 2 < ntiles) issue(t + 2, false, P0);
       if (t + 1 < ntiles) issue(t + 1, true, 1 - P0);
-      row_max(S, min(kBN, len - t * kBN));
-      // math block: exps of tile t || S^T of tile t+1 (computed on the last
-      // tile too, on stale LDS data, and discarded), then O^T += V^T P^T
+      row_max(S, mx, min(kBN, len - t * kBN));
+      // region A: exps of tile t || S^T of tile t+1 (computed on the last
+      // tile too, on stale LDS data, and discarded)
       f32x16 Sn[2];
       qk(1 - P0, Sn);
       bf16x8 P[2][2];
       exps(S, P);
       schedule_a();
       __builtin_amdgcn_sched_barrier(0);
+      // region B: O^T += V^T P^T || lane max of tile t+1's scores
       pv(P0, P);
+      mx = lane_max(Sn);
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" : "+v"(mx));  // keep the max here, among the PV MFMAs
+#endif
       schedule_b();
       S[0] = Sn[0];
       S[1] = Sn[1];
@@ -386,7 +440,7 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   }
 
   // -------------------------------------------------------------- epilogue --
-  const float lt = lsum + __shfl_xor(lsum, 32);
+  const float lt = lsum + other_half(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse_s = partial_lse(m2, lt);
   const int64_t q = qw0 + r;
@@ -456,7 +510,7 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     }
     Fq[ks] = f;
   }
-  const float den = dn + __shfl_xor(dn, 32);
+  const float den = dn + other_half(dn);
   const float lse_l = den > 0.f ? logf(den) : -INFINITY;
   const MergeW w = merge_weights(lse_s, lse_l);
   const float inv_den = den > 0.f ? 1.f / den : 0.f;
