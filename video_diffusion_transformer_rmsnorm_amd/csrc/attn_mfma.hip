@@ -44,8 +44,8 @@
 #include "attn_epilogue.hpp"
 #include "vdit_internal.hpp"
 
-#ifndef VDIT_ATTN_WPE
-#define VDIT_ATTN_WPE 2
+#ifndef VDIT_ATTN_BIG_QB
+#define VDIT_ATTN_BIG_QB 1  // query blocks per wavefront for large problems (2: one wavefront per SIMD)
 #endif
 #ifndef VDIT_ATTN_SCHED
 #define VDIT_ATTN_SCHED 1
@@ -107,10 +107,13 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// second launch bound: workgroups per CU, i.e. VDIT_ATTN_WPE wavefronts per SIMD
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_kernel(AttnLaunch p, int64_t total) {
-  constexpr int BM = 32 * NW;       // queries per workgroup
+// QB blocks of 32 queries per wavefront.  QB = 1: two wavefronts per SIMD
+// (<= 256 registers each); QB = 2: one wavefront per SIMD with 512 registers,
+// every K / V^T operand read from LDS feeding two MFMAs (half the LDS traffic
+// per FLOP).  Second launch bound: workgroups per CU.
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_kernel(AttnLaunch p, int64_t total) {
+  constexpr int BM = 32 * NW * QB;  // queries per workgroup
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -171,17 +174,18 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   const int64_t rs = int64_t(p.Hk) * ROWB;  // bytes between consecutive keys
 
   // ------------------------------------------------------------ Q in VGPRs --
-  bf16x8 Qr[KS];
-  const int64_t qw0 = q_begin + wave * 32;
-  {
-    const int64_t qrow = qw0 + r;
+  bf16x8 Qr[QB][KS];
+  const int64_t qw0 = q_begin + wave * 32 * QB;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t qrow = qw0 + 32 * qb + r;
     const bool ok = qrow < q_end;
     const uint16_t* src = static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.Lq + (ok ? qrow : q_begin)) * p.Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 u = *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g);
       if (!ok) u = make_uint4(0, 0, 0, 0);
-      Qr[ks] = __builtin_bit_cast(bf16x8, u);
+      Qr[qb][ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
 
@@ -251,101 +255,126 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     }
   };
 
-  f32x16 O[DB];
+  f32x16 O[DB][QB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) O[db][i] = 0.f;
-  float m2 = -INFINITY, lsum = 0.f;
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) O[db][qb][i] = 0.f;
+  float m2[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m2[qb] = -INFINITY; lsum[qb] = 0.f; }
   const float c2 = p.scale_log2;
 
-  // S^T of the tile in K buffer `buf` (unmasked)
-  auto qk = [&](int buf, f32x16* S) {
+  // S^T of the tile in K buffer `buf` (unmasked); each K operand feeds QB MFMAs
+  auto qk = [&](int buf, f32x16 (*S)[QB]) {
     const char* Kl = lds + buf * KTILE_B + kaddr;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb][qb][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + ks * 32 + kb * 32 * KROWB);
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[ks], S[kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[qb][ks], S[kb][qb], 0, 0, 0);
       }
   };
 
-  // mask keys >= nv of a tail tile, then the tile row max -> lazy rescale
-  // lane-local max of a tile's 32 scores (a 4-level max3 tree)
-  auto lane_max = [&](const f32x16* S) -> float {
+  // lane-local max of one query block's 32 tile scores (a 4-level max3 tree)
+  auto lane_max = [&](f32x16 (*S)[QB], int qb) -> float {
     float a[11];
 #pragma unroll
     for (int j = 0; j < 10; ++j) {
       const int i0 = 3 * j, i1 = 3 * j + 1, i2 = 3 * j + 2;
-      a[j] = fmaxf(fmaxf(S[i0 >> 4][i0 & 15], S[i1 >> 4][i1 & 15]), S[i2 >> 4][i2 & 15]);
+      a[j] = fmaxf(fmaxf(S[i0 >> 4][qb][i0 & 15], S[i1 >> 4][qb][i1 & 15]), S[i2 >> 4][qb][i2 & 15]);
     }
-    a[10] = fmaxf(S[1][14], S[1][15]);
+    a[10] = fmaxf(S[1][qb][14], S[1][qb][15]);
     const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
     const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
     return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
   };
 
-  // row max of tile scores S (lane max mx precomputed on unmasked scores):
+  // row max of tile scores S (lane maxima mx precomputed on unmasked scores):
   // mask the keys >= nv of a tail tile, combine the two lane halves, then the
   // lazy rescale
-  auto row_max = [&](f32x16* S, float mx, int nv) {
+  auto row_max = [&](f32x16 (*S)[QB], float* mx, int nv) {
     if (nv < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
-          if (key >= nv) S[kb][i] = -INFINITY;
+          if (key >= nv) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) S[kb][qb][i] = -INFINITY;
+          }
         }
-      mx = lane_max(S);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = lane_max(S, qb);
     }
-    mx = fmaxf(mx, other_half(mx));
-    const float mcand = mx * c2;
-    const bool grow = mcand > m2 + kLazy;
-    if (__ballot(grow)) {
-      const float mn = grow ? mcand : m2;
-      const float alpha = fast_exp2(m2 - mn);
-      m2 = mn;
-      lsum *= alpha;
+    bool grow[QB];
+    float mcand[QB];
+    bool any = false;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m = fmaxf(mx[qb], other_half(mx[qb]));
+      mcand[qb] = m * c2;
+      grow[qb] = mcand[qb] > m2[qb] + kLazy;
+      any = any || grow[qb];
+    }
+    if (__ballot(any)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) O[db][i] *= alpha;
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mn = grow[qb] ? mcand[qb] : m2[qb];
+        const float alpha = fast_exp2(m2[qb] - mn);
+        m2[qb] = mn;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[db][qb][i] *= alpha;
+      }
     }
   };
 
   // p = 2^(s*c2 - m2) -> P (bf16 B operands); row sum as a shallow tree
-  auto exps = [&](const f32x16* S, bf16x8 (*P)[2]) {
-    const float mn = m2;
-    float part[4];
+  auto exps = [&](f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mn = m2[qb];
+      float part[4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float e[8];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(S[kb][8 * hh + j], c2, -mn));
-        bf16x8 pv8;
+        for (int hh = 0; hh < 2; ++hh) {
+          float e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv8[j] = static_cast<__bf16>(e[j]);
-        P[kb][hh] = pv8;
-        part[2 * kb + hh] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      }
-    lsum += (part[0] + part[1]) + (part[2] + part[3]);
-    // materialise the sum here: otherwise the compiler sinks these adds into
-    // the next tile and keeps all 32 exponentials live across the PV MFMAs
+          for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(S[kb][qb][8 * hh + j], c2, -mn));
+          bf16x8 pv8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv8[j] = static_cast<__bf16>(e[j]);
+          P[kb][qb][hh] = pv8;
+          part[2 * kb + hh] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        }
+      lsum[qb] += (part[0] + part[1]) + (part[2] + part[3]);
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("" : "+v"(lsum));  // (a VGPR constraint exists only in the device pass)
+      // materialise the sum here: otherwise the compiler sinks these adds
+      // into the next tile and keeps the exponentials live across the PV
+      // MFMAs (a VGPR constraint exists only in the device pass)
+      asm volatile("" : "+v"(lsum[qb]));
 #endif
+    }
   };
 
-  // O^T += V^T P^T with V from V buffer `buf`
-  auto pv = [&](int buf, bf16x8 (*P)[2]) {
+  // O^T += V^T P^T with V from V buffer `buf`; each V^T operand feeds QB MFMAs
+  auto pv = [&](int buf, bf16x8 (*P)[QB][2]) {
     const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -354,26 +383,27 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk) * ROWB));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk + 4) * ROWB));
         const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kk >> 1][kk & 1], O[db], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kk >> 1][qb][kk & 1], O[db][qb], 0, 0, 0);
       }
   };
 
-  // Instruction interleave of one tile's math block: the QK^T MFMAs of the
-  // next tile are spread through the exp/convert VALU work of this tile (the
-  // wavefront issues in order, so VALU work only overlaps the matrix cores
-  // when it sits between MFMAs), then the PV MFMAs with their V reads.
   // Instruction interleave of one tile's math, in two regions.  Region A: the
   // QK^T MFMAs of the next tile spread through this tile's exp/convert VALU
   // work (a wavefront issues in order, so VALU work overlaps the matrix
-  // cores only when it sits between MFMAs), K operand reads one step ahead.
-  // Region B: the PV MFMAs with their transposed V reads two steps ahead.
+  // cores only when it sits between MFMAs), K operand reads ahead of use.
+  // Region B: the PV MFMAs with their transposed V reads ahead of use.
   auto schedule_a = [&]() {
 #if VDIT_ATTN_SCHED
     __builtin_amdgcn_sched_group_barrier(0x100, VDIT_ATTN_KPREF, 0);
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, VDIT_ATTN_VALU_PER_MFMA, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VDIT_ATTN_VALU_PER_MFMA, 0);
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #endif
@@ -383,9 +413,12 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * VDIT_ATTN_VPREF, 1);
 #pragma unroll
     for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);
     }
 #endif
   };
@@ -401,9 +434,11 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
     issue(0, true, 0);
     if (ntiles > 1) issue(1, false, 1);
     wait_and_sync();
-    f32x16 S[2];
+    f32x16 S[2][QB];
     qk(0, S);
-    float mx = lane_max(S);
+    float mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = lane_max(S, qb);
     __syncthreads();
 
     auto iteration = [&](int t, auto parity) {
@@ -414,21 +449,26 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
       row_max(S, mx, min(kBN, len - t * kBN));
       // region A: exps of tile t || S^T of tile t+1 (computed on the last
       // tile too, on stale LDS data, and discarded)
-      f32x16 Sn[2];
+      f32x16 Sn[2][QB];
       qk(1 - P0, Sn);
-      bf16x8 P[2][2];
+      bf16x8 P[2][QB][2];
       exps(S, P);
       schedule_a();
       __builtin_amdgcn_sched_barrier(0);
       // region B: O^T += V^T P^T || lane max of tile t+1's scores
       pv(P0, P);
-      mx = lane_max(Sn);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        mx[qb] = lane_max(Sn, qb);
 #if defined(__HIP_DEVICE_COMPILE__)
-      asm volatile("" : "+v"(mx));  // keep the max here, among the PV MFMAs
+        asm volatile("" : "+v"(mx[qb]));  // keep the max here, among the PV MFMAs
 #endif
+      }
       schedule_b();
-      S[0] = Sn[0];
-      S[1] = Sn[1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) S[kb][qb] = Sn[kb][qb];
       wait_and_sync();
     };
     int t = 0;
@@ -440,49 +480,51 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   }
 
   // -------------------------------------------------------------- epilogue --
-  const float lt = lsum + other_half(lsum);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const float lse_s = partial_lse(m2, lt);
-  const int64_t q = qw0 + r;
-
   if (p.epi == kEpiPlain || p.epi == kEpiRing) {
-    if (q >= q_end) return;
-    const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
-    const int64_t lrowi = (int64_t(b) * p.Hq + h) * p.Lq + q;
-    float wa = 0.f, wb = inv, lse_out = lse_s;
-    const bool merge_prev = p.epi == kEpiRing && p.has_prev;
-    if (merge_prev) {
-      const MergeW w = merge_weights(p.part_lse[lrowi], lse_s);
-      wa = w.wa;
-      wb = w.wb * inv;
-      lse_out = w.lse;
-    }
-    const bool to_part = p.epi == kEpiRing && !p.final_out;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * db + 8 * i4 + 4 * g;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = O[db][4 * i4 + e] * wb;
-        if (merge_prev) {
-          const float4 pv4 = *reinterpret_cast<const float4*>(p.part_o + orow + d);
-          y[0] = fmaf(wa, pv4.x, y[0]); y[1] = fmaf(wa, pv4.y, y[1]);
-          y[2] = fmaf(wa, pv4.z, y[2]); y[3] = fmaf(wa, pv4.w, y[3]);
-        }
-        if (to_part) {
-          *reinterpret_cast<float4*>(p.part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
-        } else {
-          uint2 w;
-          w.x = pack_bf16x2(y[0], y[1]);
-          w.y = pack_bf16x2(y[2], y[3]);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
-        }
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = lsum[qb] + other_half(lsum[qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse_s = partial_lse(m2[qb], lt);
+      const int64_t q = qw0 + 32 * qb + r;
+      if (q >= q_end) continue;
+      const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
+      const int64_t lrowi = (int64_t(b) * p.Hq + h) * p.Lq + q;
+      float wa = 0.f, wb = inv, lse_out = lse_s;
+      const bool merge_prev = p.epi == kEpiRing && p.has_prev;
+      if (merge_prev) {
+        const MergeW w = merge_weights(p.part_lse[lrowi], lse_s);
+        wa = w.wa;
+        wb = w.wb * inv;
+        lse_out = w.lse;
       }
-    if (g == 0) {
-      if (to_part) p.part_lse[lrowi] = lse_out;
-      else if (p.lse) p.lse[lrowi] = lse_out;
+      const bool to_part = p.epi == kEpiRing && !p.final_out;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = 32 * db + 8 * i4 + 4 * g;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = O[db][qb][4 * i4 + e] * wb;
+          if (merge_prev) {
+            const float4 pv4 = *reinterpret_cast<const float4*>(p.part_o + orow + d);
+            y[0] = fmaf(wa, pv4.x, y[0]); y[1] = fmaf(wa, pv4.y, y[1]);
+            y[2] = fmaf(wa, pv4.z, y[2]); y[3] = fmaf(wa, pv4.w, y[3]);
+          }
+          if (to_part) {
+            *reinterpret_cast<float4*>(p.part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
+          } else {
+            uint2 w;
+            w.x = pack_bf16x2(y[0], y[1]);
+            w.y = pack_bf16x2(y[2], y[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
+          }
+        }
+      if (g == 0) {
+        if (to_part) p.part_lse[lrowi] = lse_out;
+        else if (p.lse) p.lse[lrowi] = lse_out;
+      }
     }
     return;
   }
@@ -494,79 +536,91 @@ __global__ __launch_bounds__(64 * NW, 4 * VDIT_ATTN_WPE / NW) void attn_mfma_ker
   const uint16_t* st_hi = static_cast<const uint16_t*>(p.st) + sidx * D * D;
   const uint16_t* st_lo = st_hi + plane;
   const float* z = p.zc + sidx * D;
-  bf16x8 Fq[KS];
-  float dn = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
-    const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
-    const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
-    bf16x8 f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = phi_elu1(static_cast<float>(Qr[ks][j]));
-      dn = fmaf(x, zz[j], dn);
-      f[j] = static_cast<__bf16>(x);
-    }
-    Fq[ks] = f;
-  }
-  const float den = dn + other_half(dn);
-  const float lse_l = den > 0.f ? logf(den) : -INFINITY;
-  const MergeW w = merge_weights(lse_s, lse_l);
-  const float inv_den = den > 0.f ? 1.f / den : 0.f;
-  const float ws = w.wa * inv, wl = w.wb * inv_den;
-  const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    f32x16 A;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) A[i] = 0.f;
-    const int dout = 32 * db + r;
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = lsum[qb] + other_half(lsum[qb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_s = partial_lse(m2[qb], lt);
+    const int64_t q = qw0 + 32 * qb + r;
+    bf16x8 Fq[KS];
+    float dn = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(st_hi + dout * D + 16 * ks + 8 * g);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(st_lo + dout * D + 16 * ks + 8 * g);
-      A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, Fq[ks], A, 0, 0, 0);
-      A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, Fq[ks], A, 0, 0, 0);
+      const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
+      const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
+      const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+      bf16x8 f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = phi_elu1(static_cast<float>(Qr[qb][ks][j]));
+        dn = fmaf(x, zz[j], dn);
+        f[j] = static_cast<__bf16>(x);
+      }
+      Fq[ks] = f;
     }
-    if (q < q_end) {
+    const float den = dn + other_half(dn);
+    const float lse_l = den > 0.f ? logf(den) : -INFINITY;
+    const MergeW w = merge_weights(lse_s, lse_l);
+    const float inv_den = den > 0.f ? 1.f / den : 0.f;
+    const float ws = w.wa * inv, wl = w.wb * inv_den;
+    const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * db + 8 * i4 + 4 * g;
-        float y[4];
+    for (int db = 0; db < DB; ++db) {
+      f32x16 A;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = ws * O[db][4 * i4 + e] + wl * A[4 * i4 + e];
-        uint2 u;
-        u.x = pack_bf16x2(y[0], y[1]);
-        u.y = pack_bf16x2(y[2], y[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = u;
+      for (int i = 0; i < 16; ++i) A[i] = 0.f;
+      const int dout = 32 * db + r;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(st_hi + dout * D + 16 * ks + 8 * g);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(st_lo + dout * D + 16 * ks + 8 * g);
+        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, Fq[ks], A, 0, 0, 0);
+        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, Fq[ks], A, 0, 0, 0);
+      }
+      if (q < q_end) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = 32 * db + 8 * i4 + 4 * g;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = ws * O[db][qb][4 * i4 + e] + wl * A[4 * i4 + e];
+          uint2 u;
+          u.x = pack_bf16x2(y[0], y[1]);
+          u.y = pack_bf16x2(y[2], y[3]);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = u;
+        }
       }
     }
+    if (p.lse && g == 0 && q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = w.lse;
   }
-  if (p.lse && g == 0 && q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = w.lse;
 }
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * 32 * QB;
   int64_t total;
   if (p.epi == kEpiHybrid) total = ((p.chunk + BM - 1) / BM) * p.n_chunks * p.Hq * p.B;
   else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
-  // 128 queries per workgroup (4 wavefronts); problems too small to fill the
-  // 256 CUs twice over use 64-query workgroups.
+  // Large query sets: VDIT_ATTN_BIG_QB blocks of 32 queries per wavefront,
+  // 4 wavefronts per workgroup.  Problems too small to fill the 256 CUs twice
+  // over with 128-query workgroups use 64-query workgroups.
   const int64_t rows = (p.epi == kEpiHybrid ? p.chunk : p.Lq);
   const int64_t wg128 = ((rows + 127) / 128) * p.Hq * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1);
-  const bool big = wg128 >= 512;
-  if (p.D == 128) return big ? launch_cfg<128, 4>(p, s) : launch_cfg<128, 2>(p, s);
-  return big ? launch_cfg<64, 4>(p, s) : launch_cfg<64, 2>(p, s);
+  const int64_t wg256 = ((rows + 255) / 256) * p.Hq * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1);
+  if (p.D == 128) {
+    if (VDIT_ATTN_BIG_QB == 2 && wg256 >= 512) return launch_cfg<128, 4, 2>(p, s);
+    return wg128 >= 512 ? launch_cfg<128, 4, 1>(p, s) : launch_cfg<128, 2, 1>(p, s);
+  }
+  if (VDIT_ATTN_BIG_QB == 2 && wg256 >= 512) return launch_cfg<64, 4, 2>(p, s);
+  return wg128 >= 512 ? launch_cfg<64, 4, 1>(p, s) : launch_cfg<64, 2, 1>(p, s);
 }
 
 }  // namespace vdit
