@@ -246,7 +246,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the oracle's timed sample")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--calibrate-copy", action="store_true",
