@@ -240,18 +240,72 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
                       "bytes_written_per_launch": nbytes, "launches": reps}), flush=True)
 
 
+def _counter_rows(run_dir: str):
+    """(kernel name, counter name, value) rows of a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _mean_counter(rows, kernel_substr: str, counter: str) -> tuple[float, int]:
+    vals = [v for k, c, v in rows if kernel_substr in k and c == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel matching {kernel_substr!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_from(run_root: str):
+    """Turn four rocprofv3 --pmc runs under run_root (fetch/, write/: this bench;
+    cfetch/, cwrite/: `bench.py --calibrate-copy`) into HBM bytes per attention
+    launch.  FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is scaled by
+    the ratio (bytes actually copied) / (counter x 1024) of the 1 GiB copy."""
+    nbytes = float(1 << 30)
+    cf, _ = _mean_counter(_counter_rows(os.path.join(run_root, "cfetch")), "copyBuffer", "FETCH_SIZE")
+    cw, _ = _mean_counter(_counter_rows(os.path.join(run_root, "cwrite")), "copyBuffer", "WRITE_SIZE")
+    f_fetch, f_write = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    out = {"kernel_source_sha256_16": src_hash(ATTN_SRC), "calibration": {
+        "copy_bytes": int(nbytes), "copy_FETCH_SIZE_KiB": cf, "copy_WRITE_SIZE_KiB": cw,
+        "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}}
+    for name, sub in (("attn", "attn_mfma_kernel"), ("rope", "rope_qk_kernel")):
+        fe, n_f = _mean_counter(_counter_rows(os.path.join(run_root, "fetch")), sub, "FETCH_SIZE")
+        wr, n_w = _mean_counter(_counter_rows(os.path.join(run_root, "write")), sub, "WRITE_SIZE")
+        out[name] = {"FETCH_SIZE_KiB": fe, "WRITE_SIZE_KiB": wr, "dispatches": [n_f, n_w],
+                     "read_bytes": round(fe * 1024 * f_fetch), "write_bytes": round(wr * 1024 * f_write)}
+    out["hbm_bytes_per_launch"] = out["attn"]["read_bytes"] + out["attn"]["write_bytes"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the oracle's timed sample")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs DIR/{fetch,write,cfetch,cwrite} "
+                         "into the traffic JSON (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        t = traffic_from(args.traffic_from)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+            f.write("\n")
+        print(json.dumps(t), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the layer's sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
