@@ -119,6 +119,23 @@ def test_tiny_workload_f32_end_to_end(norm):
     check(qr, wq, "f32", "q roped"); check(o, wo, "f32", "O"); check_lse(lse, wl, "f32", "LSE")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_full_attention_wide_workgroups_sampled(D):
+    # 8 query heads x ceil(16347 / 256) = 512 workgroups of 256 queries: two
+    # even rounds on a 256-CU part, so the 8-wavefront workgroup shape runs;
+    # ragged query and key tails, grouped-query heads.
+    Lq, Lkv, Hq, Hk = 16347, 5013, 8, 2
+    log(f"full attention, 256-query workgroups: D={D} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+    q = raw((1, Lq, Hq, D), 61, "bf16"); k = raw((1, Lkv, Hk, D), 62, "bf16"); v = raw((1, Lkv, Hk, D), 63, "bf16")
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v))
+    torch.cuda.synchronize()
+    rows = WL.sample_rows(Lq, 160, seed=64)
+    rows = np.unique(np.concatenate([rows, [0, 31, 32, 255, 256, 16127, 16128, Lq - 1]]))
+    wo, wl = O.attention(q.values[:, rows], k.values, v.values)
+    check(from_dev(o)[:, rows], wo, "bf16", "O (sampled rows)")
+    check_lse(from_dev(lse)[:, :, rows], wl, "bf16", "LSE (sampled rows)")
+
+
 def _sampled_attention(qr64, kr64, v64, rows, scale=None):
     o, l = O.attention(qr64[:, rows], kr64, v64, scale)
     return o, l
