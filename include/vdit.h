@@ -150,7 +150,13 @@ typedef enum {
  * lse: [B, n_heads, Lq] float32 or NULL.  o must not overlap q, k, v, the
  * caches or the workspace.  workspace: device scratch of at least
  * vdit_attn_workspace_bytes(args) bytes (may be NULL when that is 0);
- * its contents need no initialisation and are clobbered.
+ * its contents need no initialisation and are clobbered.  RING (with more
+ * than one chunk) and CHUNK_HYBRID require it.  For FULL and ROLLING it is
+ * optional: bf16 calls with too few queries to occupy the device (fewer
+ * than two 128-query blocks per compute unit) split the keys into up to 8
+ * ranges whose float32 partials live in the workspace and are merged with
+ * the log-sum-exp combination of vdit_lse_merge; without a large enough
+ * workspace they run unsplit (same result up to rounding order).
  */
 typedef struct {
   int32_t mode;  /* vdit_attn_mode */
@@ -179,8 +185,10 @@ typedef struct {
   size_t workspace_bytes;
 } vdit_attn_args;
 
-/* Bytes of device workspace vdit_attn_fwd needs for these arguments
- * (0 if none).  Returns (size_t)-1 for arguments that fail validation. */
+/* Bytes of device workspace vdit_attn_fwd needs (RING, CHUNK_HYBRID) or can
+ * use (FULL, ROLLING: the key split) for these arguments on the current
+ * device (0 if none).  Returns (size_t)-1 for arguments that fail
+ * validation. */
 size_t vdit_attn_workspace_bytes(const vdit_attn_args* args /* host */);
 
 /* Enqueue one attention call (see vdit_attn_args).  head_dim in {64, 128}. */

@@ -85,6 +85,24 @@ int main() {
   b.Lkv = 100; b.chunk_tokens = 0;
   EXPECT(check_attn(b).code == Check::invalid, "hybrid chunk");
 
+  // key split plan (256 compute units)
+  {
+    SplitPlan sp = split_plan(0, 1, 2040, 16, 5 * 2040, 256);  // rolling decode frame: 256 workgroups of 128 queries
+    EXPECT(sp.nsplit == 2 && sp.split_keys == 5120, "rolling split in two");
+    EXPECT(split_workspace_bytes(sp, 1, 2040, 16, 64) == align256(2ull * 2040 * 16 * 64 * 4) + align256(2ull * 16 * 2040 * 4), "split workspace");
+    EXPECT(split_plan(0, 1, 32760, 12, 32760, 256).nsplit == 1, "large layer unsplit");
+    EXPECT(split_plan(1, 1, 2040, 16, 10200, 256).nsplit == 1, "float32 unsplit");
+    EXPECT(split_plan(0, 1, 300, 4, 333, 256).nsplit == 1, "too few keys to split");
+    sp = split_plan(0, 1, 1000, 2, 5000, 256);  // 16 workgroups: up to 8 ranges of >= 256 keys
+    EXPECT(sp.nsplit == 8 && sp.split_keys == 640, "eight ranges, last one ragged");
+    EXPECT((sp.nsplit - 1) * sp.split_keys < 5000 && sp.nsplit * sp.split_keys >= 5000, "ranges cover the keys");
+    AttnArgs r = a; r.mode = 2; r.n_slots = 5; r.frame = 0; r.Lq = 2040; r.n_heads = 16; r.n_kv_heads = 16; r.head_dim = 64;
+    EXPECT(attn_keys(r) == 2040, "rolling keys at frame 0");
+    r.frame = 9;
+    EXPECT(attn_keys(r) == 5 * 2040, "rolling keys once the ring is full");
+    EXPECT(attn_workspace_bytes(r, 256) == split_workspace_bytes(split_plan(0, 1, 2040, 16, 10200, 256), 1, 2040, 16, 64), "rolling workspace");
+  }
+
   // merge
   EXPECT(bool(check_merge(P(0x1000), (float*)P(0x2000), P(0x3000), (float*)P(0x4000), P(0x1000), (float*)P(0x2000), 0, 0, 1, 8, 2, 64)), "merge in place ok");
   EXPECT(check_merge(P(0x1000), (float*)P(0x2000), P(0x3000), (float*)P(0x4000), P(0x1000), nullptr, 0, 1, 1, 8, 2, 64).code == Check::invalid, "merge in place dtype");

@@ -136,6 +136,23 @@ def test_full_attention_wide_workgroups_sampled(D):
     check_lse(from_dev(lse)[:, :, rows], wl, "bf16", "LSE (sampled rows)")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_full_attention_key_split(D):
+    # 16 workgroups of 128 queries: the keys are cut into 8 ranges of 640
+    # (the last one ragged) whose float32 partials are merged; with a
+    # workspace too small for the partials the same call runs unsplit.
+    Lq, Lkv, Hq, Hk = 1000, 5000, 2, 1
+    log(f"full attention with key split: D={D} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+    q = raw((1, Lq, Hq, D), 71, "bf16"); k = raw((1, Lkv, Hk, D), 72, "bf16"); v = raw((1, Lkv, Hk, D), 73, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o_split, lse_split = V.vdit_attn_fwd(qd, kd, vd)
+    o_plain, lse_plain = V.vdit_attn_fwd(qd, kd, vd, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, k.values, v.values)
+    check(o_split, wo, "bf16", "O (split)"); check_lse(lse_split, wl, "bf16", "LSE (split)")
+    check(o_plain, wo, "bf16", "O (unsplit)"); check_lse(lse_plain, wl, "bf16", "LSE (unsplit)")
+
+
 def _sampled_attention(qr64, kr64, v64, rows, scale=None):
     o, l = O.attention(qr64[:, rows], kr64, v64, scale)
     return o, l

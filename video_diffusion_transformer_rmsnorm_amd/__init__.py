@@ -173,7 +173,8 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     """One attention call.  Returns (o, lse) (lse None unless wanted).
 
     full:    k, v [B,Lkv,Hk,D].
-    ring:    k_chunks, v_chunks lists of [B,len_c,Hk,D]; workspace allocated if not given.
+    ring:    k_chunks, v_chunks lists of [B,len_c,Hk,D]; workspace allocated if not given
+             (also for full / rolling calls small enough to use the key split).
     rolling: k_cache, v_cache [B,n_slots,Lq,Hk,D]; k, v = this frame's keys/values or None
              (slot already filled); frame = stream index.
     hybrid:  k, v [B,L,Hk,D]; chunk_tokens; state_s [B,Hk,D,D], state_z [B,Hk,D] float32 (in/out).

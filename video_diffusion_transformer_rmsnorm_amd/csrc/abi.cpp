@@ -63,6 +63,42 @@ hipError_t launch_attn(const vdit::AttnLaunch& p, int dtype, hipStream_t s) {
   return dtype == VDIT_BF16 ? vdit::launch_attn_bf16(p, s) : vdit::launch_attn_f32(p, s);
 }
 
+// Plain attention of p (FULL or ROLLING), with the key split when the
+// caller's workspace holds its partials.  A workspace that is large enough
+// but misplaced is an error; a missing or smaller one runs unsplit.
+vdit_status launch_plain(vdit::AttnLaunch p, const vdit::AttnArgs& a, hipStream_t stream, const char* what) {
+  const int64_t keys = p.nseg ? p.seg[0].len : 0;
+  const vdit::SplitPlan sp = vdit::split_plan(a.dtype, a.B, a.Lq, a.n_heads, keys, vdit::device_cus());
+  const size_t need = vdit::split_workspace_bytes(sp, a.B, a.Lq, a.n_heads, a.head_dim);
+  if (need == 0 || !a.workspace || a.workspace_bytes < need)
+    return from_hip(launch_attn(p, a.dtype, stream), what);
+  const size_t nq = size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * vdit::esize(a.dtype);
+  if (!vdit::aligned16(a.workspace)) return fail(VDIT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (vdit::overlaps(a.workspace, need, a.o, nq)) return fail(VDIT_ERR_INVALID_ARG, "workspace overlaps o");
+  char* ws = static_cast<char*>(a.workspace);
+  p.nsplit = sp.nsplit;
+  p.split_keys = sp.split_keys;
+  p.epi = vdit::kEpiRing;  // every key range writes its float32 partial
+  p.has_prev = 0;
+  p.final_out = 0;
+  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_lse = reinterpret_cast<float*>(
+      ws + vdit::align256(size_t(sp.nsplit) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * 4));
+  if (auto st = from_hip(launch_attn(p, a.dtype, stream), what); st != VDIT_OK) return st;
+  vdit::SplitMergeLaunch m;
+  m.part_o = p.part_o;
+  m.part_lse = p.part_lse;
+  m.o = a.o;
+  m.lse = a.lse;
+  m.L = a.Lq;
+  m.B = a.B;
+  m.H = a.n_heads;
+  m.D = a.head_dim;
+  m.nsplit = sp.nsplit;
+  m.out_dtype = a.dtype;
+  return from_hip(vdit::launch_split_merge(m, stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,7 +156,7 @@ size_t vdit_attn_workspace_bytes(const vdit_attn_args* args) {
     g_last_error = r.msg;
     return size_t(-1);
   }
-  return vdit::attn_workspace_bytes(a);
+  return vdit::attn_workspace_bytes(a, vdit::device_cus());
 }
 
 vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
@@ -139,7 +175,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         p.nseg = 1;
         p.seg[0] = {a.k, a.v, a.Lkv, a.Lkv * a.n_kv_heads * D};
       }
-      return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(FULL) launch");
+      return launch_plain(p, a, stream, "vdit_attn_fwd(FULL) launch");
     }
     case VDIT_ATTN_RING: {
       if (empty_q) return VDIT_OK;
@@ -201,7 +237,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       vdit::AttnLaunch p = base_launch(a);
       p.nseg = 1;
       p.seg[0] = {kc, vc, nvalid * a.Lq, int64_t(a.n_slots) * a.Lq * a.n_kv_heads * D};
-      return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(ROLLING) launch");
+      return launch_plain(p, a, stream, "vdit_attn_fwd(ROLLING) launch");
     }
     case VDIT_ATTN_CHUNK_HYBRID: {
       const vdit::HybridLayout lay = vdit::hybrid_layout(a);

@@ -151,15 +151,32 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   int64_t q_begin, q_end, chunk_id = 0;
   int h, b;
   KvSeg sg;  // the keys/values this workgroup attends to
+  float* part_o = p.part_o;
+  float* part_lse = p.part_lse;
   if (!hybrid) {
     const int64_t tiles = (p.Lq + BM - 1) / BM;
-    const int64_t qt = lid % tiles, rest = lid / tiles;
+    const int64_t qt = lid % tiles;
+    int64_t rest = lid / tiles;
+    int64_t split = 0;
+    if (p.nsplit > 1) {
+      split = rest % p.nsplit;
+      rest /= p.nsplit;
+    }
     h = int(rest % p.Hq);
     b = int(rest / p.Hq);
     q_begin = qt * BM;
     q_end = min(p.Lq, q_begin + BM);
     sg = p.seg[0];
     if (p.nseg == 0) sg.len = 0;
+    if (p.nsplit > 1) {  // keys [split * split_keys, +split_keys) of the segment
+      const int64_t k0 = split * p.split_keys;
+      const int64_t n = min(p.split_keys, sg.len - k0);
+      sg.k = static_cast<const uint16_t*>(sg.k) + k0 * p.Hk * D;
+      sg.v = static_cast<const uint16_t*>(sg.v) + k0 * p.Hk * D;
+      sg.len = n > 0 ? n : 0;
+      part_o += split * (int64_t(p.B) * p.Lq * p.Hq * D);
+      part_lse += split * (int64_t(p.B) * p.Hq * p.Lq);
+    }
   } else {
     const int64_t tpc = (p.chunk + BM - 1) / BM;
     const int64_t t = lid % tpc, rest = lid / tpc;
@@ -524,7 +541,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       float wa = 0.f, wb = inv, lse_out = lse_s;
       const bool merge_prev = p.epi == kEpiRing && p.has_prev;
       if (merge_prev) {
-        const MergeW w = merge_weights(p.part_lse[lrowi], lse_s);
+        const MergeW w = merge_weights(part_lse[lrowi], lse_s);
         wa = w.wa;
         wb = w.wb * inv;
         lse_out = w.lse;
@@ -539,12 +556,12 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = O[db][qb][4 * i4 + e] * wb;
           if (merge_prev) {
-            const float4 pv4 = *reinterpret_cast<const float4*>(p.part_o + orow + d);
+            const float4 pv4 = *reinterpret_cast<const float4*>(part_o + orow + d);
             y[0] = fmaf(wa, pv4.x, y[0]); y[1] = fmaf(wa, pv4.y, y[1]);
             y[2] = fmaf(wa, pv4.z, y[2]); y[3] = fmaf(wa, pv4.w, y[3]);
           }
           if (to_part) {
-            *reinterpret_cast<float4*>(p.part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<float4*>(part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
           } else {
             uint2 w;
             w.x = pack_bf16x2(y[0], y[1]);
@@ -553,7 +570,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
           }
         }
       if (g == 0) {
-        if (to_part) p.part_lse[lrowi] = lse_out;
+        if (to_part) part_lse[lrowi] = lse_out;
         else if (p.lse) p.lse[lrowi] = lse_out;
       }
     }
@@ -631,13 +648,14 @@ hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
   constexpr int BM = NW * 32 * QB;
   int64_t total;
   if (p.epi == kEpiHybrid) total = ((p.chunk + BM - 1) / BM) * p.n_chunks * p.Hq * p.B;
-  else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B;
+  else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B * (p.nsplit > 1 ? p.nsplit : 1);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device).
+}  // namespace
+
 int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
@@ -649,6 +667,8 @@ int device_cus() {
   }
   return cus[dev];
 }
+
+namespace {
 
 // The 8-wavefront shape holds a whole CU per workgroup: it streams each K/V
 // tile into LDS once for 256 queries (half the tile traffic of two 4-wavefront
@@ -671,7 +691,7 @@ hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
   // (4 wavefronts, two workgroups per CU); else, for problems too small to
   // give every CU two such workgroups, 64 queries.
   const int64_t rows = (p.epi == kEpiHybrid ? p.chunk : p.Lq);
-  const int64_t units = int64_t(p.Hq) * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1);
+  const int64_t units = int64_t(p.Hq) * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1) * (p.nsplit > 1 ? p.nsplit : 1);
   const int64_t wg128 = ((rows + 127) / 128) * units;
   const int64_t wg256 = ((rows + 255) / 256) * units;
   const bool wide = prefer_wide(wg256, device_cus());

@@ -83,7 +83,59 @@ hipError_t launch_merge_d(const MergeLaunch& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// n-way form of the same combination, for the partials of a key-split
+// attention call: L = ln sum_s e^{L_s}, O = sum_s e^{L_s - L} O_s.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(SplitMergeLaunch p) {
+  constexpr int TPR = D / 8;
+  const int64_t rows = int64_t(p.B) * p.L * p.H;
+  const int64_t gt = int64_t(blockIdx.x) * kMergeThreads + threadIdx.x;
+  const int64_t row = gt / TPR;  // (b, l, h) row in [B, L, H] order
+  if (row >= rows) return;
+  const int c = int(gt % TPR);
+  const int h = int(row % p.H);
+  const int64_t bl = row / p.H;
+  const int64_t l = bl % p.L, b = bl / p.L;
+  const int64_t li = (b * p.H + h) * p.L + l;  // [B, H, L]
+  const int64_t so = rows * D, sl = rows;      // one whole partial
+  float mx = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) mx = fmaxf(mx, p.part_lse[s * sl + li]);
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lo = -INFINITY;
+  if (mx != -INFINITY) {
+    float tot = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float w = expf(p.part_lse[s * sl + li] - mx);
+      tot += w;
+      float x[8];
+      load8<false>(p.part_o, s * so + row * D + c * 8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = fmaf(w, x[e], y[e]);
+    }
+    const float inv = 1.f / tot;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] *= inv;
+    lo = mx + logf(tot);
+  }
+  store8<OUT_BF16>(p.o, row * D + c * 8, y);
+  if (p.lse && c == 0) p.lse[li] = lo;
+}
+
+template <int D>
+hipError_t launch_split_merge_d(const SplitMergeLaunch& p, hipStream_t s) {
+  const int64_t threads = int64_t(p.B) * p.L * p.H * (D / 8);
+  dim3 grid(static_cast<unsigned>((threads + kMergeThreads - 1) / kMergeThreads));
+  if (p.out_dtype == 0) hipLaunchKernelGGL((split_merge_kernel<D, true>), grid, dim3(kMergeThreads), 0, s, p);
+  else hipLaunchKernelGGL((split_merge_kernel<D, false>), grid, dim3(kMergeThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_split_merge(const SplitMergeLaunch& p, hipStream_t s) {
+  if (int64_t(p.B) * p.L == 0) return hipSuccess;
+  return p.D == 128 ? launch_split_merge_d<128>(p, s) : launch_split_merge_d<64>(p, s);
+}
 
 hipError_t launch_merge(const MergeLaunch& p, hipStream_t s) {
   if (int64_t(p.B) * p.L == 0) return hipSuccess;

@@ -166,6 +166,51 @@ inline size_t ring_workspace_bytes(const AttnArgs& a) {
   return align256(o) + align256(l);
 }
 
+// Key split of FULL / ROLLING bf16 attention.  When the 128-query
+// workgroups of a call would not give each of the device's `cus` compute
+// units two of them, the keys are cut into nsplit ranges of split_keys keys
+// (a multiple of the 64-key tile, each range at least 256 keys, at most 8
+// ranges); every range yields a float32 partial (normalised O and its LSE)
+// and a merge pass combines them.
+struct SplitPlan {
+  int nsplit = 1;
+  int64_t split_keys = 0;
+};
+
+inline SplitPlan split_plan(int dtype, int64_t B, int64_t Lq, int64_t Hq, int64_t keys, int cus) {
+  SplitPlan s;
+  if (dtype != 0 || B <= 0 || Lq <= 0 || Hq <= 0 || keys <= 0 || cus <= 0) return s;
+  const int64_t wg = ((Lq + 127) / 128) * Hq * B;
+  const int64_t target = 2 * int64_t(cus);
+  if (wg >= target) return s;
+  int64_t n = (target + wg - 1) / wg;
+  if (n > 8) n = 8;
+  if (n > keys / 256) n = keys / 256;
+  if (n < 2) return s;
+  const int64_t per = ((keys + n - 1) / n + 63) / 64 * 64;
+  n = (keys + per - 1) / per;
+  if (n < 2) return s;
+  s.nsplit = int(n);
+  s.split_keys = per;
+  return s;
+}
+
+inline size_t split_workspace_bytes(const SplitPlan& s, int64_t B, int64_t Lq, int64_t Hq, int64_t D) {
+  if (s.nsplit < 2) return 0;
+  const size_t n = size_t(s.nsplit);
+  return align256(n * size_t(B) * size_t(Lq) * size_t(Hq) * size_t(D) * 4) +
+         align256(n * size_t(B) * size_t(Hq) * size_t(Lq) * 4);
+}
+
+// Keys one FULL / ROLLING call attends to.
+inline int64_t attn_keys(const AttnArgs& a) {
+  if (a.mode == 2) {
+    const int64_t nvalid = a.frame + 1 < a.n_slots ? a.frame + 1 : a.n_slots;
+    return nvalid * a.Lq;
+  }
+  return a.Lkv;
+}
+
 inline CheckResult check_attn(const AttnArgs& a) {
   if (auto r = check_dtype(a.dtype); !r) return r;
   if (auto r = check_head_dim(a.head_dim); !r) return r;
@@ -256,11 +301,15 @@ inline CheckResult check_attn(const AttnArgs& a) {
   return CheckResult::good();
 }
 
-inline size_t attn_workspace_bytes(const AttnArgs& a) {
+// Workspace of one call on a device with `cus` compute units.  FULL and
+// ROLLING need none; the amount returned for them enables the key split.
+inline size_t attn_workspace_bytes(const AttnArgs& a, int cus) {
   switch (a.mode) {
     case 1: return ring_workspace_bytes(a);
     case 3: return hybrid_layout(a).total;
-    default: return 0;
+    default:
+      return split_workspace_bytes(split_plan(a.dtype, a.B, a.Lq, a.n_heads, attn_keys(a), cus), a.B, a.Lq,
+                                   a.n_heads, a.head_dim);
   }
 }
 

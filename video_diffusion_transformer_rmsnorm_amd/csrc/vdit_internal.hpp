@@ -48,11 +48,30 @@ struct AttnLaunch {
   const float* zc;   // [n_chunks][B][Hk][D]
   const void* hk;    // key / value base of the whole sequence (hybrid)
   const void* hv;
+  // key split (plain attention): nsplit ranges of split_keys keys; range s
+  // writes its partial to part_o / part_lse offset by s whole partials
+  int32_t nsplit;
+  int64_t split_keys;
 };
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s);
 hipError_t launch_attn_f32(const AttnLaunch& p, hipStream_t s);
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Merge of nsplit float32 attention partials ([nsplit][B][L][H][D] normalised
+// O, [nsplit][B][H][L] LSE) into o (out_dtype) and lse (may be NULL).
+struct SplitMergeLaunch {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int64_t L;
+  int32_t B, H, D, nsplit, out_dtype;
+};
+hipError_t launch_split_merge(const SplitMergeLaunch& p, hipStream_t s);
 
 struct RopeLaunch {
   const void* q_in;
