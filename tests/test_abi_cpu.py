@@ -137,11 +137,19 @@ def test_workspace_sizes(lib):
     h.Lq = h.Lkv = w5.tokens
     h.chunk_tokens = w5.chunk_tokens
     n = V.vdit_attn_workspace_bytes(h)
-    nch, ns = 11, 8
+    nch, ns = 11, 2  # 264 (chunk, head) units -> 2 token splits for ~512 delta workgroups
     expect = align(nch * ns * 24 * 128 * 128 * 4) + align(nch * ns * 24 * 128 * 4) + \
         align(nch * 24 * 128 * 128 * 4) + align(nch * 24 * 128 * 4)
     assert n == expect
     assert w3.heads == 10
+    # FULL on few queries: the optional key-split workspace (256 compute units
+    # assumed when no device is present): 2040 queries x 16 heads -> 2 ranges
+    f = V.VditAttnArgs()
+    f.mode, f.dtype, f.B, f.n_heads, f.n_kv_heads, f.head_dim = 0, 0, 1, 16, 16, 64
+    f.Lq, f.Lkv = 2040, 10200
+    assert V.vdit_attn_workspace_bytes(f) == align(2 * 2040 * 16 * 64 * 4) + align(2 * 16 * 2040 * 4)
+    f.Lq, f.n_heads, f.n_kv_heads, f.head_dim, f.Lkv = 32760, 12, 12, 128, 32760
+    assert V.vdit_attn_workspace_bytes(f) == 0
     h.head_dim = 96
     with pytest.raises(V.VditError):
         V.vdit_attn_workspace_bytes(h)

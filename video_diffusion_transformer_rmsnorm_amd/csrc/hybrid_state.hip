@@ -17,6 +17,7 @@
 //     kernel consumes it on the matrix cores with ~16 significant bits);
 //     for float32 models as float32.
 #include "attn_epilogue.hpp"
+#include "device_common.hpp"
 #include "vdit_internal.hpp"
 
 namespace vdit {
@@ -84,6 +85,131 @@ __global__ __launch_bounds__(kDeltaThreads) void hybrid_delta_kernel(HybridState
   if (dout0 == 0) p.dz[slot * D + din] = zacc;
 }
 
+// Delta pass on the matrix cores (bf16 models).  dS^T = V^T phi(K) over the
+// split's tokens with v_mfma_f32_32x32x16_bf16: A = V^T (d_out x tokens),
+// B = phi(K) (tokens x d_in).  phi is applied in float32 to the bf16 keys
+// and fed as a bf16 hi + lo pair (two MFMAs), so the products keep ~16
+// significant bits; V is exact in bf16.  64-token tiles of K and V are
+// staged row-major in LDS with the 16-byte chunk of row r at chunk
+// position c ^ swz(r); both operands are then read "transposed" (8
+// consecutive tokens of one channel per lane) with ds_read_b64_tr_b16.
+// Wavefront w owns d_in block w % (D/32) and (D/32)^2 / 4 blocks of d_out.
+typedef short dl_i16x4 __attribute__((ext_vector_type(4)));
+typedef short dl_i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) dl_i16x4 dl_lds_i16x4;
+constexpr int kMDeltaBN = 64;  // tokens per LDS tile
+
+template <int D>
+__device__ __forceinline__ int dswz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void hybrid_delta_mfma_kernel(HybridStateLaunch p) {
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int ROWB = 2 * D;              // bytes per token row
+  constexpr int NB = D / 32;               // 32-channel blocks
+  constexpr int MBW = NB * NB / 4;         // d_out blocks per wavefront
+  __shared__ __attribute__((aligned(16))) char kt[kMDeltaBN * ROWB];
+  __shared__ __attribute__((aligned(16))) char vt[kMDeltaBN * ROWB];
+
+  // blockIdx.x = ((c * nsplit + s) * B + b) * Hk + hk
+  int64_t bid = blockIdx.x;
+  const int hk = int(bid % p.Hk); bid /= p.Hk;
+  const int b = int(bid % p.B); bid /= p.B;
+  const int s = int(bid % p.nsplit);
+  const int64_t c = bid / p.nsplit;
+  const int64_t c0 = c * p.chunk, c1 = min(p.L, c0 + p.chunk);
+  const int64_t per = (c1 - c0 + p.nsplit - 1) / p.nsplit;
+  const int64_t t0 = min(c1, c0 + s * per), t1 = min(c1, t0 + per);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int nb = wave % NB;                // d_in block
+  const int mb0 = (wave / NB) * MBW;       // first d_out block
+
+  // transposed-read address of block db (see the attention kernel's V^T reads)
+  auto tr_addr = [&](int db) {
+    const int s16 = lane & 15, rho = s16 >> 2, q4 = s16 & 3;
+    const int rowo = 8 * g + rho;
+    const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * q4;
+    return uint32_t(rowo * ROWB + (((d >> 3) ^ dswz<D>(rowo)) * 16) + (d & 7) * 2);
+  };
+  const uint32_t kaddr = tr_addr(nb);
+  uint32_t vaddr[MBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) vaddr[i] = tr_addr(mb0 + i);
+  auto tr8 = [&](const char* base, uint32_t addr, int kk) {
+    const dl_i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dl_lds_i16x4*)(base + addr + (16 * kk) * ROWB));
+    const dl_i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dl_lds_i16x4*)(base + addr + (16 * kk + 4) * ROWB));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  f32x16 acc[MBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+  float zacc = 0.f;
+  const int64_t tok_stride = int64_t(p.Hk) * D;  // elements between tokens
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.L * p.Hk + hk) * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.L * p.Hk + hk) * D;
+
+  for (int64_t j0 = t0; j0 < t1; j0 += kMDeltaBN) {
+    const int nv = int(min<int64_t>(kMDeltaBN, t1 - j0));
+    __syncthreads();
+    for (int e = tid; e < kMDeltaBN * CPR; e += 256) {
+      const int row = e / CPR, ch = e % CPR;
+      uint4 ku = make_uint4(0, 0, 0, 0), vu = ku;
+      if (row < nv) {
+        const int64_t off = (j0 + row) * tok_stride + ch * 8;
+        ku = *reinterpret_cast<const uint4*>(kg + off);
+        vu = *reinterpret_cast<const uint4*>(vg + off);
+      }
+      const int at = row * ROWB + ((ch ^ dswz<D>(row)) * 16);
+      *reinterpret_cast<uint4*>(kt + at) = ku;
+      *reinterpret_cast<uint4*>(vt + at) = vu;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kMDeltaBN / 16; ++kk) {
+      if (16 * kk >= nv) break;
+      // B = phi(K) for tokens 16kk + 8g + j, channel 32nb + lane%32
+      const dl_i16x8 kr = tr8(kt, kaddr, kk);
+      bf16x8 bh, bl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float f = phi_elu1(bf16_to_f32(static_cast<uint16_t>(kr[j])));
+        if (16 * kk + 8 * g + j >= nv) f = 0.f;
+        zacc += f;
+        const __bf16 h = static_cast<__bf16>(f);
+        bh[j] = h;
+        bl[j] = static_cast<__bf16>(f - static_cast<float>(h));
+      }
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, tr8(vt, vaddr[i], kk));
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[i], 0, 0, 0);
+      }
+    }
+  }
+  const int64_t slot = ((c * p.nsplit + s) * p.B + b) * p.Hk + hk;
+  float* ds = p.ds + slot * D * D;
+  const int r = lane & 31;
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = 8 * (e / 4) + 4 * g + (e % 4);  // accumulator row of register e
+      ds[int64_t(32 * (mb0 + i) + m) * D + 32 * nb + r] = acc[i][e];
+    }
+  // dz: each lane summed 8 of every 16 tokens of channel 32nb + r
+  zacc += __shfl_xor(zacc, 32);
+  if (wave < NB && g == 0) p.dz[slot * D + 32 * nb + r] = zacc;
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
   constexpr int NE = D * D + D;
@@ -120,7 +246,10 @@ template <int D, bool BF16>
 hipError_t launch_d(const HybridStateLaunch& p, hipStream_t s) {
   const int64_t nblk = p.n_chunks * p.nsplit * p.B * p.Hk;
   if (nblk > 0) {
-    hipLaunchKernelGGL((hybrid_delta_kernel<D, BF16>), dim3(static_cast<unsigned>(nblk)), dim3(kDeltaThreads), 0, s, p);
+    if constexpr (BF16)
+      hipLaunchKernelGGL((hybrid_delta_mfma_kernel<D>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((hybrid_delta_kernel<D, BF16>), dim3(static_cast<unsigned>(nblk)), dim3(kDeltaThreads), 0, s, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t nthr = int64_t(p.B) * p.Hk * (D * D + D);

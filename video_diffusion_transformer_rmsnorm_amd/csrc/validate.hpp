@@ -134,12 +134,14 @@ struct HybridLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline int hybrid_nsplit(int64_t chunk_tokens) {
-  // enough token splits that every chunk state delta is spread over several
-  // workgroups, but each split still covers >= 128 tokens
-  int64_t s = chunk_tokens / 128;
-  if (s < 1) s = 1;
+inline int hybrid_nsplit(int64_t chunk_tokens, int64_t n_chunks, int64_t B, int64_t Hk) {
+  // token splits per chunk: enough (chunk, split, batch, head) workgroups for
+  // about 512 in total (two per CU), each split >= 64 tokens, at most 8
+  const int64_t units = n_chunks * B * Hk;
+  int64_t s = units > 0 ? (512 + units - 1) / units : 1;
+  if (s > chunk_tokens / 64) s = chunk_tokens / 64;
   if (s > 8) s = 8;
+  if (s < 1) s = 1;
   return int(s);
 }
 
@@ -148,7 +150,7 @@ inline HybridLayout hybrid_layout(const AttnArgs& a) {
   const int64_t L = a.Lq, C = a.chunk_tokens;
   const size_t D = size_t(a.head_dim), B = size_t(a.B), Hk = size_t(a.n_kv_heads);
   h.n_chunks = C > 0 ? (L + C - 1) / C : 0;
-  h.nsplit = hybrid_nsplit(C);
+  h.nsplit = hybrid_nsplit(C, h.n_chunks, a.B, a.n_kv_heads);
   const size_t nc = size_t(h.n_chunks), ns = size_t(h.nsplit);
   size_t off = 0;
   h.off_ds = off; off = align256(off + nc * ns * B * Hk * D * D * 4);
