@@ -47,14 +47,11 @@
 #ifndef VDIT_ATTN_BIG_QB
 #define VDIT_ATTN_BIG_QB 1  // query blocks per wavefront for large problems (2: one wavefront per SIMD)
 #endif
-#ifndef VDIT_ATTN_NBUF8
-#define VDIT_ATTN_NBUF8 2  // tile buffers of the 8-wavefront kernel (2 or 3)
-#endif
 #ifndef VDIT_ATTN_SCHED
 #define VDIT_ATTN_SCHED 1
 #endif
 #ifndef VDIT_ATTN_VALU_PER_MFMA
-#define VDIT_ATTN_VALU_PER_MFMA 4
+#define VDIT_ATTN_VALU_PER_MFMA 5
 #endif
 #ifndef VDIT_ATTN_KPREF
 #define VDIT_ATTN_KPREF 3  // K operand reads issued ahead of their MFMA
@@ -134,11 +131,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   constexpr int KI = KTILE_B / 1024;            // K direct-load instructions per tile
   constexpr int KIW = (KI + NW - 1) / NW;       // ... per wavefront (at most)
   static_assert(KTILE_B % 1024 == 0, "padded K tile is whole 1 KB blocks");
-  // K and V tile buffers (3: loads run two tiles ahead; needs the LDS of a
-  // single workgroup per CU)
-  constexpr int NBUF = (NW == 8 && VDIT_ATTN_NBUF8 == 3) ? 3 : 2;
-  constexpr int KMIN = KI / NW;  // K load instructions issued by every wavefront
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF * KTILE_B + NBUF * TILE_B];  // K buffers, V buffers
+  __shared__ __attribute__((aligned(1024))) char lds[2 * KTILE_B + 2 * TILE_B];  // K0 K1 V0 V1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -266,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(tb), (short)0, __builtin_amdgcn_readfirstlane(int(avail)), 0x00020000);
     if (is_v) {
-      char* lb = lds + NBUF * KTILE_B + buf * TILE_B + wave * IPW * 1024;
+      char* lb = lds + 2 * KTILE_B + buf * TILE_B + wave * IPW * 1024;
 #pragma unroll
       for (int u = 0; u < IPW; ++u) buffer_load_lds16(rsrc, (lds_void*)(lb + u * 1024), voff[u]);
     } else {
@@ -399,7 +392,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 
   // O^T += V^T P^T with V from V buffer `buf`; each V^T operand feeds QB MFMAs
   auto pv = [&](int buf, bf16x8 (*P)[QB][2]) {
-    const char* Vl = lds + NBUF * KTILE_B + buf * TILE_B;
+    const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -453,13 +446,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   };
 
   if (ntiles > 0) {
-    // prologue: K_0 .. K_{NBUF-1} and V_0 .. V_{NBUF-2} in flight; S^T of tile 0
-#pragma unroll
-    for (int i = 0; i < NBUF; ++i)
-      if (i < ntiles) issue(i, false, i);
-#pragma unroll
-    for (int i = 0; i + 1 < NBUF; ++i)
-      if (i < ntiles) issue(i, true, i);
+    // prologue: K_0, V_0, K_1 in flight; S^T of tile 0
+    issue(0, false, 0);
+    issue(0, true, 0);
+    if (ntiles > 1) issue(1, false, 1);
     wait_and_sync();
     f32x16 S[2][QB];
     qk(0, S);
@@ -468,18 +458,16 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     for (int qb = 0; qb < QB; ++qb) mx[qb] = lane_max(S, qb);
     __syncthreads();
 
-    auto iteration = [&](int t, auto phase) {
-      constexpr int P0 = decltype(phase)::value;  // t % NBUF
-      constexpr int PK1 = (P0 + 1) % NBUF, PV1 = (P0 + NBUF - 1) % NBUF;
-      // stream K_{t+NBUF} into K_t's buffer and V_{t+NBUF-1} into V_{t-1}'s
-      const bool ld_k = t + NBUF < ntiles, ld_v = t + NBUF - 1 < ntiles;
-      if (ld_k) issue(t + NBUF, false, P0);
-      if (ld_v) issue(t + NBUF - 1, true, PV1);
+    auto iteration = [&](int t, auto parity) {
+      constexpr int P0 = decltype(parity)::value;
+      // stream K_{t+2} into K buffer P0 and V_{t+1} into V buffer 1-P0
+      if (t + 2 < ntiles) issue(t + 2, false, P0);
+      if (t + 1 < ntiles) issue(t + 1, true, 1 - P0);
       row_max(S, mx, min(kBN, len - t * kBN));
       // region A: exps of tile t || S^T of tile t+1 (computed on the last
       // tile too, on stale LDS data, and discarded)
       f32x16 Sn[2][QB];
-      qk(PK1, Sn);
+      qk(1 - P0, Sn);
       bf16x8 P[2][QB][2];
       exps(S, P);
       schedule_a();
@@ -498,33 +486,14 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) S[kb][qb] = Sn[kb][qb];
-      // tiles t+1 (K_{t+2}, V_{t+1}) must have landed; with three buffers
-      // this iteration's own loads (the newest) may stay in flight
-      if constexpr (NBUF == 3) {
-        if (ld_k) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KMIN + IPW) : "memory");
-        else if (ld_v) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-      } else {
-        wait_and_sync();
-      }
+      wait_and_sync();
     };
     int t = 0;
-    if constexpr (NBUF == 3) {
-      for (; t + 2 < ntiles; t += 3) {
-        iteration(t, std::integral_constant<int, 0>{});
-        iteration(t + 1, std::integral_constant<int, 1>{});
-        iteration(t + 2, std::integral_constant<int, 2>{});
-      }
-      if (t < ntiles) iteration(t, std::integral_constant<int, 0>{});
-      if (t + 1 < ntiles) iteration(t + 1, std::integral_constant<int, 1>{});
-    } else {
-      for (; t + 1 < ntiles; t += 2) {
-        iteration(t, std::integral_constant<int, 0>{});
-        iteration(t + 1, std::integral_constant<int, 1>{});
-      }
-      if (t < ntiles) iteration(t, std::integral_constant<int, 0>{});
+    for (; t + 1 < ntiles; t += 2) {
+      iteration(t, std::integral_constant<int, 0>{});
+      iteration(t + 1, std::integral_constant<int, 1>{});
     }
+    if (t < ntiles) iteration(t, std::integral_constant<int, 0>{});
   }
 
   // -------------------------------------------------------------- epilogue --
