@@ -128,9 +128,10 @@ def test_workspace_sizes(lib):
     o_bytes = 15600 * 10 * 128 * 4
     lse_bytes = 10 * 15600 * 4
     align = lambda x: (x + 255) // 256 * 256
-    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes)
+    bound = lambda B, Hk: align(B * Hk * 16 * 4)  # optional key-norm partials (bf16)
+    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes) + bound(1, 10)
     a.n_kv_chunks = 1
-    assert V.vdit_attn_workspace_bytes(a) == 0
+    assert V.vdit_attn_workspace_bytes(a) == bound(1, 10)
     w5 = WL.WORKLOADS[5]
     h = V.VditAttnArgs()
     h.mode, h.dtype, h.B, h.n_heads, h.n_kv_heads, h.head_dim = 3, 0, 1, 24, 24, 128
@@ -139,7 +140,7 @@ def test_workspace_sizes(lib):
     n = V.vdit_attn_workspace_bytes(h)
     nch, ns = 11, 2  # 264 (chunk, head) units -> 2 token splits for ~512 delta workgroups
     expect = align(nch * ns * 24 * 128 * 128 * 4) + align(nch * ns * 24 * 128 * 4) + \
-        align(nch * 24 * 128 * 128 * 4) + align(nch * 24 * 128 * 4)
+        align(nch * 24 * 128 * 128 * 4) + align(nch * 24 * 128 * 4) + bound(nch, 24)
     assert n == expect
     assert w3.heads == 10
     # FULL on few queries: the optional key-split workspace (256 compute units
@@ -147,8 +148,10 @@ def test_workspace_sizes(lib):
     f = V.VditAttnArgs()
     f.mode, f.dtype, f.B, f.n_heads, f.n_kv_heads, f.head_dim = 0, 0, 1, 16, 16, 64
     f.Lq, f.Lkv = 2040, 10200
-    assert V.vdit_attn_workspace_bytes(f) == align(2 * 2040 * 16 * 64 * 4) + align(2 * 16 * 2040 * 4)
+    assert V.vdit_attn_workspace_bytes(f) == bound(1, 16) + align(2 * 2040 * 16 * 64 * 4) + align(2 * 16 * 2040 * 4)
     f.Lq, f.n_heads, f.n_kv_heads, f.head_dim, f.Lkv = 32760, 12, 12, 128, 32760
+    assert V.vdit_attn_workspace_bytes(f) == bound(1, 12)
+    f.dtype = 1  # float32: neither the bound nor the split
     assert V.vdit_attn_workspace_bytes(f) == 0
     h.head_dim = 96
     with pytest.raises(V.VditError):

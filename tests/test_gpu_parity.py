@@ -153,6 +153,37 @@ def test_full_attention_key_split(D):
     check(o_plain, wo, "bf16", "O (unsplit)"); check_lse(lse_plain, wl, "bf16", "LSE (unsplit)")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_full_attention_bounded_and_online_softmax(D):
+    # 256-query workgroups (8 heads x 64 query tiles: two even rounds on 256
+    # CUs), where the key-norm bound is used: a wavefront whose queries
+    # satisfy 2 c2 |q| max|k| <= 64 skips the running maximum.  Query rows
+    # 4000..6099 are scaled by 8, beyond that bound, so wavefronts of both
+    # kinds share workgroups.  Without the bound (workspace too small) every
+    # wavefront keeps the online maximum.
+    Lq, Lkv, Hq, Hk = 16347, 3001, 8, 2
+    log(f"bounded-score and online-max softmax: D={D} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+    rng = np.random.default_rng(81)
+    q64 = rng.standard_normal((1, Lq, Hq, D))
+    q64[:, 4000:6100] *= 8.0
+    k64 = rng.standard_normal((1, Lkv, Hk, D)); v64 = rng.standard_normal((1, Lkv, Hk, D))
+
+    def bf16(x64):
+        bits = WL.f32_to_bf16_bits(x64.astype(np.float32))
+        return WL.Tensor(WL.bf16_bits_to_f64(bits), bits, "bf16")
+    q, k, v = bf16(q64), bf16(k64), bf16(v64)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o_b, lse_b = V.vdit_attn_fwd(qd, kd, vd)
+    o_o, lse_o = V.vdit_attn_fwd(qd, kd, vd, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([WL.sample_rows(Lq, 128, seed=82), np.arange(3990, 4010),
+                                     np.arange(6090, 6110), [0, Lq - 1]]))
+    wo, wl = O.attention(q.values[:, rows], k.values, v.values)
+    for o, lse, tag in ((o_b, lse_b, "bounded"), (o_o, lse_o, "online")):
+        check(from_dev(o)[:, rows], wo, "bf16", f"O ({tag}, sampled rows)")
+        check_lse(from_dev(lse)[:, :, rows], wl, "bf16", f"LSE ({tag}, sampled rows)")
+
+
 def _sampled_attention(qr64, kr64, v64, rows, scale=None):
     o, l = O.attention(qr64[:, rows], kr64, v64, scale)
     return o, l

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvdit.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "rope_qk.hip", "lse_merge.hip", "attn_mfma.hip", "attn_valu.hip", "hybrid_state.hip"]
+SOURCES = ["abi.cpp", "rope_qk.hip", "lse_merge.hip", "attn_mfma.hip", "attn_valu.hip", "hybrid_state.hip",
+           "key_bound.hip"]
 
 # Packed float32 VALU forms are disabled on purpose: the compiler otherwise
 # forms them from ordinary float code.

@@ -12,6 +12,7 @@
 #include "vdit_internal.hpp"
 
 static_assert(sizeof(vdit_attn_args) == sizeof(vdit::AttnArgs), "vdit_attn_args layout mirror");
+static_assert(vdit::kKeyBoundParts == vdit::kKeyBoundBlocks, "key-bound partials");
 static_assert(offsetof(vdit_attn_args, workspace_bytes) == offsetof(vdit::AttnArgs, workspace_bytes),
               "vdit_attn_args layout mirror");
 
@@ -63,28 +64,63 @@ hipError_t launch_attn(const vdit::AttnLaunch& p, int dtype, hipStream_t s) {
   return dtype == VDIT_BF16 ? vdit::launch_attn_bf16(p, s) : vdit::launch_attn_f32(p, s);
 }
 
-// Plain attention of p (FULL or ROLLING), with the key split when the
-// caller's workspace holds its partials.  A workspace that is large enough
-// but misplaced is an error; a missing or smaller one runs unsplit.
+size_t q_bytes(const vdit::AttnArgs& a) {
+  return size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * vdit::esize(a.dtype);
+}
+
+// Optional workspace area [off, off + bytes): usable when the caller's
+// workspace holds it.  A workspace that holds it but is misplaced (unaligned
+// or overlapping o) is an error.
+vdit_status optional_area(const vdit::AttnArgs& a, size_t off, size_t bytes, char** area) {
+  *area = nullptr;
+  if (bytes == 0 || !a.workspace || a.workspace_bytes < off + bytes) return VDIT_OK;
+  if (!vdit::aligned16(a.workspace)) return fail(VDIT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (vdit::overlaps(a.workspace, off + bytes, a.o, q_bytes(a)))
+    return fail(VDIT_ERR_INVALID_ARG, "workspace overlaps o");
+  *area = static_cast<char*>(a.workspace) + off;
+  return VDIT_OK;
+}
+
+// Bounded-score softmax: key-norm maxima of the launch's keys into the
+// workspace area `area` (bf16 only), or nothing when there is no area.
+vdit_status add_key_bound(vdit::AttnLaunch& p, const vdit::KvSeg& keys, char* area, hipStream_t stream,
+                          int64_t part_len = 0) {
+  if (!area || keys.len <= 0 || !vdit::attn_uses_key_bound(p)) return VDIT_OK;
+  float* out = reinterpret_cast<float*>(area);
+  if (auto st = from_hip(vdit::launch_key_bound(keys, p.B, p.Hk, p.D, part_len, out, stream), "key bound launch");
+      st != VDIT_OK)
+    return st;
+  p.kbound = out;
+  p.kbound_n = vdit::kKeyBoundBlocks;
+  return VDIT_OK;
+}
+
+// Plain attention of p (FULL or ROLLING), with the key-norm bound and the
+// key split when the caller's workspace holds them (bound first, then the
+// split partials); a missing or smaller workspace runs without them.
 vdit_status launch_plain(vdit::AttnLaunch p, const vdit::AttnArgs& a, hipStream_t stream, const char* what) {
   const int64_t keys = p.nseg ? p.seg[0].len : 0;
+  const size_t kb = vdit::kbound_bytes(a);
+  char* bound = nullptr;
+  if (auto st = optional_area(a, 0, kb, &bound); st != VDIT_OK) return st;
   const vdit::SplitPlan sp = vdit::split_plan(a.dtype, a.B, a.Lq, a.n_heads, keys, vdit::device_cus());
   const size_t need = vdit::split_workspace_bytes(sp, a.B, a.Lq, a.n_heads, a.head_dim);
-  if (need == 0 || !a.workspace || a.workspace_bytes < need)
-    return from_hip(launch_attn(p, a.dtype, stream), what);
-  const size_t nq = size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * vdit::esize(a.dtype);
-  if (!vdit::aligned16(a.workspace)) return fail(VDIT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (vdit::overlaps(a.workspace, need, a.o, nq)) return fail(VDIT_ERR_INVALID_ARG, "workspace overlaps o");
-  char* ws = static_cast<char*>(a.workspace);
-  p.nsplit = sp.nsplit;
-  p.split_keys = sp.split_keys;
-  p.epi = vdit::kEpiRing;  // every key range writes its float32 partial
-  p.has_prev = 0;
-  p.final_out = 0;
-  p.part_o = reinterpret_cast<float*>(ws);
-  p.part_lse = reinterpret_cast<float*>(
-      ws + vdit::align256(size_t(sp.nsplit) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * 4));
+  char* ws = nullptr;
+  if (auto st = optional_area(a, kb, need, &ws); st != VDIT_OK) return st;
+  if (ws) {
+    p.nsplit = sp.nsplit;
+    p.split_keys = sp.split_keys;
+    p.epi = vdit::kEpiRing;  // every key range writes its float32 partial
+    p.has_prev = 0;
+    p.final_out = 0;
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(
+        ws + vdit::align256(size_t(sp.nsplit) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * 4));
+  }
+  if (p.nseg)
+    if (auto st = add_key_bound(p, p.seg[0], bound, stream); st != VDIT_OK) return st;
   if (auto st = from_hip(launch_attn(p, a.dtype, stream), what); st != VDIT_OK) return st;
+  if (!ws) return VDIT_OK;
   vdit::SplitMergeLaunch m;
   m.part_o = p.part_o;
   m.part_lse = p.part_lse;
@@ -183,11 +219,15 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       auto seg_of = [&](int c) -> vdit::KvSeg {
         return {a.k_chunks[c], a.v_chunks[c], a.chunk_len[c], a.chunk_len[c] * a.n_kv_heads * D};
       };
+      char* bound = nullptr;
+      if (auto st = optional_area(a, vdit::ring_workspace_bytes(a), vdit::kbound_bytes(a), &bound); st != VDIT_OK)
+        return st;
       if (n == 1) {
         vdit::AttnLaunch p = base_launch(a);
         if (a.chunk_len[0] > 0) {
           p.nseg = 1;
           p.seg[0] = seg_of(0);
+          if (auto st = add_key_bound(p, p.seg[0], bound, stream); st != VDIT_OK) return st;
         }
         return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(RING) launch");
       }
@@ -200,6 +240,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         if (a.chunk_len[c] > 0) {
           p.nseg = 1;
           p.seg[0] = seg_of(c);
+          if (auto st = add_key_bound(p, p.seg[0], bound, stream); st != VDIT_OK) return st;
         }
         p.epi = vdit::kEpiRing;
         p.part_o = part_o;
@@ -275,6 +316,13 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       p.hk = a.k;
       p.hv = a.v;
       p.nseg = 1;
+      char* bound = nullptr;
+      if (auto st = optional_area(a, lay.total, vdit::kbound_bytes(a), &bound); st != VDIT_OK) return st;
+      // a bound per chunk (so a chunk's result does not depend on the others)
+      if (auto st = add_key_bound(p, vdit::KvSeg{a.k, a.v, a.Lq, a.Lq * a.n_kv_heads * D}, bound, stream,
+                                  a.chunk_tokens);
+          st != VDIT_OK)
+        return st;
       return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(CHUNK_HYBRID) launch");
     }
   }

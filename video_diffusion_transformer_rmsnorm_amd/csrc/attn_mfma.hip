@@ -50,8 +50,14 @@
 #ifndef VDIT_ATTN_SCHED
 #define VDIT_ATTN_SCHED 1
 #endif
+#ifndef VDIT_ATTN_FENCED
+#define VDIT_ATTN_FENCED 1  // interleave written in source order with scheduling fences
+#endif
 #ifndef VDIT_ATTN_VALU_PER_MFMA
-#define VDIT_ATTN_VALU_PER_MFMA 5
+#define VDIT_ATTN_VALU_PER_MFMA 4  // VALU ops placed after each QK^T MFMA (4- and 2-wavefront kernels)
+#endif
+#ifndef VDIT_ATTN_VALU_PER_MFMA8
+#define VDIT_ATTN_VALU_PER_MFMA8 5  // ... in the 8-wavefront kernel
 #endif
 #ifndef VDIT_ATTN_KPREF
 #define VDIT_ATTN_KPREF 3  // K operand reads issued ahead of their MFMA
@@ -70,6 +76,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kBN = 64;        // keys per tile
 constexpr float kLazy = 8.0f;  // rescale threshold of the running max (log2 units)
+constexpr float kBoundSpan = 64.0f;  // largest 2 m_i (log2 units) of the bounded-score path
 
 // 16 bytes per lane from a buffer resource straight into LDS at M0 + 16*lane.
 // (The builtin only exists for the device pass; the host pass sees an empty
@@ -284,6 +291,52 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   for (int qb = 0; qb < QB; ++qb) { m2[qb] = -INFINITY; lsum[qb] = 0.f; }
   const float c2 = p.scale_log2;
 
+  // Bounded scores (Cauchy-Schwarz): s_ij <= |q_i| |k_j| <= |q_i| Kmax, with
+  // Kmax^2 the largest squared key norm from the bound pass.  m_i = c2 |q_i|
+  // Kmax then bounds every score of query i in log2 units, so
+  // p = 2^(c2 s - m_i) <= 1 needs neither a running maximum nor rescaling;
+  // and as c2 s >= -m_i, the row's largest p is >= 2^(-2 m_i): for
+  // 2 m_i <= kBoundSpan nothing that matters underflows.  A wavefront takes
+  // this path when all its queries qualify; otherwise it keeps the online
+  // maximum (both paths pass the same barriers).
+  // (8-wavefront kernel only: the 4- and 2-wavefront kernels keep their
+  // single loop, whose instruction schedule a second copy disturbs)
+  bool fast = false;
+  if (NW == 8 && p.kbound != nullptr) {
+    const float* kbp = p.kbound + ((chunk_id * p.B + b) * p.Hk + hk) * p.kbound_n;
+    float kmax2 = 0.f;
+    for (int i = 0; i < p.kbound_n; ++i) kmax2 = fmaxf(kmax2, kbp[i]);
+    bool ok = kmax2 < 3.0e38f;
+    float mb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = static_cast<float>(Qr[qb][ks][j]);
+          n2 = fmaf(x, x, n2);
+        }
+      n2 += other_half(n2);
+      mb[qb] = c2 * sqrtf(n2 * kmax2);
+      ok = ok && (2.f * mb[qb] <= kBoundSpan);
+    }
+#if defined(__HIP_DEVICE_COMPILE__)
+    // keep Q's bf16 registers as loaded (reading them as floats above must not
+    // change how the compiler holds them through the main loop)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(Qr[qb][ks]));
+#endif
+    fast = __ballot(!ok) == 0;
+    if (fast) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m2[qb] = mb[qb];
+    }
+  }
+
   // S^T of the tile in K buffer `buf` (unmasked); each K operand feeds QB MFMAs
   auto qk = [&](int buf, f32x16 (*S)[QB]) {
     const char* Kl = lds + buf * KTILE_B + kaddr;
@@ -361,26 +414,68 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     }
   };
 
-  // p = 2^(s*c2 - m2) -> P (bf16 B operands); row sum as a shallow tree
-  auto exps = [&](f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mn = m2[qb];
-      float part[4];
+  // keys >= nv of a tail tile -> -inf (bounded-score path)
+  auto mask_tail = [&](f32x16 (*S)[QB], int nv) {
+    if (nv < kBN) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          float e[8];
+        for (int i = 0; i < 16; ++i) {
+          const int key = 32 * kb + 16 * (i >> 3) + 8 * g + (i & 7);
+          if (key >= nv) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(S[kb][qb][8 * hh + j], c2, -mn));
+            for (int qb = 0; qb < QB; ++qb) S[kb][qb][i] = -INFINITY;
+          }
+        }
+    }
+  };
+
+  // Region A in source order: S^T of the next tile (K buffer `buf`) on the
+  // matrix cores, each MFMA followed by its share of this tile's
+  // p = 2^(s*c2 - m2) -> P (bf16 B operands of the PV product), with the
+  // row sum as a shallow tree per group of 8.  (The instruction scheduler
+  // keeps this interleave; a wavefront issues in order, so the exponentials
+  // overlap the matrix cores only when they sit between MFMAs.)
+  auto qk_exps = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
+    constexpr int NSTEP = 2 * KS;        // MFMAs per query block
+    constexpr int NEL = 32 * QB;         // scores per lane
+    constexpr int PER = NEL / NSTEP;     // exponentials per MFMA step
+    static_assert(NEL % NSTEP == 0 && PER % 2 == 0, "exponential split");
+    const char* Kl = lds + buf * KTILE_B + kaddr;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Sn[kb][qb][i] = 0.f;
+    float e[NEL];
+    float part[QB][4];
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const int ks = st >> 1, kb = st & 1;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + ks * 32 + kb * 32 * KROWB);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        Sn[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[qb][ks], Sn[kb][qb], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int el = st * PER + x;  // (qb, kb, hh, j) in that order
+        const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15;
+        e[el] = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
+        if ((el & 7) == 7) {
+          const int g0 = el - 7, hh = i >> 3;
           bf16x8 pv8;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pv8[j] = static_cast<__bf16>(e[j]);
-          P[kb][qb][hh] = pv8;
-          part[2 * kb + hh] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+          for (int j = 0; j < 8; ++j) pv8[j] = static_cast<__bf16>(e[g0 + j]);
+          P[kb2][qb][hh] = pv8;
+          part[qb][2 * kb2 + hh] =
+              ((e[g0] + e[g0 + 1]) + (e[g0 + 2] + e[g0 + 3])) + ((e[g0 + 4] + e[g0 + 5]) + (e[g0 + 6] + e[g0 + 7]));
         }
-      lsum[qb] += (part[0] + part[1]) + (part[2] + part[3]);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      lsum[qb] += (part[qb][0] + part[qb][1]) + (part[qb][2] + part[qb][3]);
 #if defined(__HIP_DEVICE_COMPILE__)
       // materialise the sum here: otherwise the compiler sinks these adds
       // into the next tile and keeps the exponentials live across the PV
@@ -419,7 +514,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VDIT_ATTN_VALU_PER_MFMA, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NW == 8 ? VDIT_ATTN_VALU_PER_MFMA8 : VDIT_ATTN_VALU_PER_MFMA, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -440,12 +535,114 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #endif
   };
 
+  // Fenced form of the two regions: the interleave is written out in source
+  // order and pinned with scheduling fences after every MFMA step, so it does
+  // not depend on the scheduler's pattern matching.  Region A: step st issues
+  // the K operand read for step st + KPREF, the MFMA(s) of step st, and its
+  // share of this tile's exponentials (pairs packed to bf16 as they finish,
+  // their sum folded into a running total).  Region B: step st issues the
+  // transposed V reads for step st + VPREF, the PV MFMA(s) of step st and a
+  // slice of the next tile's lane maximum.
+  auto region_a = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
+    constexpr int NSTEP = 2 * KS;
+    constexpr int NEL = 32 * QB;
+    constexpr int PER = NEL / NSTEP;
+    constexpr int KP = VDIT_ATTN_KPREF < NSTEP ? VDIT_ATTN_KPREF : NSTEP;
+    static_assert(NEL % NSTEP == 0 && PER % 2 == 0, "exponential split");
+    const char* Kl = lds + buf * KTILE_B + kaddr;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Sn[kb][qb][i] = 0.f;
+    bf16x8 ka[NSTEP];
+#pragma unroll
+    for (int st = 0; st < KP; ++st)
+      ka[st] = *reinterpret_cast<const bf16x8*>(Kl + (st >> 1) * 32 + (st & 1) * 32 * KROWB);
+    float run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) run[qb] = 0.f;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + KP < NSTEP) {
+        const int sn = st + KP;
+        ka[sn] = *reinterpret_cast<const bf16x8*>(Kl + (sn >> 1) * 32 + (sn & 1) * 32 * KROWB);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        Sn[st & 1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], Qr[qb][st >> 1], Sn[st & 1][qb], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < PER; x += 2) {
+        const int el = st * PER + x;  // (qb, kb, hh, j) in that order
+        const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15, hh = i >> 3, j = i & 7;
+        const float e0 = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
+        const float e1 = fast_exp2(fmaf(S[kb2][qb][i + 1], c2, -m2[qb]));
+        P[kb2][qb][hh][j] = static_cast<__bf16>(e0);
+        P[kb2][qb][hh][j + 1] = static_cast<__bf16>(e1);
+        run[qb] += e0 + e1;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(run[qb]));  // keep the sum in this step (no sinking)
+#endif
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += run[qb];
+  };
+  auto region_b = [&](int buf, bf16x8 (*P)[QB][2], f32x16 (*Sn)[QB], float* mx, auto domaxc) {
+    constexpr bool DOMAX = decltype(domaxc)::value;
+    constexpr int NSTEP = 4 * DB;
+    constexpr int PER = 32 / NSTEP;  // scores of one query block folded into the max per step
+    constexpr int VP = VDIT_ATTN_VPREF < NSTEP ? VDIT_ATTN_VPREF : NSTEP;
+    const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
+    i16x8 va[NSTEP];
+    auto vread = [&](int st) {
+      const int kk = st / DB, db = st % DB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk) * ROWB));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk + 4) * ROWB));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+#pragma unroll
+    for (int st = 0; st < VP; ++st) va[st] = vread(st);
+    float m[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m[qb] = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + VP < NSTEP) va[st + VP] = vread(st + VP);
+      const int kk = st / DB, db = st % DB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[st]), P[kk >> 1][qb][kk & 1],
+                                                            O[db][qb], 0, 0, 0);
+      if constexpr (DOMAX) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int x = 0; x < PER; x += 2) {
+            const int el = st * PER + x;
+            m[qb] = fmaxf(fmaxf(m[qb], Sn[el >> 4][qb][el & 15]), Sn[el >> 4][qb][(el & 15) + 1]);
+#if defined(__HIP_DEVICE_COMPILE__)
+            asm volatile("" : "+v"(m[qb]));  // keep the max in this step (no sinking)
+#endif
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DOMAX) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = m[qb];
+    }
+  };
+
   auto wait_and_sync = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
-  if (ntiles > 0) {
+  auto main_loop = [&](auto fastc) {
+    constexpr bool FAST = decltype(fastc)::value;
     // prologue: K_0, V_0, K_1 in flight; S^T of tile 0
     issue(0, false, 0);
     issue(0, true, 0);
@@ -454,8 +651,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     f32x16 S[2][QB];
     qk(0, S);
     float mx[QB];
+    if constexpr (!FAST) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = lane_max(S, qb);
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = lane_max(S, qb);
+    }
     __syncthreads();
 
     auto iteration = [&](int t, auto parity) {
@@ -463,25 +662,35 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       // stream K_{t+2} into K buffer P0 and V_{t+1} into V buffer 1-P0
       if (t + 2 < ntiles) issue(t + 2, false, P0);
       if (t + 1 < ntiles) issue(t + 1, true, 1 - P0);
-      row_max(S, mx, min(kBN, len - t * kBN));
+      if constexpr (FAST) mask_tail(S, min(kBN, len - t * kBN));
+      else row_max(S, mx, min(kBN, len - t * kBN));
       // region A: exps of tile t || S^T of tile t+1 (computed on the last
       // tile too, on stale LDS data, and discarded)
       f32x16 Sn[2][QB];
-      qk(1 - P0, Sn);
       bf16x8 P[2][QB][2];
-      exps(S, P);
+#if VDIT_ATTN_FENCED
+      __builtin_amdgcn_sched_barrier(0);
+      region_a(1 - P0, Sn, S, P);
+      // region B: O^T += V^T P^T || lane max of tile t+1's scores
+      region_b(P0, P, Sn, mx, std::integral_constant<bool, !FAST>{});
+      __builtin_amdgcn_sched_barrier(0);
+#else
+      qk_exps(1 - P0, Sn, S, P);
       schedule_a();
       __builtin_amdgcn_sched_barrier(0);
       // region B: O^T += V^T P^T || lane max of tile t+1's scores
       pv(P0, P);
+      if constexpr (!FAST) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = lane_max(Sn, qb);
+        for (int qb = 0; qb < QB; ++qb) {
+          mx[qb] = lane_max(Sn, qb);
 #if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(mx[qb]));  // keep the max here, among the PV MFMAs
+          asm volatile("" : "+v"(mx[qb]));  // keep the max here, among the PV MFMAs
 #endif
+        }
       }
       schedule_b();
+#endif
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -494,6 +703,14 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       iteration(t + 1, std::integral_constant<int, 1>{});
     }
     if (t < ntiles) iteration(t, std::integral_constant<int, 0>{});
+  };
+  if (ntiles > 0) {
+    if constexpr (NW == 8) {
+      if (fast) main_loop(std::true_type{});
+      else main_loop(std::false_type{});
+    } else {
+      main_loop(std::false_type{});
+    }
   }
 
   // -------------------------------------------------------------- epilogue --
@@ -653,6 +870,21 @@ bool prefer_wide(int64_t wg256, int cus) {
 }
 
 }  // namespace
+
+namespace {
+// Workgroup shape of a bf16 launch: 8, 4 or 2 wavefronts (one 32-query block
+// each).
+int attn_waves(const AttnLaunch& p) {
+  const int64_t rows = (p.epi == kEpiHybrid ? p.chunk : p.Lq);
+  const int64_t units = int64_t(p.Hq) * p.B * (p.epi == kEpiHybrid ? p.n_chunks : 1) * (p.nsplit > 1 ? p.nsplit : 1);
+  const int64_t wg128 = ((rows + 127) / 128) * units;
+  const int64_t wg256 = ((rows + 255) / 256) * units;
+  if (prefer_wide(wg256, device_cus())) return 8;
+  return wg128 >= 512 ? 4 : 2;
+}
+}  // namespace
+
+bool attn_uses_key_bound(const AttnLaunch& p) { return VDIT_ATTN_BIG_QB == 1 && attn_waves(p) == 8; }
 
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
   // Workgroup shape by problem size: 256 queries (8 wavefronts) when its

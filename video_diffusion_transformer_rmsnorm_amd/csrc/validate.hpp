@@ -303,16 +303,36 @@ inline CheckResult check_attn(const AttnArgs& a) {
   return CheckResult::good();
 }
 
-// Workspace of one call on a device with `cus` compute units.  FULL and
-// ROLLING need none; the amount returned for them enables the key split.
-inline size_t attn_workspace_bytes(const AttnArgs& a, int cus) {
+// Key-norm bound of the bounded-score softmax (bf16): 16 partial maxima per
+// (batch, kv head), and per chunk in the chunk-hybrid mode.  Optional in
+// every mode.
+constexpr int kKeyBoundParts = 16;
+inline size_t kbound_bytes(const AttnArgs& a) {
+  if (a.dtype != 0) return 0;
+  const size_t runs = a.mode == 3 ? size_t(hybrid_layout(a).n_chunks) : 1;
+  return align256(runs * size_t(a.B) * size_t(a.n_kv_heads) * kKeyBoundParts * 4);
+}
+
+// Bytes of a workspace that mode requires (RING with several chunks,
+// CHUNK_HYBRID); FULL and ROLLING require none.
+inline size_t attn_required_bytes(const AttnArgs& a) {
   switch (a.mode) {
     case 1: return ring_workspace_bytes(a);
     case 3: return hybrid_layout(a).total;
-    default:
-      return split_workspace_bytes(split_plan(a.dtype, a.B, a.Lq, a.n_heads, attn_keys(a), cus), a.B, a.Lq,
-                                   a.n_heads, a.head_dim);
+    default: return 0;
   }
+}
+
+// Workspace of one call on a device with `cus` compute units: the required
+// part, then the key-norm bound, then (FULL, ROLLING) the key-split
+// partials.  Everything past the required part is optional and used when
+// the workspace holds it.
+inline size_t attn_workspace_bytes(const AttnArgs& a, int cus) {
+  size_t n = attn_required_bytes(a) + kbound_bytes(a);
+  if (a.mode == 0 || a.mode == 2)
+    n += split_workspace_bytes(split_plan(a.dtype, a.B, a.Lq, a.n_heads, attn_keys(a), cus), a.B, a.Lq,
+                               a.n_heads, a.head_dim);
+  return n;
 }
 
 // Workspace check that ignores the workspace fields themselves (used by

@@ -52,7 +52,19 @@ struct AttnLaunch {
   // writes its partial to part_o / part_lse offset by s whole partials
   int32_t nsplit;
   int64_t split_keys;
+  // bounded-score softmax: kbound[((r * B + b) * Hk + hk) * kbound_n + i]
+  // are partial maxima of the squared norms of the keys a workgroup attends
+  // to (r: its hybrid chunk, else 0); NULL: online maximum
+  const float* kbound;
+  int32_t kbound_n;
 };
+
+// Partial maxima of squared key norms (bf16 keys), per run of part_len keys
+// (part_len <= 0: one run, the whole segment), batch and kv head:
+// out[((r * B + b) * Hk + hk) * kKeyBoundBlocks + i].
+constexpr int kKeyBoundBlocks = 16;
+hipError_t launch_key_bound(const KvSeg& seg, int32_t B, int32_t Hk, int32_t D, int64_t part_len, float* out,
+                            hipStream_t s);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s);
@@ -60,6 +72,9 @@ hipError_t launch_attn_f32(const AttnLaunch& p, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cus();
+
+// Whether the bf16 kernel chosen for p uses the key-norm bound (p.kbound).
+bool attn_uses_key_bound(const AttnLaunch& p);
 
 // Merge of nsplit float32 attention partials ([nsplit][B][L][H][D] normalised
 // O, [nsplit][B][H][L] LSE) into o (out_dtype) and lse (may be NULL).
