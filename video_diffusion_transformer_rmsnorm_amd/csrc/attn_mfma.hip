@@ -50,6 +50,9 @@
 #ifndef VDIT_ATTN_SCHED
 #define VDIT_ATTN_SCHED 1
 #endif
+#ifndef VDIT_ATTN_NPB
+#define VDIT_ATTN_NPB 6  // exponential pairs (of 16) computed among the PV MFMAs
+#endif
 #ifndef VDIT_ATTN_FENCED
 #define VDIT_ATTN_FENCED 1  // interleave written in source order with scheduling fences
 #endif
@@ -543,12 +546,31 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // their sum folded into a running total).  Region B: step st issues the
   // transposed V reads for step st + VPREF, the PV MFMA(s) of step st and a
   // slice of the next tile's lane maximum.
+  // Exponential pairs (2 scores, one packed bf16 pair of P) of this tile:
+  // pairs [0, NPA) go to region A, spread evenly over its MFMA steps; the
+  // last NPB pairs (second key half) to region B, each placed before the
+  // first PV step that reads it, so both regions carry similar VALU work.
+  constexpr int NPAIR = 16 * QB;
+  constexpr int NPB = QB == 1 ? VDIT_ATTN_NPB : 0;
+  constexpr int NPA = NPAIR - NPB;
+  static_assert(NPB >= 0 && NPB <= 8, "pairs moved to region B");
+  float run[QB];
+  // p for pair pr of query block ... -> P, running sum
+  auto exp_pair = [&](int pr, f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
+    const int el = 2 * pr;  // (qb, kb, hh, j) in that order
+    const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15, hh = i >> 3, j = i & 7;
+    const float e0 = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
+    const float e1 = fast_exp2(fmaf(S[kb2][qb][i + 1], c2, -m2[qb]));
+    P[kb2][qb][hh][j] = static_cast<__bf16>(e0);
+    P[kb2][qb][hh][j + 1] = static_cast<__bf16>(e1);
+    run[qb] += e0 + e1;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(run[qb]));  // keep the sum in this step (no sinking)
+#endif
+  };
   auto region_a = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
     constexpr int NSTEP = 2 * KS;
-    constexpr int NEL = 32 * QB;
-    constexpr int PER = NEL / NSTEP;
     constexpr int KP = VDIT_ATTN_KPREF < NSTEP ? VDIT_ATTN_KPREF : NSTEP;
-    static_assert(NEL % NSTEP == 0 && PER % 2 == 0, "exponential split");
     const char* Kl = lds + buf * KTILE_B + kaddr;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -560,7 +582,6 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
     for (int st = 0; st < KP; ++st)
       ka[st] = *reinterpret_cast<const bf16x8*>(Kl + (st >> 1) * 32 + (st & 1) * 32 * KROWB);
-    float run[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) run[qb] = 0.f;
 #pragma unroll
@@ -573,28 +594,17 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       for (int qb = 0; qb < QB; ++qb)
         Sn[st & 1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], Qr[qb][st >> 1], Sn[st & 1][qb], 0, 0, 0);
 #pragma unroll
-      for (int x = 0; x < PER; x += 2) {
-        const int el = st * PER + x;  // (qb, kb, hh, j) in that order
-        const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15, hh = i >> 3, j = i & 7;
-        const float e0 = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
-        const float e1 = fast_exp2(fmaf(S[kb2][qb][i + 1], c2, -m2[qb]));
-        P[kb2][qb][hh][j] = static_cast<__bf16>(e0);
-        P[kb2][qb][hh][j + 1] = static_cast<__bf16>(e1);
-        run[qb] += e0 + e1;
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(run[qb]));  // keep the sum in this step (no sinking)
-#endif
-      }
+      for (int pr = 0; pr < NPA; ++pr)
+        if ((pr * NSTEP) / NPA == st) exp_pair(pr, S, P);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb] += run[qb];
   };
-  auto region_b = [&](int buf, bf16x8 (*P)[QB][2], f32x16 (*Sn)[QB], float* mx, auto domaxc) {
+  auto region_b = [&](int buf, f32x16 (*S)[QB], bf16x8 (*P)[QB][2], f32x16 (*Sn)[QB], float* mx, auto domaxc) {
     constexpr bool DOMAX = decltype(domaxc)::value;
     constexpr int NSTEP = 4 * DB;
     constexpr int PER = 32 / NSTEP;  // scores of one query block folded into the max per step
     constexpr int VP = VDIT_ATTN_VPREF < NSTEP ? VDIT_ATTN_VPREF : NSTEP;
+    constexpr int LASTB = 3 * DB;    // first PV step that reads the last pair
     const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
     i16x8 va[NSTEP];
     auto vread = [&](int st) {
@@ -616,6 +626,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       for (int qb = 0; qb < QB; ++qb)
         O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[st]), P[kk >> 1][qb][kk & 1],
                                                             O[db][qb], 0, 0, 0);
+      // second-half pairs: pair NPA + k at step k * LASTB / NPB, before its
+      // first reader (PV step 2 * DB for the first quarter, 3 * DB after)
+#pragma unroll
+      for (int k = 0; k < NPB; ++k)
+        if ((k * LASTB) / NPB == st) exp_pair(NPA + k, S, P);
       if constexpr (DOMAX) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -630,6 +645,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += run[qb];
     if constexpr (DOMAX) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = m[qb];
@@ -672,7 +689,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       __builtin_amdgcn_sched_barrier(0);
       region_a(1 - P0, Sn, S, P);
       // region B: O^T += V^T P^T || lane max of tile t+1's scores
-      region_b(P0, P, Sn, mx, std::integral_constant<bool, !FAST>{});
+      region_b(P0, S, P, Sn, mx, std::integral_constant<bool, !FAST>{});
       __builtin_amdgcn_sched_barrier(0);
 #else
       qk_exps(1 - P0, Sn, S, P);
