@@ -101,7 +101,7 @@ int main() {
     r.frame = 9;
     EXPECT(attn_keys(r) == 5 * 2040, "rolling keys once the ring is full");
     EXPECT(attn_workspace_bytes(r, 256) == kbound_bytes(r) + split_workspace_bytes(split_plan(0, 1, 2040, 16, 10200, 256), 1, 2040, 16, 64), "rolling workspace");
-    EXPECT(kbound_bytes(r) == 1024, "key-norm partials: 16 per (batch, kv head)");
+    EXPECT(kbound_bytes(r) == 4096, "key-norm partials: 64 per (batch, kv head)");
     r.dtype = 1;
     EXPECT(kbound_bytes(r) == 0 && attn_workspace_bytes(r, 256) == 0, "float32 needs no optional workspace");
   }

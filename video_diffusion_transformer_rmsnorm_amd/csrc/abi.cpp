@@ -12,7 +12,8 @@
 #include "vdit_internal.hpp"
 
 static_assert(sizeof(vdit_attn_args) == sizeof(vdit::AttnArgs), "vdit_attn_args layout mirror");
-static_assert(vdit::kKeyBoundParts == vdit::kKeyBoundBlocks, "key-bound partials");
+static_assert(vdit::kKeyBoundParts == vdit::kKeyBoundBlocks && vdit::kKeyBoundBlocks <= 64,
+              "key-bound partials: one per lane of a wavefront");
 static_assert(offsetof(vdit_attn_args, workspace_bytes) == offsetof(vdit::AttnArgs, workspace_bytes),
               "vdit_attn_args layout mirror");
 

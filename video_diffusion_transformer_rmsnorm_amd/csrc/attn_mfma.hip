@@ -306,9 +306,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // single loop, whose instruction schedule a second copy disturbs)
   bool fast = false;
   if (NW == 8 && p.kbound != nullptr) {
+    // the partial maxima (at most 64): one per lane, then a wavefront max
     const float* kbp = p.kbound + ((chunk_id * p.B + b) * p.Hk + hk) * p.kbound_n;
-    float kmax2 = 0.f;
-    for (int i = 0; i < p.kbound_n; ++i) kmax2 = fmaxf(kmax2, kbp[i]);
+    float kmax2 = lane < p.kbound_n ? kbp[lane] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, o));
     bool ok = kmax2 < 3.0e38f;
     float mb[QB];
 #pragma unroll

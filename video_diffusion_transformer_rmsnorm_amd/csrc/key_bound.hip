@@ -34,6 +34,7 @@ __global__ __launch_bounds__(kBoundThreads) void key_bound_kernel(KvSeg seg, int
   const int c = tid % TPR;
   const uint16_t* base = static_cast<const uint16_t*>(seg.k) + b * seg.bstride + int64_t(hk) * D + c * 8;
   float best = 0.f;
+#pragma unroll 4
   for (int64_t j = j0 + tid / TPR; j < j1; j += RPP) {
     float x[8];
     unpack8(*reinterpret_cast<const uint4*>(base + j * int64_t(Hk) * D), x);

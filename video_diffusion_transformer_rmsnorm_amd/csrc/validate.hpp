@@ -303,10 +303,10 @@ inline CheckResult check_attn(const AttnArgs& a) {
   return CheckResult::good();
 }
 
-// Key-norm bound of the bounded-score softmax (bf16): 16 partial maxima per
+// Key-norm bound of the bounded-score softmax (bf16): 64 partial maxima per
 // (batch, kv head), and per chunk in the chunk-hybrid mode.  Optional in
 // every mode.
-constexpr int kKeyBoundParts = 16;
+constexpr int kKeyBoundParts = 64;
 inline size_t kbound_bytes(const AttnArgs& a) {
   if (a.dtype != 0) return 0;
   const size_t runs = a.mode == 3 ? size_t(hybrid_layout(a).n_chunks) : 1;

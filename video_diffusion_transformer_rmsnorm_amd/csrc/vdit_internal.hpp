@@ -62,7 +62,7 @@ struct AttnLaunch {
 // Partial maxima of squared key norms (bf16 keys), per run of part_len keys
 // (part_len <= 0: one run, the whole segment), batch and kv head:
 // out[((r * B + b) * Hk + hk) * kKeyBoundBlocks + i].
-constexpr int kKeyBoundBlocks = 16;
+constexpr int kKeyBoundBlocks = 64;
 hipError_t launch_key_bound(const KvSeg& seg, int32_t B, int32_t Hk, int32_t D, int64_t part_len, float* out,
                             hipStream_t s);
 
