@@ -53,6 +53,9 @@
 #ifndef VDIT_ATTN_NPB
 #define VDIT_ATTN_NPB 6  // exponential pairs (of 16) computed among the PV MFMAs
 #endif
+#ifndef VDIT_ATTN_DOT2
+#define VDIT_ATTN_DOT2 0  // row sums by v_dot2_f32_bf16 over the packed bf16 p (slower: a serial accumulate)
+#endif
 #ifndef VDIT_ATTN_FENCED
 #define VDIT_ATTN_FENCED 1  // interleave written in source order with scheduling fences
 #endif
@@ -563,9 +566,17 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15, hh = i >> 3, j = i & 7;
     const float e0 = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
     const float e1 = fast_exp2(fmaf(S[kb2][qb][i + 1], c2, -m2[qb]));
-    P[kb2][qb][hh][j] = static_cast<__bf16>(e0);
-    P[kb2][qb][hh][j + 1] = static_cast<__bf16>(e1);
+    const __bf16 b0 = static_cast<__bf16>(e0), b1 = static_cast<__bf16>(e1);
+    P[kb2][qb][hh][j] = b0;
+    P[kb2][qb][hh][j + 1] = b1;
+#if VDIT_ATTN_DOT2
+    // the row sum of the rounded p that the PV product uses: one v_dot2 with
+    // (1, 1) per packed pair
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    run[qb] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2v{b0, b1}, bf16x2v{(__bf16)1.0f, (__bf16)1.0f}, run[qb], false);
+#else
     run[qb] += e0 + e1;
+#endif
 #if defined(__HIP_DEVICE_COMPILE__)
     asm volatile("" : "+v"(run[qb]));  // keep the sum in this step (no sinking)
 #endif
@@ -916,11 +927,13 @@ hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
   const int64_t wg256 = ((rows + 255) / 256) * units;
   const bool wide = prefer_wide(wg256, device_cus());
   if (p.D == 128) {
-    if (VDIT_ATTN_BIG_QB == 2 && wg256 >= 512) return launch_cfg<128, 4, 2>(p, s);
+    if constexpr (VDIT_ATTN_BIG_QB == 2)
+      if (wg256 >= 512) return launch_cfg<128, 4, 2>(p, s);
     if (wide) return launch_cfg<128, 8, 1>(p, s);
     return wg128 >= 512 ? launch_cfg<128, 4, 1>(p, s) : launch_cfg<128, 2, 1>(p, s);
   }
-  if (VDIT_ATTN_BIG_QB == 2 && wg256 >= 512) return launch_cfg<64, 4, 2>(p, s);
+  if constexpr (VDIT_ATTN_BIG_QB == 2)
+    if (wg256 >= 512) return launch_cfg<64, 4, 2>(p, s);
   if (wide) return launch_cfg<64, 8, 1>(p, s);
   return wg128 >= 512 ? launch_cfg<64, 4, 1>(p, s) : launch_cfg<64, 2, 1>(p, s);
 }
