@@ -156,22 +156,38 @@ __global__ __launch_bounds__(256) void hybrid_delta_mfma_kernel(HybridStateLaunc
   const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.L * p.Hk + hk) * D;
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.L * p.Hk + hk) * D;
 
+  // tile loads run one tile ahead in registers: tile j+1 is in flight while
+  // tile j is on the matrix cores
+  constexpr int NCH = kMDeltaBN * CPR / 256;  // 16-byte chunks per thread per tile
+  static_assert(NCH * 256 == kMDeltaBN * CPR, "tile chunks per thread");
+  uint4 kpre[NCH], vpre[NCH];
+  auto gload = [&](int64_t j0) {
+    const int nv = int(min<int64_t>(kMDeltaBN, t1 - j0));
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = tid + 256 * c, row = e / CPR, ch = e % CPR;
+      kpre[c] = make_uint4(0, 0, 0, 0);
+      vpre[c] = kpre[c];
+      if (row < nv) {
+        const int64_t off = (j0 + row) * tok_stride + ch * 8;
+        kpre[c] = *reinterpret_cast<const uint4*>(kg + off);
+        vpre[c] = *reinterpret_cast<const uint4*>(vg + off);
+      }
+    }
+  };
+  if (t0 < t1) gload(t0);
   for (int64_t j0 = t0; j0 < t1; j0 += kMDeltaBN) {
     const int nv = int(min<int64_t>(kMDeltaBN, t1 - j0));
     __syncthreads();
-    for (int e = tid; e < kMDeltaBN * CPR; e += 256) {
-      const int row = e / CPR, ch = e % CPR;
-      uint4 ku = make_uint4(0, 0, 0, 0), vu = ku;
-      if (row < nv) {
-        const int64_t off = (j0 + row) * tok_stride + ch * 8;
-        ku = *reinterpret_cast<const uint4*>(kg + off);
-        vu = *reinterpret_cast<const uint4*>(vg + off);
-      }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e = tid + 256 * c, row = e / CPR, ch = e % CPR;
       const int at = row * ROWB + ((ch ^ dswz<D>(row)) * 16);
-      *reinterpret_cast<uint4*>(kt + at) = ku;
-      *reinterpret_cast<uint4*>(vt + at) = vu;
+      *reinterpret_cast<uint4*>(kt + at) = kpre[c];
+      *reinterpret_cast<uint4*>(vt + at) = vpre[c];
     }
     __syncthreads();
+    if (j0 + kMDeltaBN < t1) gload(j0 + kMDeltaBN);
 #pragma unroll
     for (int kk = 0; kk < kMDeltaBN / 16; ++kk) {
       if (16 * kk >= nv) break;
