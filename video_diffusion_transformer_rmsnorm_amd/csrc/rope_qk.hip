@@ -9,8 +9,8 @@
 // Design (HBM-bound, one pass): a workgroup owns a few consecutive tokens.
 // It first computes cos/sin for each (token, pair) once -- the angle is
 // formed and reduced modulo 2*pi in float64 so large temporal offsets keep
-// float32 accuracy -- into LDS, and every q and k head of those tokens
-// reuses them.  Each lane then owns 8 channels (one 16-byte bf16 vector) of
+// float32 accuracy, then its sine and cosine are taken in float32 -- into
+// LDS, and every q and k head of those tokens reuses them.  Each lane then owns 8 channels (one 16-byte bf16 vector) of
 // one head row; the row's sum of squares is reduced across the D/8 lanes of
 // the row with cross-lane shuffles.  Loads and stores are 16-byte vectors
 // over contiguous memory, so each token's q (and k) block streams through
@@ -56,9 +56,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
     double ang = double(pos) * omega;
     const double two_pi = 6.283185307179586476925286766559;
     ang -= two_pi * rint(ang / two_pi);
-    double sn, cn;
-    sincos(ang, &sn, &cn);
-    cs[tl * P + pr] = make_float2(float(cn), float(sn));
+    // the reduced angle lies in [-pi, pi]: float32 sine and cosine suffice
+    float sn, cn;
+    sincosf(float(ang), &sn, &cn);
+    cs[tl * P + pr] = make_float2(cn, sn);
   }
   __syncthreads();
 
@@ -68,10 +69,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   const int tasks = ntok * rows_per_tok * TPR;
   const float inv_d = 1.0f / float(D);
 
+  // row index -> (token, row) without an integer division: rt < 2^16, so
+  // the float quotient, nudged by half a step, truncates exactly
+  const float inv_rpt = 1.0f / float(rows_per_tok);
   for (int t = threadIdx.x; t < tasks; t += kRopeThreads) {
     const int c = t % TPR;
     const int rt = t / TPR;
-    const int tl = rt / rows_per_tok;
+    const int tl = int((float(rt) + 0.5f) * inv_rpt);
     const int r = rt - tl * rows_per_tok;
     const int64_t row = row0 + tl;
     const bool is_q = r < rows_q;

@@ -76,6 +76,10 @@ inline CheckResult check_rope(const void* q_in, const void* k_in, const void* q_
   if (!(g->theta > 1.0f)) return CheckResult::bad("theta must be > 1");
   if (!(eps >= 0.0f)) return CheckResult::bad("eps must be >= 0");
   if (token0 < 0) return CheckResult::bad("token0 must be >= 0");
+  // one workgroup holds a token's q and k rows: at most 2048 16-byte pieces
+  // ((n_heads + n_kv_heads) * head_dim / 8), i.e. 128 heads of dim 128
+  if ((int64_t(q_in ? Hq : 0) + (k_in ? Hk : 0)) * (D / 8) > 2048)
+    return CheckResult::unsup("too many heads per token for the rotary kernel (n_heads + n_kv_heads <= 16384 / head_dim)");
   const int64_t cells = int64_t(g->T) * g->H * g->W;
   if (token0 + L > cells) return CheckResult::bad("token0 + L exceeds the T*H*W grid");
   for (const void* p : {q_in, k_in, q_out, k_out})
