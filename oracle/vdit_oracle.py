@@ -15,6 +15,8 @@ Sources (pages by title, with the passage each step follows):
     Transformers -- Sec. 3.2 "Base Architecture" (RMSNorm, GQA, 3D-RoPE applied
     separately to the temporal and spatial axes), Sec. 3.3 (rolling KV cache,
     the sliding-window attention pattern, processing order instead of masks),
+    Sec. 3.4 "Step 2: Temporal Refinement" (the same streaming with r_t
+    sub-frames per step and a window of r_t * W_frm sub-frames),
     Sec. 4 "Long Video Decoding" (RoPE positions relative to the window).
     It cites RoFormer for rotary embeddings and Zhang & Sennrich for RMSNorm;
     the rotation and the norm below are those papers' definitions.
@@ -34,7 +36,10 @@ frequency theta^(-j/P_a); tokens flattened t-major then h then w; RMSNorm per
 head with eps=1e-6 and unit gain by default; softmax scale 1/sqrt(D) by
 default; natural-log LSE with -inf for an empty key set; phi = elu + 1 applied
 to the post-norm, post-rotation q and k without the softmax scale; the
-hybrid's stabiliser c_t cancels (joint normalisation of both terms).
+hybrid's stabiliser c_t cancels (joint normalisation of both terms); KV-norm
+is a per-head RMSNorm of keys and values with queries left un-normalised; a
+temporal-refinement step holds the r_t sub-frames of one latent frame, which
+take consecutive window-relative temporal positions.
 """
 from __future__ import annotations
 
@@ -129,12 +134,18 @@ def rope_rotate(x: np.ndarray, alpha: np.ndarray) -> np.ndarray:
 
 def rope_qk(q: np.ndarray, k: np.ndarray, grid, pairs, theta: float = 10000.0,
             token0: int = 0, t_offset: int = 0, eps: float = 1e-6, norm: bool = True,
-            q_gain=None, k_gain=None):
-    """Per-head RMSNorm of q and k (not v), then 3D-RoPE at each token's grid position."""
+            q_gain=None, k_gain=None, q_norm: Optional[bool] = None):
+    """Per-head RMSNorm of q and k (not v), then 3D-RoPE at each token's grid position.
+
+    q_norm=False leaves q un-normalised while k still is: the query side of
+    FlashDecoder's KV-norm (Sec. 3.2 "Base Architecture" normalises keys and
+    values inside attention, not queries).  q_norm=None follows `norm`.
+    """
     L = q.shape[1]
     t, h, w = grid_positions(L, grid, token0, t_offset)
     alpha = rope_angles(t, h, w, pairs, theta)
-    qn = rmsnorm(q, eps, q_gain) if norm else np.asarray(q, np.float64)
+    q_norm = norm if q_norm is None else q_norm
+    qn = rmsnorm(q, eps, q_gain) if q_norm else np.asarray(q, np.float64)
     kn = rmsnorm(k, eps, k_gain) if norm else np.asarray(k, np.float64)
     return rope_rotate(qn, alpha), rope_rotate(kn, alpha)
 
@@ -247,25 +258,38 @@ def rolling_window(f: int, n_slots: int) -> range:
 
 def rolling_frame(q_frames, k_frames, v_frames, f: int, n_slots: int, frame_grid,
                   pairs, theta: float = 10000.0, eps: float = 1e-6, norm: bool = True,
-                  scale: Optional[float] = None):
-    """Output of frame f of a frame-by-frame stream with a rolling KV window.
+                  scale: Optional[float] = None, kv_norm: bool = False):
+    """Output of step f of a step-by-step stream with a rolling KV window.
 
-    Inputs are the raw (pre-norm, pre-rotation) per-frame tensors
-    [F, L_frm, H, D].  Every frame u in the window is normalised and rotated
-    with its temporal position taken relative to the window start, t = u - f0
-    (FlashDecoder Sec. 4 "Long Video Decoding"), and (h, w) from the frame's
-    own H x W grid.  q_f attends to the concatenated window with no mask.
-    Returns (o [1, L_frm, H, D], lse [1, H, L_frm]).
+    Inputs are the raw (pre-norm, pre-rotation) per-step tensors
+    [F, L_step, H, D]; a step covers the grid frame_grid = (T_step, H, W),
+    T_step temporal positions of H x W tokens each.  T_step = 1 is
+    FlashDecoder's frame-by-frame decode (Sec. 3.3); T_step = r_t is its
+    temporal refinement (Sec. 3.4, Step 2), where one step carries the r_t
+    upsampled sub-frames of a latent frame and the window of n_slots steps
+    spans r_t * n_slots sub-frames.  Every step u in the window is normalised
+    and rotated with temporal positions relative to the window start,
+    t = T_step * (u - f0) + s for its sub-frame s (FlashDecoder Sec. 4
+    "Long Video Decoding"), and (h, w) from the step's own grid.  q_f
+    attends to the concatenated window with no mask.
+
+    kv_norm=True is FlashDecoder's KV-norm (Sec. 3.2): per-head RMSNorm of
+    keys (before rotation) and values; queries are rotated only.  Otherwise
+    q and k are normalised when `norm` is set and v is left as is.
+    Returns (o [1, L_step, H, D], lse [1, H, L_step]).
     """
     win = list(rolling_window(f, n_slots))
     f0 = win[0]
+    t_step = int(frame_grid[0])
     ks, vs = [], []
     qf = None
     for u in win:
         qu, ku = rope_qk(q_frames[u][None], k_frames[u][None], frame_grid, pairs, theta,
-                         token0=0, t_offset=u - f0, eps=eps, norm=norm)
+                         token0=0, t_offset=t_step * (u - f0), eps=eps, norm=norm or kv_norm,
+                         q_norm=False if kv_norm else None)
         ks.append(ku)
-        vs.append(np.asarray(v_frames[u][None], np.float64))
+        vu = np.asarray(v_frames[u][None], np.float64)
+        vs.append(rmsnorm(vu, eps) if kv_norm else vu)
         if u == f:
             qf = qu
     K = np.concatenate(ks, axis=1)

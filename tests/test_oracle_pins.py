@@ -361,6 +361,87 @@ def test_rolling_degenerate_windows():
         assert np.allclose(got, want, atol=1e-12)
 
 
+def _rms_rows(x, eps=1e-6):
+    # RMSNorm written out from its definition: x / sqrt(mean over the head dim of x^2 + eps)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3])
+def test_rolling_kv_norm_gqa_equals_masked_brute_force(W):
+    # FlashDecoder Sec. 3.2: GQA and KV-norm (keys and values normalised inside
+    # attention, queries not); Sec. 3.3: the window as a frame mask.  Expected
+    # values: q rotated without a norm, k normalised then rotated, v normalised,
+    # KV heads repeated per query group by hand, one masked softmax over all frames.
+    F, grid, Hq, Hk, D, pairs = 4, (1, 2, 3), 6, 2, 16, (2, 3, 3)
+    L = 6
+    r = RNG(40 + W)
+    qf = 3.0 * r.standard_normal((F, L, Hq, D)); kf = 2.0 * r.standard_normal((F, L, Hk, D))
+    vf = 5.0 * r.standard_normal((F, L, Hk, D))
+    for f in range(F):
+        f0 = max(0, f - W + 1)
+        qs, ks = [], []
+        for u in range(F):
+            a, _ = O.rope_qk(qf[u][None], qf[u][None], grid, pairs, t_offset=u - f0, norm=False)
+            _, b = O.rope_qk(kf[u][None], _rms_rows(kf[u][None]), grid, pairs, t_offset=u - f0, norm=False)
+            qs.append(a); ks.append(b)
+        K = np.repeat(np.concatenate(ks, axis=1), Hq // Hk, axis=2)
+        Vv = np.repeat(np.concatenate([_rms_rows(vf[u][None]) for u in range(F)], axis=1), Hq // Hk, axis=2)
+        frame_of_key = np.repeat(np.arange(F), L)
+        allowed = (frame_of_key >= f0) & (frame_of_key <= f)
+        mask = np.where(allowed, 0.0, -np.inf)[None, None, None, :].repeat(L, axis=2)
+        want = sdpa64(qs[f], K, Vv, mask=mask)
+        got, _ = O.rolling_frame(qf, kf, vf, f, W, grid, pairs, kv_norm=True)
+        assert np.allclose(got, want, atol=1e-12), (W, f)
+
+
+def test_rolling_kv_norm_scale_behaviour():
+    # With KV-norm, scaling a frame's keys or values by a positive factor leaves
+    # the output unchanged (up to eps); scaling the queries sharpens the softmax
+    # and changes it.  A slip that normalises q, or skips v, fails here.
+    F, grid, H, D, pairs, W, f = 3, (1, 2, 2), 2, 16, (3, 3, 2), 2, 2
+    r = RNG(45)
+    qf = r.standard_normal((F, 4, H, D)); kf = r.standard_normal((F, 4, H, D))
+    vf = r.standard_normal((F, 4, H, D))
+    base, _ = O.rolling_frame(qf, kf, vf, f, W, grid, pairs, kv_norm=True, eps=0.0)
+    k2 = kf.copy(); k2[1] *= 7.0
+    v2 = vf.copy(); v2[2] *= 0.25
+    got_k, _ = O.rolling_frame(qf, k2, vf, f, W, grid, pairs, kv_norm=True, eps=0.0)
+    got_v, _ = O.rolling_frame(qf, kf, v2, f, W, grid, pairs, kv_norm=True, eps=0.0)
+    assert np.allclose(got_k, base, atol=1e-13) and np.allclose(got_v, base, atol=1e-13)
+    q2 = qf.copy(); q2[f] *= 3.0
+    got_q, _ = O.rolling_frame(q2, kf, vf, f, W, grid, pairs, kv_norm=True, eps=0.0)
+    assert np.abs(got_q - base).max() > 1e-3
+    # every output row of a KV-normed window has RMS over D at most 1 (a convex
+    # combination of unit-RMS value rows)
+    rms = np.sqrt((base * base).mean(axis=-1))
+    assert (rms <= 1.0 + 1e-12).all()
+
+
+@pytest.mark.parametrize("W", [1, 2])
+def test_rolling_steps_of_subframes_equal_global_grid(W):
+    # FlashDecoder Sec. 3.4, Step 2: a refinement step carries r_t sub-frames of
+    # one latent frame and the window spans r_t * W sub-frames.  Expected values:
+    # rotate every token once at its absolute position on the global grid
+    # (r_t * F sub-frames), then a masked softmax admitting the keys of steps
+    # f0..f.  RoPE's relative invariance makes the window-relative positions of
+    # the oracle give the same scores.
+    F, rt, Hh, Ww, H, D, pairs = 4, 3, 2, 2, 2, 16, (3, 3, 2)
+    Ls = rt * Hh * Ww
+    r = RNG(50 + W)
+    qf = r.standard_normal((F, Ls, H, D)); kf = r.standard_normal((F, Ls, H, D))
+    vf = r.standard_normal((F, Ls, H, D))
+    qa, ka = O.rope_qk(qf.reshape(1, F * Ls, H, D), kf.reshape(1, F * Ls, H, D), (rt * F, Hh, Ww), pairs)
+    Vv = vf.reshape(1, F * Ls, H, D)
+    step_of_key = np.repeat(np.arange(F), Ls)
+    for f in range(F):
+        f0 = max(0, f - W + 1)
+        allowed = (step_of_key >= f0) & (step_of_key <= f)
+        mask = np.where(allowed, 0.0, -np.inf)[None, None, None, :].repeat(Ls, axis=2)
+        want = sdpa64(qa[:, f * Ls:(f + 1) * Ls], ka, Vv, mask=mask)
+        got, _ = O.rolling_frame(qf, kf, vf, f, W, (rt, Hh, Ww), pairs)
+        assert np.allclose(got, want, atol=1e-12), (W, f)
+
+
 # ---------------------------------------------------------------- hybrid --
 
 def test_phi_is_elu_plus_one():
@@ -486,3 +567,11 @@ def test_workload_shapes_and_flop_counts():
     assert w4.tokens == 2040 and sum(w4.pairs) * 2 == w4.head_dim
     w5 = WL.WORKLOADS[5]
     assert w5.tokens == 12090 and w5.chunk_tokens == 3 * 15 * 26
+    # FlashDecoder-XL (Table 5: width 1536, 24 heads, 3 KV groups; W_frm = 2),
+    # 720p latents at spatial compression 16: 45 x 80 tokens per frame
+    w6, w7 = WL.WORKLOADS[6], WL.WORKLOADS[7]
+    assert w6.tokens == 3600 and w6.heads * w6.head_dim == 1536 and w6.kv_heads == 3 and w6.n_slots == 2
+    assert sum(w6.pairs) * 2 == w6.head_dim and w6.kv_norm and w7.kv_norm
+    assert abs(WL.flops_full(3600, 7200, 24, 64) / 1e9 - 159.25248) < 1e-5
+    assert w7.grid == (4, 45, 80) and w7.tokens == 4 * 3600 and w7.n_slots == 2
+    assert abs(WL.flops_full(14400, 28800, 24, 64) / 1e12 - 2.5480396) < 1e-6

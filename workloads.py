@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for 3D-RoPE video-DiT attention.
 
-This module only draws and stores numbers: it holds the five workload shapes
+This module only draws and stores numbers: it holds the workload shapes
 and the seeded generators that both the oracle tests and the HIP path use.
 It contains none of the method's arithmetic (no norm, rotation, softmax or
 state update), so importing it couples neither side to the other.
@@ -64,6 +64,8 @@ class Workload:
     n_frames: int = 0
     # hybrid: tokens per chunk
     chunk_tokens: int = 0
+    # rolling: per-head RMSNorm of keys and values, queries rotated only
+    kv_norm: bool = False
 
     @property
     def tokens(self) -> int:
@@ -84,6 +86,13 @@ WORKLOADS = {
                 n_slots=5, n_frames=64),
     5: Workload(5, "hybrid_chunk_12090", "hybrid", "bf16", (31, 15, 26), 24, 24, 128, (22, 21, 21),
                 chunk_tokens=1170),
+    # FlashDecoder-XL decode at 720p: 45 x 80 latent tokens per frame, 24 query
+    # heads in 3 KV groups, head dim 1536 / 24 = 64, window of 2 frames, KV-norm
+    6: Workload(6, "flashdecoder_xl_rolling_720p_3600x2", "rolling", "bf16", (1, 45, 80), 24, 3, 64,
+                (12, 10, 10), n_slots=2, n_frames=16, kv_norm=True),
+    # its temporal refinement: steps of r_t = 4 sub-frames, window 2 steps = 8 sub-frames
+    7: Workload(7, "flashdecoder_xl_refine_720p_4x3600x2", "rolling", "bf16", (4, 45, 80), 24, 3, 64,
+                (12, 10, 10), n_slots=2, n_frames=6, kv_norm=True),
 }
 
 
@@ -142,7 +151,8 @@ def draw_qkv(shape_q, shape_k, seed: int, dtype: str, structured_grid: Optional[
 def workload_inputs(w: Workload, seed: Optional[int] = None, structured: bool = False):
     """Raw (pre-norm, pre-rotation) q, k, v for a workload, over its whole grid.
 
-    Rolling workloads draw [n_frames, L_frame, H, D] per tensor, frame-major.
+    Rolling workloads draw [n_frames, L_step, H, D] per tensor, step-major
+    (L_step = tokens of the per-step grid).
     """
     seed = w.seed if seed is None else seed
     if w.mode == "rolling":
