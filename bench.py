@@ -186,12 +186,23 @@ def bench_other(args):
             kc[:, f].copy_(kd[f:f + 1]); vc[:, f].copy_(vd[f:f + 1])
         flops = WL.flops_full(w.tokens, w.tokens * w.n_slots, w.heads, w.head_dim)
         frame = [w.n_slots]
+        t_step = w.grid[0]
+        q_norm = False if w.kv_norm else None
 
         def step():
+            # one decode step: rotate q (KV-norm: without its norm), normalise and
+            # rotate k straight into the cache slot, values into their slot
+            # (normalised under KV-norm), then attend over the window
             f = frame[0]
-            V.vdit_rope_qk(qd[f % w.n_frames:f % w.n_frames + 1], None, grid, t_offset=f)
-            V.vdit_attn_fwd(qd[f % w.n_frames:f % w.n_frames + 1], kd[f % w.n_frames:f % w.n_frames + 1],
-                            vd[f % w.n_frames:f % w.n_frames + 1], mode="rolling", k_cache=kc, v_cache=vc, frame=f)
+            i, slot = f % w.n_frames, f % w.n_slots
+            qi = qd[i:i + 1]
+            V.vdit_rope_qk(qi, kd[i:i + 1], grid, q_out=qi, k_out=kc[:, slot], t_offset=t_step * f,
+                           q_norm=q_norm)
+            if w.kv_norm:
+                V.vdit_rms_norm(vd[i:i + 1], out=vc[:, slot])
+            else:
+                vc[:, slot].copy_(vd[i:i + 1])
+            V.vdit_attn_fwd(qi, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
             frame[0] += 1
     elif w.mode == "hybrid":
         s = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device=dev)
@@ -221,7 +232,9 @@ def bench_other(args):
     return {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-            "data": "synthetic", "config": {"workload": w.name, "mode": w.mode, "reference_only": True}}
+            "data": "synthetic", "config": {"workload": w.name, "mode": w.mode, "tokens": w.tokens,
+                                            "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                                            "kv_norm": w.kv_norm, "reference_only": True}}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):

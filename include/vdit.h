@@ -65,7 +65,9 @@ typedef struct {
 } vdit_grid;
 
 /* vdit_rope_qk flags */
-#define VDIT_ROPE_NO_NORM 1u /* skip the RMSNorm, rotate only */
+#define VDIT_ROPE_NO_NORM 1u   /* skip the RMSNorm of q and k, rotate only */
+#define VDIT_ROPE_NO_Q_NORM 2u /* skip it for q only: k is normalised, q rotated
+                                  only (KV-norm; normalise v with vdit_rms_norm) */
 
 /*
  * vdit_rope_qk -- fused per-head RMSNorm + 3D-RoPE of queries and keys.
@@ -73,7 +75,7 @@ typedef struct {
  * For every token i of the slice, every head and both q and k:
  *   y = x / sqrt(mean_d(x_d^2) + eps) * gain        (RMSNorm over head_dim,
  *       Zhang & Sennrich, cited by FlashDecoder Sec. 3.2; skipped with
- *       VDIT_ROPE_NO_NORM)
+ *       VDIT_ROPE_NO_NORM, and for q alone with VDIT_ROPE_NO_Q_NORM)
  *   then each pair (y_2p, y_2p+1) is rotated by angle alpha = pos * omega_p:
  *   (y0 cos a - y1 sin a, y0 sin a + y1 cos a).
  * Token i has grid index n = token0 + i, so t = n / (H W) + t_offset,
@@ -94,6 +96,24 @@ vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* 
                          int32_t head_dim, vdit_dtype dtype, const vdit_grid* grid,
                          int64_t token0, int64_t t_offset, const float* q_gain,
                          const float* k_gain, float eps, uint32_t flags, hipStream_t stream);
+
+/*
+ * vdit_rms_norm -- per-head RMSNorm without rotation, for the values of
+ * KV-norm attention (FlashDecoder Sec. 3.2 "Base Architecture" normalises
+ * keys and values inside attention; the keys take the norm in vdit_rope_qk,
+ * before their rotation, and the queries skip it with VDIT_ROPE_NO_Q_NORM).
+ *
+ * For every token and head: y = x / sqrt(mean_d(x_d^2) + eps) * gain.
+ * x_in, x_out: [B, L, n_heads, head_dim] of dtype; x_out may equal x_in (in
+ * place), partial overlap is not allowed.  A rolling-cache slot of a B = 1
+ * cache is a valid x_out, so a decode step can normalise its values straight
+ * into the cache.  gain: [head_dim] float32 or NULL (gain 1), 16-byte
+ * aligned.  eps >= 0; head_dim in {64, 128}.  With B * L = 0 nothing is
+ * done and x_in, x_out may be NULL.
+ */
+vdit_status vdit_rms_norm(const void* x_in, void* x_out, int32_t B, int64_t L, int32_t n_heads,
+                          int32_t head_dim, vdit_dtype dtype, const float* gain, float eps,
+                          hipStream_t stream);
 
 typedef enum {
   VDIT_ATTN_FULL = 0,

@@ -33,6 +33,16 @@ int main() {
   EXPECT(check_rope(P(0x1000), nullptr, nullptr, nullptr, 1, 10, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "q_out missing");
   EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 10, 12, 12, 128, 0, &g, 0, -1.f).code == Check::invalid, "negative eps");
 
+  // per-head RMSNorm (values of KV-norm attention)
+  EXPECT(bool(check_rms_norm(P(0x1000), P(0x1000), 1, 3600, 3, 64, 0, nullptr, 1e-6f)), "rms norm in place ok");
+  EXPECT(bool(check_rms_norm(P(0x1000), P(1ull << 24), 1, 3600, 3, 64, 0, nullptr, 1e-6f)), "rms norm out of place ok");
+  EXPECT(check_rms_norm(P(0x1000), P(0x1010), 1, 10, 3, 64, 0, nullptr, 1e-6f).code == Check::invalid, "rms norm partial overlap");
+  EXPECT(check_rms_norm(P(0x1000), P(0x1000), 1, 10, 3, 256, 0, nullptr, 1e-6f).code == Check::unsupported, "rms norm head_dim");
+  EXPECT(check_rms_norm(P(0x1000), nullptr, 1, 10, 3, 64, 0, nullptr, 1e-6f).code == Check::invalid, "rms norm out missing");
+  EXPECT(bool(check_rms_norm(nullptr, nullptr, 1, 0, 3, 64, 0, nullptr, 1e-6f)), "rms norm empty with NULL");
+  EXPECT(check_rms_norm(P(0x1000), P(0x1000), 1, 10, 3, 64, 0, (const float*)P(0x2004), 1e-6f).code == Check::invalid, "rms norm gain alignment");
+  EXPECT(check_rms_norm(P(0x1000), P(0x1000), 1, 10, 3, 64, 2, nullptr, 1e-6f).code == Check::invalid, "rms norm dtype");
+
   AttnArgs a{};
   a.mode = 0; a.dtype = 0; a.B = 1; a.n_heads = 12; a.n_kv_heads = 12; a.head_dim = 128;
   a.Lq = 100; a.Lkv = 100; a.q = P(1ull << 28); a.k = P(2ull << 28); a.v = P(3ull << 28); a.o = P(4ull << 28);

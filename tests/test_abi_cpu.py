@@ -105,6 +105,22 @@ def test_rope_validation_errors_return_before_any_gpu_call(lib):
     assert st == V.VDIT_ERR_INVALID_ARG and "flags" in msg
 
 
+def test_rms_norm_validation_errors_return_before_any_gpu_call(lib):
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st, msg = _status(lib, lib.vdit_rms_norm, fake, fake, 1, 100, 3, 96, 0, None, 1e-6, None)
+    assert st == V.VDIT_ERR_UNSUPPORTED and "head_dim" in msg
+    st, msg = _status(lib, lib.vdit_rms_norm, fake, None, 1, 100, 3, 64, 0, None, 1e-6, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "x_out" in msg
+    st, msg = _status(lib, lib.vdit_rms_norm, fake, fake + 64, 1, 100, 3, 64, 0, None, 1e-6, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "overlap" in msg
+    st, msg = _status(lib, lib.vdit_rms_norm, fake, fake, 1, 100, 3, 64, 0, fake + 4, 1e-6, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = _status(lib, lib.vdit_rms_norm, fake, fake, 1, 100, 0, 64, 0, None, 1e-6, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "n_heads" in msg
+    st, msg = _status(lib, lib.vdit_rms_norm, fake, fake, 1, 100, 3, 64, 0, None, -1.0, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "eps" in msg
+
+
 def test_attn_validation_errors(lib):
     a = V.VditAttnArgs()
     a.mode, a.dtype, a.B, a.n_heads, a.n_kv_heads, a.head_dim = 0, 0, 1, 12, 5, 128

@@ -65,6 +65,45 @@ def test_rope_inplace_gain_nonorm_large_offset(dtype):
     check(qo, wq2, dtype, "q no-norm")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_rms_norm_values_ragged_inplace_gain(dtype, D):
+    # per-head RMSNorm alone (the values of KV-norm attention): out of place,
+    # in place, with a gain; row count not a multiple of the block's rows
+    B, L, H = 2, 333, 3
+    log(f"rms norm {dtype} D={D} B={B} L={L} H={H}")
+    vals = raw((B, L, H, D), 31, dtype).values
+    vals[0, 5] *= 40.0  # a few large rows, rounded again to the element type below
+    v32 = vals.astype(np.float32)
+    if dtype == "bf16":
+        bits = WL.f32_to_bf16_bits(v32)
+        x = WL.Tensor(WL.bf16_bits_to_f64(bits), bits, dtype)
+    else:
+        x = WL.Tensor(v32.astype(np.float64), None, dtype)
+    g = (1.0 + 0.1 * np.random.default_rng(32).standard_normal(D)).astype(np.float32)
+    xd = to_dev(x)
+    out = V.vdit_rms_norm(xd)
+    torch.cuda.synchronize()
+    check(out, O.rmsnorm(x.values), dtype, "rms norm")
+    V.vdit_rms_norm(xd, out=xd, gain=torch.from_numpy(g).cuda(), eps=1e-5)
+    torch.cuda.synchronize()
+    check(xd, O.rmsnorm(x.values, 1e-5, g), dtype, "rms norm in place with gain")
+    empty = torch.empty((1, 0, H, D), dtype=xd.dtype, device="cuda")
+    V.vdit_rms_norm(empty, out=empty)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_without_query_norm(dtype):
+    # KV-norm: keys normalised then rotated, queries rotated only
+    D, pairs, grid = 64, (12, 10, 10), (4, 9, 10)
+    L = 360
+    log(f"rope with k norm only {dtype}")
+    q = raw((1, L, 8, D), 33, dtype); k = raw((1, L, 1, D), 34, dtype)
+    qo, ko = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*grid, pairs), t_offset=7, q_norm=False)
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs, t_offset=7, q_norm=False)
+    check(qo, wq, dtype, "q rotated only"); check(ko, wk, dtype, "k normalised and rotated")
+
+
 def test_rope_full_size_wan13b():
     w = WL.WORKLOADS[2]
     log("rope full size 32760 x 12 x 128 bf16")
@@ -305,27 +344,37 @@ def test_lse_merge(din, dout):
 
 # ---------------------------------------------------------------- rolling --
 
-def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=False):
-    """Stream frames through rope (absolute t) + ROLLING attention; return outputs per frame."""
+def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=False, kv_norm=False):
+    """Stream steps through rope (absolute t) + ROLLING attention; return outputs per step.
+
+    A step covers frame_grid = (T_step, H, W); step f's sub-frames take the
+    absolute temporal positions T_step * f + s.  With kv_norm the keys are
+    normalised and rotated, the values normalised (vdit_rms_norm) and the
+    queries rotated only."""
     F, L, H, D = qf.values.shape
     Hk = kf.values.shape[2]
+    T = frame_grid[0]
     dt = torch.bfloat16 if qf.dtype == "bf16" else torch.float32
     kc = torch.zeros((1, n_slots, L, Hk, D), dtype=dt, device="cuda")
     vc = torch.zeros_like(kc)
-    g = V.make_grid(1, frame_grid[1], frame_grid[2], pairs)
+    g = V.make_grid(*frame_grid, pairs)
     qdev, kdev, vdev = to_dev(qf), to_dev(kf), to_dev(vf)
+    qn = False if kv_norm else None
     outs = {}
     for f in range(frames):
-        qr, _ = V.vdit_rope_qk(qdev[f:f + 1], None, g, t_offset=f)
+        qr, _ = V.vdit_rope_qk(qdev[f:f + 1], None, g, t_offset=T * f, q_norm=qn)
         if prefill_slot:
             slot = f % n_slots
-            V.vdit_rope_qk(None, kdev[f:f + 1], g, k_out=kc[:, slot], t_offset=f)
-            vc[:, slot].copy_(vdev[f:f + 1])
+            V.vdit_rope_qk(None, kdev[f:f + 1], g, k_out=kc[:, slot], t_offset=T * f)
+            if kv_norm:
+                V.vdit_rms_norm(vdev[f:f + 1], out=vc[:, slot])
+            else:
+                vc[:, slot].copy_(vdev[f:f + 1])
             o, lse = V.vdit_attn_fwd(qr, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
         else:
-            _, kr = V.vdit_rope_qk(None, kdev[f:f + 1], g, t_offset=f)
-            o, lse = V.vdit_attn_fwd(qr, kr, vdev[f:f + 1].contiguous(), mode="rolling", k_cache=kc,
-                                     v_cache=vc, frame=f)
+            _, kr = V.vdit_rope_qk(None, kdev[f:f + 1], g, t_offset=T * f)
+            vr = V.vdit_rms_norm(vdev[f:f + 1]) if kv_norm else vdev[f:f + 1].contiguous()
+            o, lse = V.vdit_attn_fwd(qr, kr, vr, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
         outs[f] = (o, lse)
     torch.cuda.synchronize()
     return outs
@@ -345,6 +394,26 @@ def test_rolling_small_stream(dtype, prefill):
         check_lse(outs[f][1], wl, dtype, f"LSE frame {f}")
 
 
+@pytest.mark.parametrize("dtype,D,frame_grid,prefill", [
+    ("bf16", 64, (1, 6, 13), True), ("bf16", 64, (2, 5, 9), False), ("bf16", 128, (2, 5, 9), True),
+    ("f32", 64, (2, 5, 9), True)])
+def test_rolling_kv_norm_gqa_stream(dtype, D, frame_grid, prefill):
+    # FlashDecoder-style decode: 8 query heads per KV head, KV-norm, window of
+    # 2 steps; frame_grid[0] = 2 streams steps of two sub-frames each
+    pairs = (12, 10, 10) if D == 64 else (22, 21, 21)
+    Hq, Hk, W, F = 8, 1, 2, 5
+    L = frame_grid[0] * frame_grid[1] * frame_grid[2]
+    log(f"rolling KV-norm GQA {dtype} D={D} step grid {frame_grid} prefill={prefill} W={W} steps={F}")
+    rng = np.random.default_rng(92)
+    qf = WL.draw((F, L, Hq, D), rng, dtype); kf = WL.draw((F, L, Hk, D), rng, dtype)
+    vf = WL.draw((F, L, Hk, D), rng, dtype)
+    outs = _rolling_run(qf, kf, vf, frame_grid, pairs, W, F, prefill, kv_norm=True)
+    for f in range(F):
+        wo, wl = O.rolling_frame(qf.values, kf.values, vf.values, f, W, frame_grid, pairs, kv_norm=True)
+        check(outs[f][0], wo, dtype, f"O step {f}")
+        check_lse(outs[f][1], wl, dtype, f"LSE step {f}")
+
+
 @pytest.mark.slow
 def test_rolling_decode_shape_sampled():
     w = WL.WORKLOADS[4]
@@ -361,16 +430,39 @@ def test_rolling_decode_shape_sampled():
         check_lse(from_dev(outs[f][1])[:, :, rows], wl, "bf16", f"LSE frame {f} (sampled)")
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("number,steps,check_at", [(6, 4, (0, 1, 3)), (7, 3, (0, 2))])
+def test_flashdecoder_xl_rolling_sampled(number, steps, check_at):
+    # FlashDecoder-XL at 720p: 3600 tokens per frame, 24 query heads in 3 KV
+    # groups, head dim 64, KV-norm, window of 2; workload 7 is its temporal
+    # refinement (steps of 4 sub-frames = 14400 tokens, window of 8 sub-frames)
+    w = WL.WORKLOADS[number]
+    log(f"{w.name}: {w.tokens} tokens per step x {w.heads}/{w.kv_heads} heads x {w.head_dim}, "
+        f"{w.n_slots} slots, {steps} steps, sampled rows")
+    q, k, v = WL.workload_inputs(w)
+    sub = lambda t: WL.Tensor(t.values[:steps], None if t.bits is None else t.bits[:steps], t.dtype)
+    qf, kf, vf = sub(q), sub(k), sub(v)
+    del q, k, v
+    outs = _rolling_run(qf, kf, vf, w.grid, w.pairs, w.n_slots, steps, prefill_slot=True, kv_norm=w.kv_norm)
+    rows = WL.sample_rows(w.tokens, 96, seed=11)
+    for f in check_at:
+        wo, wl = _rolling_oracle_rows(qf, kf, vf, f, w, rows)
+        check(from_dev(outs[f][0])[:, rows], wo, "bf16", f"O step {f} (sampled)")
+        check_lse(from_dev(outs[f][1])[:, :, rows], wl, "bf16", f"LSE step {f} (sampled)")
+
+
 def _rolling_oracle_rows(qf, kf, vf, f, w, rows):
-    """oracle.rolling_frame restricted to a sample of query rows (window-relative t)."""
+    """oracle.rolling_frame restricted to a sample of query rows (window-relative t,
+    T_step temporal positions per step; KV-norm when the workload has it)."""
     win = list(O.rolling_window(f, w.n_slots))
-    f0 = win[0]
+    f0, T = win[0], w.grid[0]
     ks, vs = [], []
     for u in win:
-        _, ku = O.rope_qk(kf.values[u][None], kf.values[u][None], w.grid, w.pairs, t_offset=u - f0)
+        _, ku = O.rope_qk(kf.values[u][None], kf.values[u][None], w.grid, w.pairs, t_offset=T * (u - f0))
         ks.append(ku)
-        vs.append(vf.values[u][None])
-    qr, _ = O.rope_qk(qf.values[f][None], qf.values[f][None], w.grid, w.pairs, t_offset=f - f0)
+        vs.append(O.rmsnorm(vf.values[u][None]) if w.kv_norm else vf.values[u][None])
+    qr, _ = O.rope_qk(qf.values[f][None], qf.values[f][None], w.grid, w.pairs, t_offset=T * (f - f0),
+                      q_norm=False if w.kv_norm else None)
     return O.attention(qr[:, rows], np.concatenate(ks, 1), np.concatenate(vs, 1))
 
 

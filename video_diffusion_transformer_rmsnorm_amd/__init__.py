@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(PKG_DIR, "libvdit.so")
 VDIT_OK, VDIT_ERR_INVALID_ARG, VDIT_ERR_UNSUPPORTED, VDIT_ERR_HIP = 0, 1, 2, 3
 VDIT_BF16, VDIT_F32 = 0, 1
 VDIT_ROPE_NO_NORM = 1
+VDIT_ROPE_NO_Q_NORM = 2
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
 ABI_VERSION = 1
 
 # Every symbol include/vdit.h declares.
-EXPORTS = ("vdit_rope_qk", "vdit_attn_fwd", "vdit_attn_workspace_bytes", "vdit_lse_merge",
-           "vdit_last_error", "vdit_abi_version")
+EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_workspace_bytes",
+           "vdit_lse_merge", "vdit_last_error", "vdit_abi_version")
 
 
 class VditError(RuntimeError):
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
     h.vdit_rope_qk.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, ctypes.POINTER(VditGrid),
                                i64, i64, vp, vp, f32, u32, vp]
     h.vdit_rope_qk.restype = ctypes.c_int
+    h.vdit_rms_norm.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, f32, vp]
+    h.vdit_rms_norm.restype = ctypes.c_int
     h.vdit_attn_fwd.argtypes = [ctypes.POINTER(VditAttnArgs), vp]
     h.vdit_attn_fwd.restype = ctypes.c_int
     h.vdit_attn_workspace_bytes.argtypes = [ctypes.POINTER(VditAttnArgs)]
@@ -124,11 +127,13 @@ def make_grid(T: int, H: int, W: int, pairs: Sequence[int], theta: float = 10000
 
 
 def vdit_rope_qk(q, k, grid: VditGrid, q_out=None, k_out=None, token0: int = 0, t_offset: int = 0,
-                 q_gain=None, k_gain=None, eps: float = 1e-6, norm: bool = True, stream=None):
+                 q_gain=None, k_gain=None, eps: float = 1e-6, norm: bool = True,
+                 q_norm: Optional[bool] = None, stream=None):
     """Fused per-head RMSNorm + 3D-RoPE of q [B,L,Hq,D] and k [B,L,Hk,D].
 
-    Outputs default to new tensors; pass q_out=q / k_out=k for in-place.
-    Returns (q_out, k_out)."""
+    norm=False rotates only; q_norm=False (with norm=True) normalises k but
+    not q, as KV-norm attention does.  Outputs default to new tensors; pass
+    q_out=q / k_out=k for in-place.  Returns (q_out, k_out)."""
     import torch
     ref = q if q is not None else k
     for t, n in ((q, "q"), (k, "k"), (q_out, "q_out"), (k_out, "k_out"), (q_gain, "q_gain"), (k_gain, "k_gain")):
@@ -141,10 +146,27 @@ def vdit_rope_qk(q, k, grid: VditGrid, q_out=None, k_out=None, token0: int = 0, 
     Hq = q.shape[2] if q is not None else 0
     Hk = k.shape[2] if k is not None else 0
     flags = 0 if norm else VDIT_ROPE_NO_NORM
+    if norm and q_norm is False:
+        flags |= VDIT_ROPE_NO_Q_NORM
     _check(lib().vdit_rope_qk(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), B, L, Hq, Hk, D,
                               _dtype_code(ref), ctypes.byref(grid), token0, t_offset,
                               _ptr(q_gain), _ptr(k_gain), eps, flags, _stream(stream)))
     return q_out, k_out
+
+
+def vdit_rms_norm(x, out=None, gain=None, eps: float = 1e-6, stream=None):
+    """Per-head RMSNorm of x [B,L,H,D] (the values of KV-norm attention).
+
+    out defaults to a new tensor; out=x normalises in place.  Returns out."""
+    import torch
+    for t, n in ((x, "x"), (out, "out"), (gain, "gain")):
+        _dev(t, n)
+    if out is None:
+        out = torch.empty_like(x)
+    B, L, H, D = x.shape
+    _check(lib().vdit_rms_norm(_ptr(x), _ptr(out), B, L, H, D, _dtype_code(x), _ptr(gain), eps,
+                               _stream(stream)))
+    return out
 
 
 def _attn_args(q, k, v, mode, o, lse, scale, n_kv_heads, Lkv) -> VditAttnArgs:
@@ -244,5 +266,5 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-__all__ = ["vdit_rope_qk", "vdit_attn_fwd", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
+__all__ = ["vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
            "VditGrid", "VditAttnArgs", "VditError", "lib", "EXPORTS", "LIB_PATH"]

@@ -158,7 +158,8 @@ vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* 
   if ((q_gain && (reinterpret_cast<uintptr_t>(q_gain) & 15)) ||
       (k_gain && (reinterpret_cast<uintptr_t>(k_gain) & 15)))
     return fail(VDIT_ERR_INVALID_ARG, "gain pointers must be 16-byte aligned");
-  if (flags & ~uint32_t(VDIT_ROPE_NO_NORM)) return fail(VDIT_ERR_INVALID_ARG, "unknown rope flags");
+  if (flags & ~uint32_t(VDIT_ROPE_NO_NORM | VDIT_ROPE_NO_Q_NORM))
+    return fail(VDIT_ERR_INVALID_ARG, "unknown rope flags");
   vdit::RopeLaunch p;
   p.q_in = q_in;
   p.k_in = k_in;
@@ -181,9 +182,26 @@ vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* 
   p.pairs_w = g->pairs_w;
   p.theta = g->theta;
   p.eps = eps;
-  p.norm = (flags & VDIT_ROPE_NO_NORM) ? 0 : 1;
+  p.norm_k = (flags & VDIT_ROPE_NO_NORM) ? 0 : 1;
+  p.norm_q = (flags & (VDIT_ROPE_NO_NORM | VDIT_ROPE_NO_Q_NORM)) ? 0 : 1;
   p.dtype = int32_t(dtype);
   return from_hip(vdit::launch_rope(p, stream), "vdit_rope_qk launch");
+}
+
+vdit_status vdit_rms_norm(const void* x_in, void* x_out, int32_t B, int64_t L, int32_t n_heads,
+                          int32_t head_dim, vdit_dtype dtype, const float* gain, float eps,
+                          hipStream_t stream) {
+  if (auto r = vdit::check_rms_norm(x_in, x_out, B, L, n_heads, head_dim, int(dtype), gain, eps); !r)
+    return from_check(r);
+  vdit::RmsNormLaunch p;
+  p.x_in = x_in;
+  p.x_out = x_out;
+  p.gain = gain;
+  p.rows = int64_t(B) * L * n_heads;
+  p.D = head_dim;
+  p.eps = eps;
+  p.dtype = int32_t(dtype);
+  return from_hip(vdit::launch_rms_norm(p, stream), "vdit_rms_norm launch");
 }
 
 size_t vdit_attn_workspace_bytes(const vdit_attn_args* args) {

@@ -50,6 +50,9 @@
 #ifndef VDIT_ATTN_SCHED
 #define VDIT_ATTN_SCHED 1
 #endif
+#ifndef VDIT_ATTN_BOUND_MIN_NW
+#define VDIT_ATTN_BOUND_MIN_NW 8  // smallest workgroup shape (wavefronts) with the bounded-score path
+#endif
 #ifndef VDIT_ATTN_NPB
 #define VDIT_ATTN_NPB 6  // exponential pairs (of 16) computed among the PV MFMAs
 #endif
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // (8-wavefront kernel only: the 4- and 2-wavefront kernels keep their
   // single loop, whose instruction schedule a second copy disturbs)
   bool fast = false;
-  if (NW == 8 && p.kbound != nullptr) {
+  if (NW >= VDIT_ATTN_BOUND_MIN_NW && p.kbound != nullptr) {
     // the partial maxima (at most 64): one per lane, then a wavefront max
     const float* kbp = p.kbound + ((chunk_id * p.B + b) * p.Hk + hk) * p.kbound_n;
     float kmax2 = lane < p.kbound_n ? kbp[lane] : 0.f;
@@ -735,7 +738,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     if (t < ntiles) iteration(t, std::integral_constant<int, 0>{});
   };
   if (ntiles > 0) {
-    if constexpr (NW == 8) {
+    if constexpr (NW >= VDIT_ATTN_BOUND_MIN_NW) {
       if (fast) main_loop(std::true_type{});
       else main_loop(std::false_type{});
     } else {
@@ -914,7 +917,9 @@ int attn_waves(const AttnLaunch& p) {
 }
 }  // namespace
 
-bool attn_uses_key_bound(const AttnLaunch& p) { return VDIT_ATTN_BIG_QB == 1 && attn_waves(p) == 8; }
+bool attn_uses_key_bound(const AttnLaunch& p) {
+  return VDIT_ATTN_BIG_QB == 1 && attn_waves(p) >= VDIT_ATTN_BOUND_MIN_NW;
+}
 
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
   // Workgroup shape by problem size: 256 queries (8 wavefronts) when its

@@ -1,10 +1,13 @@
-// rope_qk.hip -- fused per-head RMSNorm + channel-split 3D rotary embedding.
+// rope_qk.hip -- fused per-head RMSNorm + channel-split 3D rotary embedding,
+// and the per-head RMSNorm alone.
 //
 // What it computes (FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder
 // with Transformers, Sec. 3.2 "Base Architecture": RMSNorm, and 3D-RoPE
 // applied separately to the temporal and spatial axes): for every token and
 // head of q and k, y = x / sqrt(mean(x^2) + eps) * g, then each adjacent
-// channel pair is rotated by pos_axis * theta^(-j / P_axis).
+// channel pair is rotated by pos_axis * theta^(-j / P_axis).  The norm can be
+// left out for q alone (KV-norm, where the same section normalises keys and
+// values inside attention) or for both; rms_norm_kernel normalises the values.
 //
 // Design (HBM-bound, one pass): a workgroup owns a few consecutive tokens.
 // It first computes cos/sin for each (token, pair) once -- the angle is
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
       const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off + 4);
       x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     }
-    if (p.norm) {
+    if (is_q ? p.norm_q : p.norm_k) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
@@ -128,7 +131,68 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   }
 }
 
+// Per-head RMSNorm alone (the values of KV-norm attention): the same lane
+// layout as above, D/8 lanes per row, 16-byte loads and stores, in place safe.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kRopeThreads) void rms_norm_kernel(RmsNormLaunch p) {
+  constexpr int TPR = D / 8;
+  const int64_t tasks = p.rows * TPR;
+  const float inv_d = 1.0f / float(D);
+  // tasks and the block size are multiples of TPR, so the lanes of one row
+  // enter and leave the loop together and the shuffles stay inside the row
+  for (int64_t t = int64_t(blockIdx.x) * kRopeThreads + threadIdx.x; t < tasks;
+       t += int64_t(gridDim.x) * kRopeThreads) {
+    const int c = int(t % TPR);
+    const int64_t off = t * 8;
+    float x[8];
+    if constexpr (BF16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x_in) + off);
+      unpack8(u, x);
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p.x_in) + off);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p.x_in) + off + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) ss += __shfl_xor(ss, m, TPR);
+    const float rinv = 1.0f / sqrtf(fmaf(ss, inv_d, p.eps));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= rinv;
+    if (p.gain) {
+      const float4 ga = *reinterpret_cast<const float4*>(p.gain + c * 8);
+      const float4 gb = *reinterpret_cast<const float4*>(p.gain + c * 8 + 4);
+      x[0] *= ga.x; x[1] *= ga.y; x[2] *= ga.z; x[3] *= ga.w;
+      x[4] *= gb.x; x[5] *= gb.y; x[6] *= gb.z; x[7] *= gb.w;
+    }
+    if constexpr (BF16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.x_out) + off) = pack8(x);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.x_out) + off) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(static_cast<float*>(p.x_out) + off + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rms_norm(const RmsNormLaunch& p, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  const int64_t tasks = p.rows * (p.D / 8);
+  int64_t blocks = (tasks + kRopeThreads - 1) / kRopeThreads;
+  if (blocks > (int64_t(1) << 20)) blocks = int64_t(1) << 20;  // grid-stride beyond
+  dim3 grid(static_cast<unsigned>(blocks));
+  if (p.dtype == 0) {
+    if (p.D == 128) hipLaunchKernelGGL((rms_norm_kernel<128, true>), grid, dim3(kRopeThreads), 0, s, p);
+    else hipLaunchKernelGGL((rms_norm_kernel<64, true>), grid, dim3(kRopeThreads), 0, s, p);
+  } else {
+    if (p.D == 128) hipLaunchKernelGGL((rms_norm_kernel<128, false>), grid, dim3(kRopeThreads), 0, s, p);
+    else hipLaunchKernelGGL((rms_norm_kernel<64, false>), grid, dim3(kRopeThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(const RopeLaunch& p, hipStream_t s) {
   const int64_t rows = int64_t(p.B) * p.L;

@@ -96,6 +96,22 @@ inline CheckResult check_rope(const void* q_in, const void* k_in, const void* q_
   return CheckResult::good();
 }
 
+inline CheckResult check_rms_norm(const void* x_in, const void* x_out, int32_t B, int64_t L,
+                                  int32_t H, int32_t D, int dtype, const float* gain, float eps) {
+  if (auto r = check_dtype(dtype); !r) return r;
+  if (auto r = check_head_dim(D); !r) return r;
+  if (B < 0 || L < 0) return CheckResult::bad("B and L must be non-negative");
+  if (H <= 0) return CheckResult::bad("n_heads must be positive");
+  const bool empty = int64_t(B) * L == 0;  // nothing to read or write: NULL allowed
+  if (!empty && (!x_in || !x_out)) return CheckResult::bad("x_in and x_out must be set");
+  if (!(eps >= 0.0f)) return CheckResult::bad("eps must be >= 0");
+  if (!aligned16(x_in) || !aligned16(x_out) || (gain && !aligned16(gain)))
+    return CheckResult::bad("tensor and gain pointers must be 16-byte aligned");
+  const size_t n = size_t(B) * size_t(L) * size_t(H) * size_t(D) * esize(dtype);
+  if (x_out != x_in && overlaps(x_in, n, x_out, n)) return CheckResult::bad("x_out partially overlaps x_in");
+  return CheckResult::good();
+}
+
 // Mirror of vdit_attn_args with plain types (kept layout-identical).
 struct AttnArgs {
   int32_t mode, dtype, B, n_heads, n_kv_heads, head_dim;

@@ -103,10 +103,23 @@ struct RopeLaunch {
   int32_t pairs_t, pairs_h, pairs_w;
   float theta;
   float eps;
-  int32_t norm;
+  int32_t norm_q;  // RMSNorm the q rows before rotating them
+  int32_t norm_k;  // RMSNorm the k rows before rotating them
   int32_t dtype;
 };
 hipError_t launch_rope(const RopeLaunch& p, hipStream_t s);
+
+// Per-head RMSNorm without rotation: rows of D channels, rows = B * L * H.
+struct RmsNormLaunch {
+  const void* x_in;
+  void* x_out;
+  const float* gain;
+  int64_t rows;
+  int32_t D;
+  float eps;
+  int32_t dtype;
+};
+hipError_t launch_rms_norm(const RmsNormLaunch& p, hipStream_t s);
 
 struct MergeLaunch {
   const void* o_a;
