@@ -192,15 +192,16 @@ def test_full_attention_key_split(D):
     check(o_plain, wo, "bf16", "O (unsplit)"); check_lse(lse_plain, wl, "bf16", "LSE (unsplit)")
 
 
-@pytest.mark.parametrize("D", [128, 64])
-def test_full_attention_bounded_and_online_softmax(D):
-    # 256-query workgroups (8 heads x 64 query tiles: two even rounds on 256
-    # CUs), where the key-norm bound is used: a wavefront whose queries
+@pytest.mark.parametrize("D,Lq", [(128, 16347), (64, 16347), (128, 9001), (64, 9001)])
+def test_full_attention_bounded_and_online_softmax(D, Lq):
+    # Lq 16347: 256-query workgroups (8 heads x 64 query tiles: two even
+    # rounds on 256 CUs); Lq 9001: 128-query workgroups (8 heads x 71 tiles,
+    # no key split).  Both use the key-norm bound: a wavefront whose queries
     # satisfy 2 c2 |q| max|k| <= 64 skips the running maximum.  Query rows
     # 4000..6099 are scaled by 8, beyond that bound, so wavefronts of both
     # kinds share workgroups.  Without the bound (workspace too small) every
     # wavefront keeps the online maximum.
-    Lq, Lkv, Hq, Hk = 16347, 3001, 8, 2
+    Lkv, Hq, Hk = 3001, 8, 2
     log(f"bounded-score and online-max softmax: D={D} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
     rng = np.random.default_rng(81)
     q64 = rng.standard_normal((1, Lq, Hq, D))

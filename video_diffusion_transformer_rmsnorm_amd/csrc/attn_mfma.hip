@@ -51,7 +51,7 @@
 #define VDIT_ATTN_SCHED 1
 #endif
 #ifndef VDIT_ATTN_BOUND_MIN_NW
-#define VDIT_ATTN_BOUND_MIN_NW 8  // smallest workgroup shape (wavefronts) with the bounded-score path
+#define VDIT_ATTN_BOUND_MIN_NW 4  // smallest workgroup shape (wavefronts) with the bounded-score path
 #endif
 #ifndef VDIT_ATTN_NPB
 #define VDIT_ATTN_NPB 6  // exponential pairs (of 16) computed among the PV MFMAs
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // 2 m_i <= kBoundSpan nothing that matters underflows.  A wavefront takes
   // this path when all its queries qualify; otherwise it keeps the online
   // maximum (both paths pass the same barriers).
-  // (8-wavefront kernel only: the 4- and 2-wavefront kernels keep their
-  // single loop, whose instruction schedule a second copy disturbs)
+  // (8- and 4-wavefront kernels; the 2-wavefront kernel, for problems too
+  // small to fill the chip, keeps a single loop)
   bool fast = false;
   if (NW >= VDIT_ATTN_BOUND_MIN_NW && p.kbound != nullptr) {
     // the partial maxima (at most 64): one per lane, then a wavefront max
@@ -917,8 +917,13 @@ int attn_waves(const AttnLaunch& p) {
 }
 }  // namespace
 
+// The key-norm pre-pass pays for itself where each query sees many keys:
+// the chunk-hybrid's 128-query workgroups see one chunk (about a thousand
+// keys) and run faster on the online maximum alone.
 bool attn_uses_key_bound(const AttnLaunch& p) {
-  return VDIT_ATTN_BIG_QB == 1 && attn_waves(p) >= VDIT_ATTN_BOUND_MIN_NW;
+  const int nw = attn_waves(p);
+  if (VDIT_ATTN_BIG_QB != 1 || nw < VDIT_ATTN_BOUND_MIN_NW) return false;
+  return nw == 8 || p.epi != kEpiHybrid;
 }
 
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
