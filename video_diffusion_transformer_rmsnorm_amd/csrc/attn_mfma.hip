@@ -32,9 +32,13 @@
 //    V_{j+1} stream into the free buffers meanwhile.  One barrier per tile.
 //    Two wavefronts share each SIMD (<= 256 VGPRs), so one's exp/max work
 //    overlaps the other's matrix products.
-//  * Online softmax in log2 units with a lazy rescale: the running max only
-//    moves when a row's tile max exceeds it by more than 8 (so p <= 2^8),
-//    which skips the output rescale on almost every tile.
+//  * Bounded-score softmax where a key-norm pre-pass bounds every score of
+//    the wavefront's queries: p = 2^(c2 s) needs no running maximum, and
+//    with Q pre-scaled by c2 the exponent comes straight from the MFMA
+//    accumulator (one VALU op less per score).  Otherwise an online softmax
+//    in log2 units with a lazy rescale: the running max only moves when a
+//    row's tile max exceeds it by more than 8 (so p <= 2^8), which skips the
+//    output rescale on almost every tile.
 //  * All LDS addresses are precomputed per lane; tile and buffer offsets are
 //    instruction immediates (the loop is unrolled by two over the buffer
 //    parity).  Workgroup ids are remapped so each XCD walks a contiguous
@@ -47,9 +51,6 @@
 #ifndef VDIT_ATTN_BIG_QB
 #define VDIT_ATTN_BIG_QB 1  // query blocks per wavefront for large problems (2: one wavefront per SIMD)
 #endif
-#ifndef VDIT_ATTN_SCHED
-#define VDIT_ATTN_SCHED 1
-#endif
 #ifndef VDIT_ATTN_BOUND_MIN_NW
 #define VDIT_ATTN_BOUND_MIN_NW 4  // smallest workgroup shape (wavefronts) with the bounded-score path
 #endif
@@ -58,15 +59,6 @@
 #endif
 #ifndef VDIT_ATTN_DOT2
 #define VDIT_ATTN_DOT2 0  // row sums by v_dot2_f32_bf16 over the packed bf16 p (slower: a serial accumulate)
-#endif
-#ifndef VDIT_ATTN_FENCED
-#define VDIT_ATTN_FENCED 1  // interleave written in source order with scheduling fences
-#endif
-#ifndef VDIT_ATTN_VALU_PER_MFMA
-#define VDIT_ATTN_VALU_PER_MFMA 4  // VALU ops placed after each QK^T MFMA (4- and 2-wavefront kernels)
-#endif
-#ifndef VDIT_ATTN_VALU_PER_MFMA8
-#define VDIT_ATTN_VALU_PER_MFMA8 5  // ... in the 8-wavefront kernel
 #endif
 #ifndef VDIT_ATTN_KPREF
 #define VDIT_ATTN_KPREF 3  // K operand reads issued ahead of their MFMA
@@ -300,14 +292,14 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   for (int qb = 0; qb < QB; ++qb) { m2[qb] = -INFINITY; lsum[qb] = 0.f; }
   const float c2 = p.scale_log2;
 
-  // Bounded scores (Cauchy-Schwarz): s_ij <= |q_i| |k_j| <= |q_i| Kmax, with
-  // Kmax^2 the largest squared key norm from the bound pass.  m_i = c2 |q_i|
-  // Kmax then bounds every score of query i in log2 units, so
-  // p = 2^(c2 s - m_i) <= 1 needs neither a running maximum nor rescaling;
-  // and as c2 s >= -m_i, the row's largest p is >= 2^(-2 m_i): for
-  // 2 m_i <= kBoundSpan nothing that matters underflows.  A wavefront takes
-  // this path when all its queries qualify; otherwise it keeps the online
-  // maximum (both paths pass the same barriers).
+  // Bounded scores (Cauchy-Schwarz): |s_ij| <= |q_i| |k_j| <= |q_i| Kmax,
+  // with Kmax^2 the largest squared key norm from the bound pass.  m_i =
+  // c2 |q_i| Kmax then bounds every score of query i in log2 units: for
+  // m_i <= kBoundSpan / 2 every p = 2^(c2 s) is representable as it stands,
+  // so the wavefront needs neither a running maximum nor rescaling nor a
+  // shift of the scores.  A wavefront takes this path when all its queries
+  // qualify; otherwise it keeps the online maximum (both paths pass the
+  // same barriers).
   // (8- and 4-wavefront kernels; the 2-wavefront kernel, for problems too
   // small to fill the chip, keeps a single loop)
   bool fast = false;
@@ -333,19 +325,31 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       mb[qb] = c2 * sqrtf(n2 * kmax2);
       ok = ok && (2.f * mb[qb] <= kBoundSpan);
     }
+    fast = __ballot(!ok) == 0;
+    if (fast) {
+      // |c2 s| <= mb <= kBoundSpan / 2 = 32: p = 2^(c2 s) lies in
+      // [2^-32, 2^32] and the row's largest p is >= 2^-32, well inside the
+      // float32 and bfloat16 exponent range (a row sum over fewer than 2^31
+      // keys stays below 2^63).  So the scores need no shift
+      // (m = 0) and, with Q pre-scaled by c2 (one more bf16 rounding of q,
+      // a relative 2^-9 at most), the MFMA accumulator holds c2 s itself.
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        m2[qb] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) Qr[qb][ks][j] = static_cast<__bf16>(static_cast<float>(Qr[qb][ks][j]) * c2);
+      }
+    }
 #if defined(__HIP_DEVICE_COMPILE__)
-    // keep Q's bf16 registers as loaded (reading them as floats above must not
-    // change how the compiler holds them through the main loop)
+    // keep Q's bf16 registers where they are (reading them as floats above
+    // must not change how the compiler holds them through the main loop)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(Qr[qb][ks]));
 #endif
-    fast = __ballot(!ok) == 0;
-    if (fast) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) m2[qb] = mb[qb];
-    }
   }
 
   // S^T of the tile in K buffer `buf` (unmasked); each K operand feeds QB MFMAs
@@ -441,112 +445,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     }
   };
 
-  // Region A in source order: S^T of the next tile (K buffer `buf`) on the
-  // matrix cores, each MFMA followed by its share of this tile's
-  // p = 2^(s*c2 - m2) -> P (bf16 B operands of the PV product), with the
-  // row sum as a shallow tree per group of 8.  (The instruction scheduler
-  // keeps this interleave; a wavefront issues in order, so the exponentials
-  // overlap the matrix cores only when they sit between MFMAs.)
-  auto qk_exps = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
-    constexpr int NSTEP = 2 * KS;        // MFMAs per query block
-    constexpr int NEL = 32 * QB;         // scores per lane
-    constexpr int PER = NEL / NSTEP;     // exponentials per MFMA step
-    static_assert(NEL % NSTEP == 0 && PER % 2 == 0, "exponential split");
-    const char* Kl = lds + buf * KTILE_B + kaddr;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Sn[kb][qb][i] = 0.f;
-    float e[NEL];
-    float part[QB][4];
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int ks = st >> 1, kb = st & 1;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + ks * 32 + kb * 32 * KROWB);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        Sn[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Qr[qb][ks], Sn[kb][qb], 0, 0, 0);
-#pragma unroll
-      for (int x = 0; x < PER; ++x) {
-        const int el = st * PER + x;  // (qb, kb, hh, j) in that order
-        const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15;
-        e[el] = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
-        if ((el & 7) == 7) {
-          const int g0 = el - 7, hh = i >> 3;
-          bf16x8 pv8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pv8[j] = static_cast<__bf16>(e[g0 + j]);
-          P[kb2][qb][hh] = pv8;
-          part[qb][2 * kb2 + hh] =
-              ((e[g0] + e[g0 + 1]) + (e[g0 + 2] + e[g0 + 3])) + ((e[g0 + 4] + e[g0 + 5]) + (e[g0 + 6] + e[g0 + 7]));
-        }
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      lsum[qb] += (part[qb][0] + part[qb][1]) + (part[qb][2] + part[qb][3]);
-#if defined(__HIP_DEVICE_COMPILE__)
-      // materialise the sum here: otherwise the compiler sinks these adds
-      // into the next tile and keeps the exponentials live across the PV
-      // MFMAs (a VGPR constraint exists only in the device pass)
-      asm volatile("" : "+v"(lsum[qb]));
-#endif
-    }
-  };
-
-  // O^T += V^T P^T with V from V buffer `buf`; each V^T operand feeds QB MFMAs
-  auto pv = [&](int buf, bf16x8 (*P)[QB][2]) {
-    const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk) * ROWB));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk + 4) * ROWB));
-        const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), P[kk >> 1][qb][kk & 1], O[db][qb], 0, 0, 0);
-      }
-  };
-
-  // Instruction interleave of one tile's math, in two regions.  Region A: the
-  // QK^T MFMAs of the next tile spread through this tile's exp/convert VALU
-  // work (a wavefront issues in order, so VALU work overlaps the matrix
-  // cores only when it sits between MFMAs), K operand reads ahead of use.
-  // Region B: the PV MFMAs with their transposed V reads ahead of use.
-  auto schedule_a = [&]() {
-#if VDIT_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, VDIT_ATTN_KPREF, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, NW == 8 ? VDIT_ATTN_VALU_PER_MFMA8 : VDIT_ATTN_VALU_PER_MFMA, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#endif
-  };
-  auto schedule_b = [&]() {
-#if VDIT_ATTN_SCHED
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * VDIT_ATTN_VPREF, 1);
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-    }
-#endif
-  };
-
-  // Fenced form of the two regions: the interleave is written out in source
+  // The two regions of a tile: the interleave is written out in source
   // order and pinned with scheduling fences after every MFMA step, so it does
   // not depend on the scheduler's pattern matching.  Region A: step st issues
   // the K operand read for step st + KPREF, the MFMA(s) of step st, and its
@@ -563,12 +462,16 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   constexpr int NPA = NPAIR - NPB;
   static_assert(NPB >= 0 && NPB <= 8, "pairs moved to region B");
   float run[QB];
-  // p for pair pr of query block ... -> P, running sum
-  auto exp_pair = [&](int pr, f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
+  // p for pair pr of query block ... -> P, running sum.  Bounded-score
+  // wavefronts hold scores already in log2 units (Q pre-scaled by c2, no
+  // shift): p = 2^s straight from the accumulator.
+  auto exp_pair = [&](int pr, f32x16 (*S)[QB], bf16x8 (*P)[QB][2], auto fastc) {
+    constexpr bool FAST = decltype(fastc)::value;
     const int el = 2 * pr;  // (qb, kb, hh, j) in that order
     const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15, hh = i >> 3, j = i & 7;
-    const float e0 = fast_exp2(fmaf(S[kb2][qb][i], c2, -m2[qb]));
-    const float e1 = fast_exp2(fmaf(S[kb2][qb][i + 1], c2, -m2[qb]));
+    const float x0 = S[kb2][qb][i], x1 = S[kb2][qb][i + 1];
+    const float e0 = fast_exp2(FAST ? x0 : fmaf(x0, c2, -m2[qb]));
+    const float e1 = fast_exp2(FAST ? x1 : fmaf(x1, c2, -m2[qb]));
     const __bf16 b0 = static_cast<__bf16>(e0), b1 = static_cast<__bf16>(e1);
     P[kb2][qb][hh][j] = b0;
     P[kb2][qb][hh][j + 1] = b1;
@@ -584,7 +487,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     asm volatile("" : "+v"(run[qb]));  // keep the sum in this step (no sinking)
 #endif
   };
-  auto region_a = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2]) {
+  auto region_a = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2], auto fastc) {
     constexpr int NSTEP = 2 * KS;
     constexpr int KP = VDIT_ATTN_KPREF < NSTEP ? VDIT_ATTN_KPREF : NSTEP;
     const char* Kl = lds + buf * KTILE_B + kaddr;
@@ -611,7 +514,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
         Sn[st & 1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], Qr[qb][st >> 1], Sn[st & 1][qb], 0, 0, 0);
 #pragma unroll
       for (int pr = 0; pr < NPA; ++pr)
-        if ((pr * NSTEP) / NPA == st) exp_pair(pr, S, P);
+        if ((pr * NSTEP) / NPA == st) exp_pair(pr, S, P, fastc);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -646,7 +549,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       // first reader (PV step 2 * DB for the first quarter, 3 * DB after)
 #pragma unroll
       for (int k = 0; k < NPB; ++k)
-        if ((k * LASTB) / NPB == st) exp_pair(NPA + k, S, P);
+        if ((k * LASTB) / NPB == st) exp_pair(NPA + k, S, P, std::integral_constant<bool, !DOMAX>{});
       if constexpr (DOMAX) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -701,29 +604,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       // tile too, on stale LDS data, and discarded)
       f32x16 Sn[2][QB];
       bf16x8 P[2][QB][2];
-#if VDIT_ATTN_FENCED
       __builtin_amdgcn_sched_barrier(0);
-      region_a(1 - P0, Sn, S, P);
+      region_a(1 - P0, Sn, S, P, fastc);
       // region B: O^T += V^T P^T || lane max of tile t+1's scores
       region_b(P0, S, P, Sn, mx, std::integral_constant<bool, !FAST>{});
       __builtin_amdgcn_sched_barrier(0);
-#else
-      qk_exps(1 - P0, Sn, S, P);
-      schedule_a();
-      __builtin_amdgcn_sched_barrier(0);
-      // region B: O^T += V^T P^T || lane max of tile t+1's scores
-      pv(P0, P);
-      if constexpr (!FAST) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          mx[qb] = lane_max(Sn, qb);
-#if defined(__HIP_DEVICE_COMPILE__)
-          asm volatile("" : "+v"(mx[qb]));  // keep the max here, among the PV MFMAs
-#endif
-        }
-      }
-      schedule_b();
-#endif
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
