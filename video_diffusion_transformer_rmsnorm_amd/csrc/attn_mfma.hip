@@ -386,6 +386,19 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     return fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
   };
 
+  // The tail masks must stay inside their (wavefront-uniform) branch: left
+  // to itself the compiler turns them into selects at the join, one per
+  // score on every tile.  An empty asm on the masked registers in the branch
+  // keeps them there.
+  auto pin_scores = [&](f32x16 (*S)[QB]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(S[kb][qb]));
+#endif
+  };
+
   // row max of tile scores S (lane maxima mx precomputed on unmasked scores):
   // mask the keys >= nv of a tail tile, combine the two lane halves, then the
   // lazy rescale
@@ -401,6 +414,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
             for (int qb = 0; qb < QB; ++qb) S[kb][qb][i] = -INFINITY;
           }
         }
+      pin_scores(S);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = lane_max(S, qb);
     }
@@ -442,6 +456,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
             for (int qb = 0; qb < QB; ++qb) S[kb][qb][i] = -INFINITY;
           }
         }
+      pin_scores(S);
     }
   };
 
