@@ -325,28 +325,58 @@ def _merge_softmax_linear(o_s, lse_s, num_lin, den_lin):
     return wa[:, None] * o_s + wb[:, None] * o_l, L
 
 
-def hybrid_explicit(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
-                    s0=None, z0=None):
-    """Chunk-hybrid attention, explicit form (MobileWan review, Sec. 3.2).
+def _window(c0: int, c1: int, ctx: int, overlap: int):
+    """Keys a query chunk [c0, c1) (query indices) attends to with softmax: its
+    own tokens plus the `overlap` tokens before them, in key indices of a call
+    whose first `ctx` keys precede the first query (MobileWan review, Appendix
+    A.3.1 as the ledger quotes it: chunk T_c, overlap T_o temporal slices for
+    the softmax attention)."""
+    return max(0, ctx + c0 - overlap), ctx + c1
 
-    Token i in chunk c = [c*C, (c+1)*C) attends with softmax to the keys of
-    its own chunk (bidirectional) and, through linear attention with
-    phi = elu + 1, to every token of every earlier chunk:
-        O_i = (sum_{j in c} e^{s_ij} v_j + sum_{j < c*C} (phi(q_i).phi(k_j)) v_j)
-              / (sum_{j in c} e^{s_ij} + sum_{j < c*C} phi(q_i).phi(k_j)),
-    with s_ij = scale q_i.k_j.  The incoming state (s0, z0) stands for tokens
-    before this sequence.  The earlier-chunk sums are formed directly from all
-    earlier tokens (no running state).  Returns (o, lse, s_final, z_final).
-    """
+
+def _folded_end(Lkv: int, overlap: int) -> int:
+    """Keys the returned state covers: all but the last `overlap`, which the
+    next call passes back as its context."""
+    return max(0, Lkv - overlap)
+
+
+def _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap):
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     B, L, Hq, D = q.shape
     Hk = k.shape[2]
+    if k.shape[1] != ctx + L or v.shape[1] != ctx + L:
+        raise ValueError("k and v hold ctx + Lq tokens")
+    if not 0 <= ctx <= overlap:
+        raise ValueError("0 <= ctx <= overlap")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    s0 = np.zeros((B, Hk, D, D)) if s0 is None else np.asarray(s0, np.float64)
-    z0 = np.zeros((B, Hk, D)) if z0 is None else np.asarray(z0, np.float64)
+    s0 = np.zeros((B, Hk, D, D)) if s0 is None else np.array(s0, np.float64)
+    z0 = np.zeros((B, Hk, D)) if z0 is None else np.array(z0, np.float64)
+    return q, k, v, scale, s0, z0
+
+
+def hybrid_explicit(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
+                    s0=None, z0=None, overlap: int = 0, ctx: int = 0):
+    """Chunk-hybrid attention, explicit form (MobileWan review, Sec. 3.2).
+
+    Query token i in chunk c = [c*C, (c+1)*C) attends with softmax to the keys
+    of its window W_c (its own chunk, bidirectional, plus the `overlap`
+    tokens before it; Appendix A.3.1's T_o) and, through linear attention
+    with phi = elu + 1, to every key before that window:
+        O_i = (sum_{j in W_c} e^{s_ij} v_j + sum_{j < start(W_c)} (phi(q_i).phi(k_j)) v_j)
+              / (sum_{j in W_c} e^{s_ij} + sum_{j < start(W_c)} phi(q_i).phi(k_j)),
+    with s_ij = scale q_i.k_j, so each earlier key enters once.  k and v hold
+    ctx + Lq tokens: the first ctx (at most `overlap`) are context from before
+    the first query.  The incoming state (s0, z0) stands for keys before this
+    call; the earlier-key sums are formed directly from all earlier keys (no
+    running state).  The returned state adds every key but the last
+    `overlap`.  Returns (o, lse, s_final, z_final).
+    """
+    q, k, v, scale, s0, z0 = _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap)
+    B, L, Hq, D = q.shape
+    Hk = k.shape[2]
     o = np.zeros((B, L, Hq, D))
     lse = np.zeros((B, Hq, L))
     fq = phi(q)
@@ -355,41 +385,50 @@ def hybrid_explicit(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
         for h in range(Hq):
             kh = _kv_head(h, Hq, Hk)
             for c0, c1 in _chunks(L, chunk_tokens):
-                os_, ls_ = attention(q[b:b + 1, c0:c1, h:h + 1], k[b:b + 1, c0:c1, kh:kh + 1],
-                                     v[b:b + 1, c0:c1, kh:kh + 1], scale)
-                S = s0[b, kh] + fk[b, :c0, kh, :].T @ v[b, :c0, kh, :]
-                z = z0[b, kh] + fk[b, :c0, kh, :].sum(axis=0)
+                w0, w1 = _window(c0, c1, ctx, overlap)
+                os_, ls_ = attention(q[b:b + 1, c0:c1, h:h + 1], k[b:b + 1, w0:w1, kh:kh + 1],
+                                     v[b:b + 1, w0:w1, kh:kh + 1], scale)
+                S = s0[b, kh] + fk[b, :w0, kh, :].T @ v[b, :w0, kh, :]
+                z = z0[b, kh] + fk[b, :w0, kh, :].sum(axis=0)
                 num = fq[b, c0:c1, h, :] @ S
                 den = fq[b, c0:c1, h, :] @ z
                 oc, lc = _merge_softmax_linear(os_[0, :, 0, :], ls_[0, 0, :], num, den)
                 o[b, c0:c1, h, :] = oc
                 lse[b, h, c0:c1] = lc
-    s_fin = s0 + np.einsum("blhd,blhe->bhde", fk, v)
-    z_fin = z0 + fk.sum(axis=1)
+    e = _folded_end(k.shape[1], overlap)
+    s_fin = s0 + np.einsum("blhd,blhe->bhde", fk[:, :e], v[:, :e])
+    z_fin = z0 + fk[:, :e].sum(axis=1)
     return o, lse, s_fin, z_fin
 
 
 def hybrid_recurrent(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
-                     s0=None, z0=None):
+                     s0=None, z0=None, overlap: int = 0, ctx: int = 0):
     """Chunk-hybrid attention run as an RNN over chunks (MobileWan review,
-    Sec. 3.2, Eqs. 5-10 as described): for each chunk, read the running state
-    (s_t, z_t) for the cross-chunk term, then absorb the chunk:
-    s += phi(K_c)^T V_c, z += sum_j phi(k_j).  Returns (o, lse, s, z)."""
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
+    Sec. 3.2, Eqs. 5-10 as described): for each chunk, first absorb into the
+    running state (s_t, z_t) the keys that now fall before the chunk's
+    softmax window (s += phi(k_j) v_j^T, z += phi(k_j)), then read it for the
+    cross-chunk term; at the end absorb all keys but the last `overlap`.
+    Window, context and overlap as in hybrid_explicit.  Returns (o, lse, s, z)."""
+    q, k, v, scale, s, z = _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap)
     B, L, Hq, D = q.shape
     Hk = k.shape[2]
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    s = np.zeros((B, Hk, D, D)) if s0 is None else np.array(s0, np.float64)
-    z = np.zeros((B, Hk, D)) if z0 is None else np.array(z0, np.float64)
     o = np.zeros((B, L, Hq, D))
     lse = np.zeros((B, Hq, L))
+    pos = 0  # keys absorbed so far
+
+    def absorb(upto):
+        nonlocal s, z, pos
+        if upto > pos:
+            fk = phi(k[:, pos:upto])
+            s = s + np.einsum("blhd,blhe->bhde", fk, v[:, pos:upto])
+            z = z + fk.sum(axis=1)
+            pos = upto
+
     for c0, c1 in _chunks(L, chunk_tokens):
-        os_, ls_ = attention(q[:, c0:c1], k[:, c0:c1], v[:, c0:c1], scale)
+        w0, w1 = _window(c0, c1, ctx, overlap)
+        absorb(w0)
+        os_, ls_ = attention(q[:, c0:c1], k[:, w0:w1], v[:, w0:w1], scale)
         fq = phi(q[:, c0:c1])
-        fk = phi(k[:, c0:c1])
         for b in range(B):
             for h in range(Hq):
                 kh = _kv_head(h, Hq, Hk)
@@ -398,34 +437,31 @@ def hybrid_recurrent(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
                 oc, lc = _merge_softmax_linear(os_[b, :, h, :], ls_[b, h, :], num, den)
                 o[b, c0:c1, h, :] = oc
                 lse[b, h, c0:c1] = lc
-        s = s + np.einsum("blhd,blhe->bhde", fk, v[:, c0:c1])
-        z = z + fk.sum(axis=1)
+    absorb(_folded_end(k.shape[1], overlap))
     return o, lse, s, z
 
 
-def hybrid_partials(q, k, v, chunk_tokens: int, scale: Optional[float] = None, s0=None, z0=None):
+def hybrid_partials(q, k, v, chunk_tokens: int, scale: Optional[float] = None, s0=None, z0=None,
+                    overlap: int = 0, ctx: int = 0):
     """The two partials of the hybrid, per token: softmax (o_s, lse_s) over the
-    token's own chunk and linear (o_l, lse_l) over earlier chunks, with
+    token's window and linear (o_l, lse_l) over the keys before it, with
     lse_l = ln(phi(q)^T z) (-inf when z = 0).  Used to check each partial on its own."""
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
-    v = np.asarray(v, np.float64)
+    q, k, v, scale, s0, z0 = _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap)
     B, L, Hq, D = q.shape
     Hk = k.shape[2]
-    s0 = np.zeros((B, Hk, D, D)) if s0 is None else np.asarray(s0, np.float64)
-    z0 = np.zeros((B, Hk, D)) if z0 is None else np.asarray(z0, np.float64)
     o_s = np.zeros((B, L, Hq, D)); l_s = np.zeros((B, Hq, L))
     o_l = np.zeros((B, L, Hq, D)); l_l = np.full((B, Hq, L), -np.inf)
     fq = phi(q); fk = phi(k)
     for c0, c1 in _chunks(L, chunk_tokens):
-        oc, lc = attention(q[:, c0:c1], k[:, c0:c1], v[:, c0:c1], scale)
+        w0, w1 = _window(c0, c1, ctx, overlap)
+        oc, lc = attention(q[:, c0:c1], k[:, w0:w1], v[:, w0:w1], scale)
         o_s[:, c0:c1] = oc
         l_s[:, :, c0:c1] = lc
         for b in range(B):
             for h in range(Hq):
                 kh = _kv_head(h, Hq, Hk)
-                S = s0[b, kh] + fk[b, :c0, kh, :].T @ v[b, :c0, kh, :]
-                z = z0[b, kh] + fk[b, :c0, kh, :].sum(axis=0)
+                S = s0[b, kh] + fk[b, :w0, kh, :].T @ v[b, :w0, kh, :]
+                z = z0[b, kh] + fk[b, :w0, kh, :].sum(axis=0)
                 den = fq[b, c0:c1, h, :] @ z
                 num = fq[b, c0:c1, h, :] @ S
                 pos = den > 0

@@ -451,19 +451,21 @@ def test_phi_is_elu_plus_one():
     assert np.allclose(O.phi(np.linspace(-5, 5, 101)), t.numpy(), atol=1e-15)
 
 
-def _hybrid_brute(q, k, v, C, scale):
-    # Full L x L weight matrix by loops: same chunk -> e^{s_ij}; earlier chunk ->
-    # phi(q_i).phi(k_j); later chunk -> 0.  O = W V / W 1.
+def _hybrid_brute(q, k, v, C, scale, overlap=0):
+    # Full L x L weight matrix by loops: key in the query's chunk or in the
+    # `overlap` tokens before that chunk -> e^{s_ij}; any earlier key ->
+    # phi(q_i).phi(k_j); later key -> 0.  O = W V / W 1.
     B, L, H, D = q.shape
     out = np.zeros_like(q)
     for h in range(H):
         for i in range(L):
+            start = (i // C) * C
             wts = []
             for j in range(L):
-                if j // C == i // C:
+                if start - overlap <= j < start + C:
                     s = scale * math.fsum(q[0, i, h, d] * k[0, j, h, d] for d in range(D))
                     wts.append(math.exp(s))
-                elif j // C < i // C:
+                elif j < start - overlap:
                     fq = [q[0, i, h, d] + 1 if q[0, i, h, d] > 0 else math.exp(q[0, i, h, d]) for d in range(D)]
                     fk = [k[0, j, h, d] + 1 if k[0, j, h, d] > 0 else math.exp(k[0, j, h, d]) for d in range(D)]
                     wts.append(math.fsum(a * b for a, b in zip(fq, fk)))
@@ -484,6 +486,78 @@ def test_hybrid_matches_brute_force_weight_matrix():
     o_r, _, _, _ = O.hybrid_recurrent(q, k, v, 4, 0.5)
     assert np.allclose(o_e, want, atol=1e-12)
     assert np.allclose(o_r, want, atol=1e-12)
+
+
+@pytest.mark.parametrize("overlap", [2, 5, 9])
+def test_hybrid_overlap_matches_brute_force_weight_matrix(overlap):
+    # MobileWan review, Appendix A.3.1 (ledger): the softmax window of a chunk
+    # reaches T_o slices back; keys before the window go through the linear
+    # term, each key exactly once.
+    r = RNG(60 + overlap)
+    q = r.standard_normal((1, 11, 2, 4)); k = r.standard_normal((1, 11, 2, 4))
+    v = r.standard_normal((1, 11, 2, 4))
+    want = _hybrid_brute(q, k, v, 4, 0.5, overlap)
+    o_e, _, _, _ = O.hybrid_explicit(q, k, v, 4, 0.5, overlap=overlap)
+    o_r, _, _, _ = O.hybrid_recurrent(q, k, v, 4, 0.5, overlap=overlap)
+    assert np.allclose(o_e, want, atol=1e-12)
+    assert np.allclose(o_r, want, atol=1e-12)
+    if overlap:
+        o_0, _, _, _ = O.hybrid_explicit(q, k, v, 4, 0.5)
+        assert np.abs(o_0 - want).max() > 1e-3  # the overlap changes the result
+
+
+def test_hybrid_overlap_recurrent_equals_explicit_and_state():
+    r = RNG(62)
+    B, L, Hq, Hk, D, C, Ov = 2, 37, 4, 2, 8, 9, 4
+    q = r.standard_normal((B, L, Hq, D)); k = r.standard_normal((B, L, Hk, D))
+    v = r.standard_normal((B, L, Hk, D))
+    s0 = r.standard_normal((B, Hk, D, D)) * 0.1; z0 = np.abs(r.standard_normal((B, Hk, D)))
+    e = O.hybrid_explicit(q, k, v, C, s0=s0, z0=z0, overlap=Ov)
+    rr = O.hybrid_recurrent(q, k, v, C, s0=s0, z0=z0, overlap=Ov)
+    for a, b in zip(e, rr):
+        assert np.allclose(a, b, atol=1e-11)
+    # final state: all keys but the last Ov, by loops
+    fk = O.phi(k)
+    s_want = s0.copy(); z_want = z0.copy()
+    for b in range(B):
+        for h in range(Hk):
+            for j in range(L - Ov):
+                s_want[b, h] += np.outer(fk[b, j, h], v[b, j, h])
+                z_want[b, h] += fk[b, j, h]
+    assert np.allclose(rr[2], s_want, atol=1e-11) and np.allclose(rr[3], z_want, atol=1e-11)
+
+
+def test_hybrid_overlap_streaming_calls_with_context_equal_one_call():
+    # Streaming with overlap: each call after the first passes the previous
+    # call's last `overlap` keys/values as context ahead of its queries.
+    r = RNG(63)
+    L, C, Ov = 30, 6, 4
+    q = r.standard_normal((1, L, 2, 8)); k = r.standard_normal((1, L, 2, 8))
+    v = r.standard_normal((1, L, 2, 8))
+    o, lse, s, z = O.hybrid_recurrent(q, k, v, C, overlap=Ov)
+    outs, st, zt = [], None, None
+    for a, b in ((0, 12), (12, 18), (18, 30)):
+        c = min(Ov, a)
+        oc, lc, st, zt = O.hybrid_explicit(q[:, a:b], k[:, a - c:b], v[:, a - c:b], C, s0=st, z0=zt,
+                                           overlap=Ov, ctx=c)
+        outs.append((oc, lc))
+    assert np.allclose(np.concatenate([x[0] for x in outs], 1), o, atol=1e-12)
+    assert np.allclose(np.concatenate([x[1] for x in outs], 2), lse, atol=1e-12)
+    assert np.allclose(st, s, atol=1e-12) and np.allclose(zt, z, atol=1e-12)
+
+
+def test_hybrid_overlap_covering_everything_is_block_causal_softmax():
+    # With the window reaching back to the first key no linear term is left:
+    # chunk-causal softmax attention (masked torch float64 SDPA).
+    r = RNG(64)
+    L, C = 14, 4
+    q = r.standard_normal((1, L, 2, 8)); k = r.standard_normal((1, L, 2, 8))
+    v = r.standard_normal((1, L, 2, 8))
+    o, _, s, z = O.hybrid_explicit(q, k, v, C, overlap=L)
+    chunk = np.arange(L) // C
+    mask = np.where(chunk[None, :] <= chunk[:, None], 0.0, -np.inf)[None, None]
+    assert np.allclose(o, sdpa64(q, k, v, mask=mask), atol=1e-12)
+    assert not s.any() and not z.any()
 
 
 def test_hybrid_recurrent_equals_explicit_and_state():
@@ -545,6 +619,12 @@ def test_hybrid_partials_merge_to_output():
     m, lm = O.lse_merge(o_s, l_s, o_l, l_l)
     assert np.allclose(m, o, atol=1e-12) and np.allclose(lm, lse, atol=1e-12)
     assert np.isneginf(l_l[:, :, :4]).all() and np.isfinite(l_l[:, :, 4:]).all()
+    # overlap 5: chunk 1's window reaches key 0 (no linear term), chunk 2's starts at key 3
+    o, lse, _, _ = O.hybrid_explicit(q, k, v, 4, overlap=5)
+    o_s, l_s, o_l, l_l = O.hybrid_partials(q, k, v, 4, overlap=5)
+    m, lm = O.lse_merge(o_s, l_s, o_l, l_l)
+    assert np.allclose(m, o, atol=1e-12) and np.allclose(lm, lse, atol=1e-12)
+    assert np.isneginf(l_l[:, :, :8]).all() and np.isfinite(l_l[:, :, 8:]).all()
 
 
 # ------------------------------------------------------------- workloads --
