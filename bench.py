@@ -207,14 +207,12 @@ def bench_other(args):
     elif w.mode == "hybrid":
         s = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device=dev)
         z = torch.zeros((1, w.kv_heads, w.head_dim), device=dev)
-        n_ch = WL.ceil_div(w.tokens, w.chunk_tokens)
-        flops = sum(WL.flops_full(min(w.chunk_tokens, w.tokens - c * w.chunk_tokens),
-                                  min(w.chunk_tokens, w.tokens - c * w.chunk_tokens), w.heads, w.head_dim)
-                    for c in range(n_ch))
+        flops = WL.hybrid_flops(w)
 
         def step():
             s.zero_(); z.zero_()
-            V.vdit_attn_fwd(qd, kd, vd, mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=s, state_z=z)
+            V.vdit_attn_fwd(qd, kd, vd, mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=s, state_z=z,
+                            overlap_tokens=w.overlap_tokens)
     else:
         flops = WL.flops_full(w.tokens, w.tokens, w.heads, w.head_dim)
 
@@ -234,7 +232,8 @@ def bench_other(args):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
             "data": "synthetic", "config": {"workload": w.name, "mode": w.mode, "tokens": w.tokens,
                                             "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
-                                            "kv_norm": w.kv_norm, "reference_only": True}}
+                                            "kv_norm": w.kv_norm, "chunk_tokens": w.chunk_tokens,
+                                            "overlap_tokens": w.overlap_tokens, "reference_only": True}}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):

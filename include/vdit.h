@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define VDIT_ABI_VERSION 1
+#define VDIT_ABI_VERSION 2
 
 typedef enum {
   VDIT_OK = 0,
@@ -158,14 +158,22 @@ typedef enum {
  *   tokens plus causal linear attention across chunks with running state
  *   (MobileWan: Closing the Quality Gap for Mobile Video Diffusion, review
  *   of Sec. 3.2).  Token i of chunk c gets
- *     (sum_{j in c} e^{s_ij} v_j + phi(q_i)^T S_c) / (sum_{j in c} e^{s_ij} + phi(q_i)^T z_c)
- *   with phi(x) = elu(x) + 1 on the (already normalised and rotated) q and k,
- *   S_c = s_in + sum_{j before chunk c} phi(k_j) v_j^T, z_c = z_in + sum phi(k_j).
- *   Self-attention: Lkv must equal Lq.  state_s [B, n_kv_heads, D, D] and
- *   state_z [B, n_kv_heads, D] (float32) hold the incoming state (zero for a
- *   new sequence) and receive the state after the last chunk, so calling
- *   once per chunk equals one call over the whole sequence.  Needs
- *   `workspace` of vdit_attn_workspace_bytes().
+ *     (sum_{j in W_c} e^{s_ij} v_j + phi(q_i)^T S_c) / (sum_{j in W_c} e^{s_ij} + phi(q_i)^T z_c)
+ *   with phi(x) = elu(x) + 1 on the (already normalised and rotated) q and k.
+ *   The softmax window W_c is the chunk's own tokens plus the overlap_tokens
+ *   keys before them (the review's appendix ledger: chunks of T_c temporal
+ *   slices overlapping by T_o slices for the softmax attention; 0 = no
+ *   overlap), and S_c = s_in + sum_{j before W_c} phi(k_j) v_j^T,
+ *   z_c = z_in + sum_{j before W_c} phi(k_j): every key enters once.
+ *   k, v hold Lkv = ctx_tokens + Lq tokens: the first ctx_tokens
+ *   (0 <= ctx_tokens <= overlap_tokens) are keys/values from before the
+ *   first query, which a streaming caller carries over from its previous
+ *   call.  state_s [B, n_kv_heads, D, D] and state_z [B, n_kv_heads, D]
+ *   (float32) hold the incoming state (zero for a new sequence) and receive
+ *   it with every key of the call folded in except the last overlap_tokens
+ *   (the next call's context), so calling once per chunk equals one call
+ *   over the whole sequence.  Needs `workspace` of
+ *   vdit_attn_workspace_bytes().
  *
  * lse: [B, n_heads, Lq] float32 or NULL.  o must not overlap q, k, v, the
  * caches or the workspace.  workspace: device scratch of at least
@@ -203,6 +211,8 @@ typedef struct {
   float* state_z;              /* CHUNK_HYBRID */
   void* workspace;
   size_t workspace_bytes;
+  int64_t overlap_tokens;      /* CHUNK_HYBRID (0 in the other modes) */
+  int64_t ctx_tokens;          /* CHUNK_HYBRID (0 in the other modes) */
 } vdit_attn_args;
 
 /* Bytes of device workspace vdit_attn_fwd needs (RING, CHUNK_HYBRID) or can

@@ -94,6 +94,16 @@ int main() {
   EXPECT(check_attn(b).code == Check::invalid, "hybrid Lkv");
   b.Lkv = 100; b.chunk_tokens = 0;
   EXPECT(check_attn(b).code == Check::invalid, "hybrid chunk");
+  b.chunk_tokens = 30; b.overlap_tokens = 15; b.ctx_tokens = 15; b.Lkv = 115;
+  EXPECT(bool(check_attn(b)), "hybrid with overlap and context");
+  b.Lkv = 100;
+  EXPECT(check_attn(b).code == Check::invalid, "hybrid Lkv = ctx + Lq");
+  b.Lkv = 116; b.ctx_tokens = 16;
+  EXPECT(check_attn(b).code == Check::invalid, "hybrid context beyond the overlap");
+  b.ctx_tokens = 0; b.Lkv = 100; b.overlap_tokens = -1;
+  EXPECT(check_attn(b).code == Check::invalid, "hybrid negative overlap");
+  AttnArgs f = a; f.overlap_tokens = 4;
+  EXPECT(check_attn(f).code == Check::invalid, "overlap outside the hybrid mode");
 
   // key split plan (256 compute units)
   {

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vdit_abi_version() == V.ABI_VERSION == 1
+    assert lib.vdit_abi_version() == V.ABI_VERSION == 2
 
 
 def test_struct_layout_matches_header(tmp_path):

@@ -513,6 +513,84 @@ def test_hybrid_chunkwise_calls_equal_one_call():
     assert torch.equal(s1, s2) and torch.equal(z1, z2)
 
 
+@pytest.mark.parametrize("dtype,D,L,C,Ov,Hq,Hk", [
+    ("bf16", 128, 300, 72, 36, 2, 2), ("bf16", 64, 260, 64, 100, 4, 2), ("bf16", 128, 200, 64, 200, 2, 1),
+    ("f32", 64, 100, 24, 12, 2, 1), ("f32", 128, 70, 16, 40, 2, 2),
+])
+def test_hybrid_overlap_small(dtype, D, L, C, Ov, Hq, Hk):
+    # softmax windows reaching Ov keys before each chunk (wider than a chunk,
+    # or covering everything); the linear state covers the keys before them
+    log(f"chunk hybrid with overlap {dtype} D={D} L={L} chunk={C} overlap={Ov} Hq={Hq} Hk={Hk}")
+    q = raw((1, L, Hq, D), 121, dtype); k = raw((1, L, Hk, D), 122, dtype); v = raw((1, L, Hk, D), 123, dtype)
+    rng = np.random.default_rng(124)
+    s0 = (0.05 * rng.standard_normal((1, Hk, D, D))).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((1, Hk, D))).astype(np.float32)
+    sd = torch.from_numpy(s0).cuda(); zd = torch.from_numpy(z0).cuda()
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), mode="hybrid", chunk_tokens=C,
+                             state_s=sd, state_z=zd, overlap_tokens=Ov)
+    torch.cuda.synchronize()
+    wo, wl, ws_, wz = O.hybrid_recurrent(q.values, k.values, v.values, C, s0=s0, z0=z0, overlap=Ov)
+    check(o, wo, dtype, "O hybrid"); check_lse(lse, wl, dtype, "LSE hybrid")
+    gs, gz = from_dev(sd), from_dev(zd)
+    rs = np.linalg.norm(gs - ws_) / np.linalg.norm(ws_)
+    rz = np.linalg.norm(gz - wz) / np.linalg.norm(wz)
+    log(f"  state relF s={rs:.3e} z={rz:.3e}")
+    assert rs <= 1e-5 and rz <= 1e-5
+
+
+def test_hybrid_overlap_streaming_calls_equal_one_call():
+    # calls on chunk boundaries, each after the first carrying the previous
+    # overlap keys/values as context, equal one call (bit for bit) and the oracle
+    log("chunk hybrid with overlap: streaming calls with context == one call")
+    D, L, C, Ov, H = 128, 320, 64, 32, 2
+    q = raw((1, L, H, D), 131, "bf16"); k = raw((1, L, H, D), 132, "bf16"); v = raw((1, L, H, D), 133, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    s1 = torch.zeros((1, H, D, D), device="cuda"); z1 = torch.zeros((1, H, D), device="cuda")
+    o1, l1 = V.vdit_attn_fwd(qd, kd, vd, mode="hybrid", chunk_tokens=C, state_s=s1, state_z=z1,
+                             overlap_tokens=Ov)
+    s2 = torch.zeros_like(s1); z2 = torch.zeros_like(z1)
+    parts = []
+    for a, b in ((0, 128), (128, 192), (192, 320)):
+        c = min(Ov, a)
+        oc, _ = V.vdit_attn_fwd(qd[:, a:b].contiguous(), kd[:, a - c:b].contiguous(), vd[:, a - c:b].contiguous(),
+                                mode="hybrid", chunk_tokens=C, state_s=s2, state_z=z2, overlap_tokens=Ov,
+                                ctx_tokens=c)
+        parts.append(oc)
+    torch.cuda.synchronize()
+    o2 = torch.cat(parts, dim=1)
+    assert torch.equal(o1, o2), float((o1.float() - o2.float()).abs().max())
+    assert torch.equal(s1, s2) and torch.equal(z1, z2)
+    wo, wl, ws_, _ = O.hybrid_recurrent(q.values, k.values, v.values, C, overlap=Ov)
+    check(o1, wo, "bf16", "O hybrid"); check_lse(l1, wl, "bf16", "LSE hybrid")
+    rs = np.linalg.norm(from_dev(s1) - ws_) / np.linalg.norm(ws_)
+    assert rs <= 1e-5, rs
+
+
+@pytest.mark.slow
+def test_hybrid_overlap_full_c4_o2():
+    # chunks of T_c = 4 latent frames (1560 tokens) with T_o = 2 frames (780
+    # tokens) of softmax overlap on the 31 x 15 x 26 grid, all rows
+    w = WL.WORKLOADS[8]
+    log(f"{w.name}: rope + hybrid (chunk {w.chunk_tokens}, overlap {w.overlap_tokens}) vs oracle (all rows)")
+    q, k, v = WL.workload_inputs(w)
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*w.grid, w.pairs))
+    sd = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device="cuda")
+    zd = torch.zeros((1, w.kv_heads, w.head_dim), device="cuda")
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v), mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=sd,
+                             state_z=zd, overlap_tokens=w.overlap_tokens)
+    torch.cuda.synchronize()
+    wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
+    o_s, l_s, o_l, l_l = O.hybrid_partials(wq, wk, v.values, w.chunk_tokens, overlap=w.overlap_tokens)
+    wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
+    check(o, wo, "bf16", "O hybrid (all rows)")
+    check_lse(lse, wl, "bf16", "LSE hybrid")
+    e = w.tokens - w.overlap_tokens
+    ws_ = np.einsum("blhd,blhe->bhde", O.phi(wk[:, :e]), v.values[:, :e])
+    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
+    log(f"  state relF={rs:.3e}")
+    assert rs <= 1e-2  # as in the no-overlap case: the library's k is the bf16-rounded rotation
+
+
 @pytest.mark.slow
 def test_hybrid_5b_full():
     w = WL.WORKLOADS[5]

@@ -647,6 +647,9 @@ def test_workload_shapes_and_flop_counts():
     assert w4.tokens == 2040 and sum(w4.pairs) * 2 == w4.head_dim
     w5 = WL.WORKLOADS[5]
     assert w5.tokens == 12090 and w5.chunk_tokens == 3 * 15 * 26
+    assert abs(WL.hybrid_flops(w5) / 1e12 - 0.1701) < 1e-4  # chunk-local softmax work
+    w8 = WL.WORKLOADS[8]
+    assert w8.chunk_tokens == 4 * 15 * 26 and w8.overlap_tokens == 2 * 15 * 26  # T_c = 4, T_o = 2
     # FlashDecoder-XL (Table 5: width 1536, 24 heads, 3 KV groups; W_frm = 2),
     # 720p latents at spatial compression 16: 45 x 80 tokens per frame
     w6, w7 = WL.WORKLOADS[6], WL.WORKLOADS[7]

@@ -21,7 +21,7 @@ VDIT_BF16, VDIT_F32 = 0, 1
 VDIT_ROPE_NO_NORM = 1
 VDIT_ROPE_NO_Q_NORM = 2
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # Every symbol include/vdit.h declares.
 EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_workspace_bytes",
@@ -54,6 +54,7 @@ class VditAttnArgs(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int64),
         ("state_s", ctypes.c_void_p), ("state_z", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("overlap_tokens", ctypes.c_int64), ("ctx_tokens", ctypes.c_int64),
     ]
 
 
@@ -191,7 +192,8 @@ def vdit_attn_workspace_bytes(args: VditAttnArgs) -> int:
 def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_lse: bool = True,
                   scale: float = 0.0, k_chunks=None, v_chunks=None, k_cache=None, v_cache=None,
                   frame: int = 0, chunk_tokens: int = 0, state_s=None, state_z=None, workspace=None,
-                  n_kv_heads: Optional[int] = None, stream=None):
+                  n_kv_heads: Optional[int] = None, overlap_tokens: int = 0, ctx_tokens: int = 0,
+                  stream=None):
     """One attention call.  Returns (o, lse) (lse None unless wanted).
 
     full:    k, v [B,Lkv,Hk,D].
@@ -199,7 +201,9 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
              (also for full / rolling calls small enough to use the key split).
     rolling: k_cache, v_cache [B,n_slots,Lq,Hk,D]; k, v = this frame's keys/values or None
              (slot already filled); frame = stream index.
-    hybrid:  k, v [B,L,Hk,D]; chunk_tokens; state_s [B,Hk,D,D], state_z [B,Hk,D] float32 (in/out).
+    hybrid:  k, v [B,ctx_tokens+Lq,Hk,D]; chunk_tokens; state_s [B,Hk,D,D], state_z [B,Hk,D]
+             float32 (in/out); overlap_tokens keys before each chunk join its softmax
+             window; the first ctx_tokens (<= overlap_tokens) keys precede the first query.
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (k_cache, "k_cache"),
@@ -235,6 +239,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
         a = _attn_args(q, k, v, mode, o, lse, scale, n_kv_heads or hk, k.shape[1])
         a.chunk_tokens = chunk_tokens
         a.state_s, a.state_z = _ptr(state_s), _ptr(state_z)
+        a.overlap_tokens, a.ctx_tokens = overlap_tokens, ctx_tokens
     else:
         hk = k.shape[2]
         a = _attn_args(q, k, v, mode, o, lse, scale, n_kv_heads or hk, k.shape[1])

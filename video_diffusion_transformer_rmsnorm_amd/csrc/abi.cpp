@@ -16,6 +16,8 @@ static_assert(vdit::kKeyBoundParts == vdit::kKeyBoundBlocks && vdit::kKeyBoundBl
               "key-bound partials: one per lane of a wavefront");
 static_assert(offsetof(vdit_attn_args, workspace_bytes) == offsetof(vdit::AttnArgs, workspace_bytes),
               "vdit_attn_args layout mirror");
+static_assert(offsetof(vdit_attn_args, ctx_tokens) == offsetof(vdit::AttnArgs, ctx_tokens),
+              "vdit_attn_args layout mirror");
 
 namespace {
 
@@ -315,6 +317,9 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       hs.sc = ws + lay.off_sc;
       hs.zc = reinterpret_cast<float*>(ws + lay.off_zc);
       hs.L = a.Lq;
+      hs.Lkv = a.Lkv;
+      hs.ctx = a.ctx_tokens;
+      hs.overlap = a.overlap_tokens;
       hs.chunk = a.chunk_tokens;
       hs.n_chunks = lay.n_chunks;
       hs.nsplit = lay.nsplit;
@@ -330,6 +335,9 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       p.epi = vdit::kEpiHybrid;
       p.chunk = a.chunk_tokens;
       p.n_chunks = lay.n_chunks;
+      p.hyb_ctx = a.ctx_tokens;
+      p.hyb_overlap = a.overlap_tokens;
+      p.hyb_lkv = a.Lkv;
       p.st = ws + lay.off_sc;
       p.zc = reinterpret_cast<const float*>(ws + lay.off_zc);
       p.hk = a.k;
@@ -337,11 +345,13 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       p.nseg = 1;
       char* bound = nullptr;
       if (auto st = optional_area(a, lay.total, vdit::kbound_bytes(a), &bound); st != VDIT_OK) return st;
-      // a bound per chunk (so a chunk's result does not depend on the others)
-      if (auto st = add_key_bound(p, vdit::KvSeg{a.k, a.v, a.Lq, a.Lq * a.n_kv_heads * D}, bound, stream,
-                                  a.chunk_tokens);
-          st != VDIT_OK)
-        return st;
+      // a bound per chunk (so a chunk's result does not depend on the others);
+      // overlapping windows run on the online maximum
+      if (a.overlap_tokens == 0)
+        if (auto st = add_key_bound(p, vdit::KvSeg{a.k, a.v, a.Lq, a.Lq * a.n_kv_heads * D}, bound, stream,
+                                    a.chunk_tokens);
+            st != VDIT_OK)
+          return st;
       return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(CHUNK_HYBRID) launch");
     }
   }

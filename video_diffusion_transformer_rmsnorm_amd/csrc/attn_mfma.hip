@@ -190,10 +190,12 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     q_begin = c0 + t * BM;
     q_end = min(c1, q_begin + BM);
     if (q_begin >= q_end) return;
-    sg.k = static_cast<const uint16_t*>(p.hk) + c0 * p.Hk * D;
-    sg.v = static_cast<const uint16_t*>(p.hv) + c0 * p.Hk * D;
-    sg.len = c1 - c0;
-    sg.bstride = p.Lq * p.Hk * D;
+    // softmax window: the chunk's keys and the hyb_overlap keys before them
+    const int64_t w0 = max<int64_t>(0, p.hyb_ctx + c0 - p.hyb_overlap), w1 = p.hyb_ctx + c1;
+    sg.k = static_cast<const uint16_t*>(p.hk) + w0 * p.Hk * D;
+    sg.v = static_cast<const uint16_t*>(p.hv) + w0 * p.Hk * D;
+    sg.len = w1 - w0;
+    sg.bstride = p.hyb_lkv * p.Hk * D;
   }
   const int hk = h / (p.Hq / p.Hk);
   const int64_t rs = int64_t(p.Hk) * ROWB;  // bytes between consecutive keys

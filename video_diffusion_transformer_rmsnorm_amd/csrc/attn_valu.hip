@@ -66,11 +66,13 @@ __global__ __launch_bounds__(kValuBM) void attn_valu_kernel(AttnLaunch p, int64_
     q_end = min(c1, q_begin + kValuBM);
     if (q_begin >= q_end) return;
     const int64_t es = BF16 ? 2 : 4;
+    // softmax window: the chunk's keys and the hyb_overlap keys before them
+    const int64_t w0 = max<int64_t>(0, p.hyb_ctx + c0 - p.hyb_overlap), w1 = p.hyb_ctx + c1;
     nseg = 1;
-    segs[0].k = static_cast<const char*>(p.hk) + c0 * p.Hk * D * es;
-    segs[0].v = static_cast<const char*>(p.hv) + c0 * p.Hk * D * es;
-    segs[0].len = c1 - c0;
-    segs[0].bstride = p.Lq * p.Hk * D;
+    segs[0].k = static_cast<const char*>(p.hk) + w0 * p.Hk * D * es;
+    segs[0].v = static_cast<const char*>(p.hv) + w0 * p.Hk * D * es;
+    segs[0].len = w1 - w0;
+    segs[0].bstride = p.hyb_lkv * p.Hk * D;
   }
   const int hk = h / (p.Hq / p.Hk);
   const int64_t qi = q_begin + lane;

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(kDeltaThreads) void hybrid_delta_kernel(HybridState
   const int b = int(bid % p.B); bid /= p.B;
   const int s = int(bid % p.nsplit);
   const int64_t c = bid / p.nsplit;
-  const int64_t c0 = c * p.chunk, c1 = min(p.L, c0 + p.chunk);
+  int64_t c0, c1;
+  hybrid_delta_range(p, c, &c0, &c1);
   const int64_t per = (c1 - c0 + p.nsplit - 1) / p.nsplit;
   const int64_t t0 = min(c1, c0 + s * per), t1 = min(c1, t0 + per);
 
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kDeltaThreads) void hybrid_delta_kernel(HybridState
       const int jj = e / D, d = e % D;
       float kx = 0.f, vx = 0.f;
       if (jj < nv) {
-        const int64_t off = ((int64_t(b) * p.L + j0 + jj) * p.Hk + hk) * D + d;
+        const int64_t off = ((int64_t(b) * p.Lkv + j0 + jj) * p.Hk + hk) * D + d;
         if constexpr (BF16) {
           kx = phi_elu1(bf16_to_f32(static_cast<const uint16_t*>(p.k)[off]));
           vx = bf16_to_f32(static_cast<const uint16_t*>(p.v)[off]);
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(256) void hybrid_delta_mfma_kernel(HybridStateLaunc
   const int b = int(bid % p.B); bid /= p.B;
   const int s = int(bid % p.nsplit);
   const int64_t c = bid / p.nsplit;
-  const int64_t c0 = c * p.chunk, c1 = min(p.L, c0 + p.chunk);
+  int64_t c0, c1;
+  hybrid_delta_range(p, c, &c0, &c1);
   const int64_t per = (c1 - c0 + p.nsplit - 1) / p.nsplit;
   const int64_t t0 = min(c1, c0 + s * per), t1 = min(c1, t0 + per);
 
@@ -153,8 +155,8 @@ __global__ __launch_bounds__(256) void hybrid_delta_mfma_kernel(HybridStateLaunc
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
   float zacc = 0.f;
   const int64_t tok_stride = int64_t(p.Hk) * D;  // elements between tokens
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.L * p.Hk + hk) * D;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.L * p.Hk + hk) * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Lkv * p.Hk + hk) * D;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Lkv * p.Hk + hk) * D;
 
   // tile loads run one tile ahead in registers: tile j+1 is in flight while
   // tile j is on the matrix cores

@@ -136,6 +136,8 @@ struct AttnArgs {
   float* state_z;
   void* workspace;
   size_t workspace_bytes;
+  int64_t overlap_tokens;
+  int64_t ctx_tokens;
 };
 
 constexpr int kMaxRingChunks = 64;
@@ -250,6 +252,8 @@ inline CheckResult check_attn(const AttnArgs& a) {
   }
   if (a.lse && !aligned16(a.lse)) return CheckResult::bad("lse must be 16-byte aligned");
   if (!empty_q && overlaps(a.q, nq, a.o, nq)) return CheckResult::bad("o overlaps q");
+  if (a.mode != 3 && (a.overlap_tokens != 0 || a.ctx_tokens != 0))
+    return CheckResult::bad("overlap_tokens and ctx_tokens belong to CHUNK_HYBRID (0 otherwise)");
   switch (a.mode) {
     case 0: {  // FULL
       if (a.Lkv > 0 && !empty_q) {
@@ -304,7 +308,11 @@ inline CheckResult check_attn(const AttnArgs& a) {
     }
     case 3: {  // CHUNK_HYBRID
       if (a.chunk_tokens < 1) return CheckResult::bad("CHUNK_HYBRID needs chunk_tokens >= 1");
-      if (a.Lkv != a.Lq) return CheckResult::bad("CHUNK_HYBRID is self-attention: Lkv must equal Lq");
+      if (a.overlap_tokens < 0) return CheckResult::bad("overlap_tokens must be >= 0");
+      if (a.ctx_tokens < 0 || a.ctx_tokens > a.overlap_tokens)
+        return CheckResult::bad("ctx_tokens must lie in [0, overlap_tokens]");
+      if (a.Lkv != a.ctx_tokens + a.Lq)
+        return CheckResult::bad("CHUNK_HYBRID: Lkv must equal ctx_tokens + Lq");
       if (!a.state_s || !a.state_z) return CheckResult::bad("CHUNK_HYBRID needs state_s and state_z");
       if (!aligned16(a.state_s) || !aligned16(a.state_z))
         return CheckResult::bad("state buffers must be 16-byte aligned");

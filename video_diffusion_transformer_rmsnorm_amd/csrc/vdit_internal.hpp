@@ -41,9 +41,14 @@ struct AttnLaunch {
   float* part_lse;   // [B, Hq, Lq]
   int32_t has_prev;  // part_* hold the partial of the earlier chunks
   int32_t final_out; // write o / lse (else write part_*)
-  // chunk-hybrid (self-attention over q's own sequence, chunks of `chunk`)
+  // chunk-hybrid (self-attention over q's own sequence, chunks of `chunk`
+  // queries; chunk [c0, c1) attends with softmax to keys
+  // [max(0, hyb_ctx + c0 - hyb_overlap), hyb_ctx + c1) of hyb_lkv keys)
   int64_t chunk;
   int64_t n_chunks;
+  int64_t hyb_ctx;
+  int64_t hyb_overlap;
+  int64_t hyb_lkv;
   const void* st;    // per chunk state S_c^T [n_chunks][B][Hk][D][D]: bf16 hi,lo pairs or float32
   const float* zc;   // [n_chunks][B][Hk][D]
   const void* hk;    // key / value base of the whole sequence (hybrid)
@@ -145,11 +150,24 @@ struct HybridStateLaunch {
   float* dz;           // [n_chunks][nsplit][B][Hk][D]
   void* sc;            // per-chunk state, transposed, bf16 hi/lo pairs or float32
   float* zc;
-  int64_t L, chunk, n_chunks;
+  int64_t L, chunk, n_chunks;  // L: query tokens (chunks are defined on them)
+  int64_t Lkv, ctx, overlap;   // key tokens (= ctx + L), context keys, softmax overlap
   int32_t nsplit;
   int32_t B, Hk, D;
   int32_t dtype;       // of k, v; also selects the S_c format
 };
 hipError_t launch_hybrid_state(const HybridStateLaunch& p, hipStream_t s);
+
+// Keys whose phi(k) v^T the delta of chunk c adds to the running state: from
+// the start of chunk c's softmax window to the start of the next one (the
+// last chunk: to all keys but the last `overlap`, the next call's context).
+// The state before chunk c then covers every key before its window.
+__host__ __device__ inline void hybrid_delta_range(const HybridStateLaunch& p, int64_t c, int64_t* t0,
+                                                   int64_t* t1) {
+  const int64_t a = p.ctx + c * p.chunk - p.overlap;
+  const int64_t e = c + 1 < p.n_chunks ? p.ctx + (c + 1) * p.chunk - p.overlap : p.Lkv - p.overlap;
+  *t0 = a > 0 ? a : 0;
+  *t1 = e > 0 ? e : 0;
+}
 
 }  // namespace vdit

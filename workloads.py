@@ -66,6 +66,8 @@ class Workload:
     chunk_tokens: int = 0
     # rolling: per-head RMSNorm of keys and values, queries rotated only
     kv_norm: bool = False
+    # hybrid: keys before each chunk that join its softmax window
+    overlap_tokens: int = 0
 
     @property
     def tokens(self) -> int:
@@ -93,7 +95,21 @@ WORKLOADS = {
     # its temporal refinement: steps of r_t = 4 sub-frames, window 2 steps = 8 sub-frames
     7: Workload(7, "flashdecoder_xl_refine_720p_4x3600x2", "rolling", "bf16", (4, 45, 80), 24, 3, 64,
                 (12, 10, 10), n_slots=2, n_frames=6, kv_norm=True),
+    # the chunk-hybrid with MobileWan's chunk of T_c = 4 latent frames and a
+    # softmax overlap of T_o = 2 frames (390 tokens per frame)
+    8: Workload(8, "hybrid_overlap_12090_c4_o2", "hybrid", "bf16", (31, 15, 26), 24, 24, 128, (22, 21, 21),
+                chunk_tokens=4 * 390, overlap_tokens=2 * 390),
 }
+
+
+def hybrid_flops(w: "Workload") -> float:
+    """Matmul FLOPs of the chunk-hybrid's softmax part: each chunk's queries
+    against its window (its own keys plus the overlap before them)."""
+    total = 0.0
+    for c0 in range(0, w.tokens, w.chunk_tokens):
+        c1 = min(w.tokens, c0 + w.chunk_tokens)
+        total += flops_full(c1 - c0, c1 - max(0, c0 - w.overlap_tokens), w.heads, w.head_dim)
+    return total
 
 
 def flops_full(Lq: int, Lkv: int, heads: int, D: int, B: int = 1) -> float:
@@ -179,6 +195,6 @@ def ceil_div(a: int, b: int) -> int:
 
 __all__ = [
     "Workload", "WORKLOADS", "Tensor", "draw", "draw_qkv", "workload_inputs",
-    "f32_to_bf16_bits", "bf16_bits_to_f64", "flops_full", "sample_rows", "ceil_div",
+    "f32_to_bf16_bits", "bf16_bits_to_f64", "flops_full", "hybrid_flops", "sample_rows", "ceil_div",
 ]
 
