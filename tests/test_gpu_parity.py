@@ -293,6 +293,54 @@ def test_ring_small_with_empty_chunk(dtype):
     check(o, from_dev(of), dtype, "ring vs full (GPU)")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_batch_of_two_ring_rolling_hybrid(dtype):
+    # B = 2 in the modes whose tensors carry more than [B, L, H, D]: ring
+    # chunks, the batch-major rolling cache [B, n_slots, L, Hk, D], and the
+    # per-(batch, kv head) hybrid state; grouped-query heads throughout
+    D, Hq, Hk = (128, 4, 2) if dtype == "bf16" else (64, 4, 1)
+    log(f"batch of two: ring, rolling, hybrid {dtype} D={D} Hq={Hq} Hk={Hk}")
+    # ring
+    q = raw((2, 150, Hq, D), 141, dtype)
+    lens = [70, 91]
+    ks = [raw((2, n, Hk, D), 142 + i, dtype) for i, n in enumerate(lens)]
+    vs = [raw((2, n, Hk, D), 144 + i, dtype) for i, n in enumerate(lens)]
+    o, lse = V.vdit_attn_fwd(to_dev(q), mode="ring", k_chunks=[to_dev(x) for x in ks],
+                             v_chunks=[to_dev(x) for x in vs])
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, np.concatenate([x.values for x in ks], 1), np.concatenate([x.values for x in vs], 1))
+    check(o, wo, dtype, "O ring B=2"); check_lse(lse, wl, dtype, "LSE ring B=2")
+    # rolling: 4 frames through a 2-slot cache, frames handed in by the call
+    F, L, W = 4, 77, 2
+    qf = raw((F, 2, L, Hq, D), 151, dtype); kf = raw((F, 2, L, Hk, D), 152, dtype); vf = raw((F, 2, L, Hk, D), 153, dtype)
+    qd, kd, vd = to_dev(qf), to_dev(kf), to_dev(vf)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.zeros((2, W, L, Hk, D), dtype=dt, device="cuda"); vc = torch.zeros_like(kc)
+    for f in range(F):
+        o, lse = V.vdit_attn_fwd(qd[f].contiguous(), kd[f].contiguous(), vd[f].contiguous(), mode="rolling",
+                                 k_cache=kc, v_cache=vc, frame=f)
+        torch.cuda.synchronize()
+        win = list(O.rolling_window(f, W))
+        K = np.concatenate([kf.values[u] for u in win], 1); Vv = np.concatenate([vf.values[u] for u in win], 1)
+        wo, wl = O.attention(qf.values[f], K, Vv)
+        check(o, wo, dtype, f"O rolling B=2 frame {f}"); check_lse(lse, wl, dtype, f"LSE rolling B=2 frame {f}")
+    # hybrid with overlap and an incoming state
+    L, C, Ov = 180, 48, 24
+    q = raw((2, L, Hq, D), 161, dtype); k = raw((2, L, Hk, D), 162, dtype); v = raw((2, L, Hk, D), 163, dtype)
+    rng = np.random.default_rng(164)
+    s0 = (0.05 * rng.standard_normal((2, Hk, D, D))).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((2, Hk, D))).astype(np.float32)
+    sd = torch.from_numpy(s0).cuda(); zd = torch.from_numpy(z0).cuda()
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), mode="hybrid", chunk_tokens=C, state_s=sd,
+                             state_z=zd, overlap_tokens=Ov)
+    torch.cuda.synchronize()
+    wo, wl, ws_, wz = O.hybrid_recurrent(q.values, k.values, v.values, C, s0=s0, z0=z0, overlap=Ov)
+    check(o, wo, dtype, "O hybrid B=2"); check_lse(lse, wl, dtype, "LSE hybrid B=2")
+    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
+    rz = np.linalg.norm(from_dev(zd) - wz) / np.linalg.norm(wz)
+    assert rs <= 1e-5 and rz <= 1e-5, (rs, rz)
+
+
 @pytest.mark.slow
 def test_ring_shard_14b_sampled_rows():
     w = WL.WORKLOADS[3]
