@@ -149,7 +149,43 @@ def bench_full(args):
                      "traffic": measured_traffic(), "kernel": "attn_mfma_kernel<128,8,1>",
                      "algorithmic_flops_per_launch": flops},
     }
+    out["measured_peaks"] = measured_peaks(achieved, out["rope_GBps"])
     return out, w
+
+
+def measured_peaks(attn_tflops: float, rope_gbps: float, reps: int = 10):
+    """Reference rates measured on the same device after the timed region: a
+    bf16 library GEMM (8192^3, hipBLASLt) as the sustained dense-MFMA rate and
+    a 1 GiB device-to-device copy as the sustained HBM rate, with the
+    attention and RoPE rates as fractions of them (context for the nominal
+    peaks in `roofline`, not a replacement)."""
+    import torch
+    n = 8192
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"gemm_bf16_8192_TFLOPs": round(gemm, 1), "attn_frac_of_gemm": round(attn_tflops / gemm, 4),
+            "copy_1GiB_GBps": round(copy, 1), "rope_frac_of_copy": round(rope_gbps / copy, 4)}
 
 
 def bench_other(args):
