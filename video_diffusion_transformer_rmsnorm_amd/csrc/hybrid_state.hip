@@ -4,7 +4,12 @@
 // Sec. 3.2) runs the hybrid attention as an RNN over chunks whose fixed-size
 // state (s_t, z_t) summarises every earlier chunk through causal linear
 // attention: s += phi(K_c)^T V_c, z += sum_j phi(k_j) after chunk c, with
-// phi = elu + 1.  Chunk c's queries need the state *before* it, S_c.
+// phi = elu + 1.  Chunk c's queries need the state *before* it, S_c.  When
+// the softmax windows overlap (the window of chunk c starts `overlap` keys
+// before the chunk), S_c covers the keys before that window instead, so the
+// delta of chunk c runs from the start of its window to the start of the
+// next one (hybrid_delta_range) and the outgoing state leaves out the last
+// `overlap` keys, which the next call receives as context.
 //
 // Instead of a serial loop over chunks this is a two-pass scan:
 //  1. delta pass: every (chunk, token split, batch, kv head) workgroup forms
