@@ -145,7 +145,14 @@ def test_workspace_sizes(lib):
     lse_bytes = 10 * 15600 * 4
     align = lambda x: (x + 255) // 256 * 256
     bound = lambda B, Hk: align(B * Hk * 64 * 4)  # optional key-norm partials (bf16)
-    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes) + bound(1, 10)
+    # required running partial + a key-bound run per chunk + one partial per
+    # chunk for the one-launch form
+    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes) + align(2 * 10 * 64 * 4) + \
+        align(2 * o_bytes) + align(2 * lse_bytes)
+    a.dtype = 1  # float32: the fold form only, no key bound
+    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes)
+    a.dtype, a.n_kv_chunks = 0, 9  # more chunks than one launch takes: fold form
+    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes) + align(9 * 10 * 64 * 4)
     a.n_kv_chunks = 1
     assert V.vdit_attn_workspace_bytes(a) == bound(1, 10)
     w5 = WL.WORKLOADS[5]

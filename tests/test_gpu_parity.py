@@ -293,6 +293,35 @@ def test_ring_small_with_empty_chunk(dtype):
     check(o, from_dev(of), dtype, "ring vs full (GPU)")
 
 
+def test_ring_one_launch_and_fold_forms():
+    # bf16 rings of 2..8 chunks run in one launch (a float32 partial per chunk,
+    # then the split merge) when the workspace holds the partials, else one
+    # launch per chunk folded into the running partial; more chunks always fold
+    D, Hq, Hk = 128, 4, 2
+    log("ring: one-launch form vs fold form (4 chunks, one empty) and a 9-chunk ring")
+    q = raw((1, 300, Hq, D), 171, "bf16")
+    lens = [100, 0, 157, 65]
+    ks = [raw((1, n, Hk, D), 172 + i, "bf16") for i, n in enumerate(lens)]
+    vs = [raw((1, n, Hk, D), 182 + i, "bf16") for i, n in enumerate(lens)]
+    kd, vd = [to_dev(x) for x in ks], [to_dev(x) for x in vs]
+    align = lambda x: (x + 255) // 256 * 256
+    required = align(300 * Hq * D * 4) + align(Hq * 300 * 4)
+    o1, l1 = V.vdit_attn_fwd(to_dev(q), mode="ring", k_chunks=kd, v_chunks=vd)
+    o2, l2 = V.vdit_attn_fwd(to_dev(q), mode="ring", k_chunks=kd, v_chunks=vd,
+                             workspace=torch.empty(required, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, np.concatenate([x.values for x in ks], 1), np.concatenate([x.values for x in vs], 1))
+    check(o1, wo, "bf16", "O ring, one launch"); check_lse(l1, wl, "bf16", "LSE ring, one launch")
+    check(o2, wo, "bf16", "O ring, folded"); check_lse(l2, wl, "bf16", "LSE ring, folded")
+    lens9 = [37, 64, 0, 129, 5, 77, 64, 1, 90]
+    ks = [raw((1, n, Hk, D), 190 + i, "bf16") for i, n in enumerate(lens9)]
+    vs = [raw((1, n, Hk, D), 200 + i, "bf16") for i, n in enumerate(lens9)]
+    o9, l9 = V.vdit_attn_fwd(to_dev(q), mode="ring", k_chunks=[to_dev(x) for x in ks], v_chunks=[to_dev(x) for x in vs])
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, np.concatenate([x.values for x in ks], 1), np.concatenate([x.values for x in vs], 1))
+    check(o9, wo, "bf16", "O ring, 9 chunks"); check_lse(l9, wl, "bf16", "LSE ring, 9 chunks")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_batch_of_two_ring_rolling_hybrid(dtype):
     # B = 2 in the modes whose tensors carry more than [B, L, H, D]: ring

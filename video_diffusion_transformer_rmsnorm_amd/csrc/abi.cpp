@@ -12,6 +12,7 @@
 #include "vdit_internal.hpp"
 
 static_assert(sizeof(vdit_attn_args) == sizeof(vdit::AttnArgs), "vdit_attn_args layout mirror");
+static_assert(vdit::kRingOneLaunchMax <= vdit::kMaxSeg, "one ring launch: a segment per chunk");
 static_assert(vdit::kKeyBoundParts == vdit::kKeyBoundBlocks && vdit::kKeyBoundBlocks <= 64,
               "key-bound partials: one per lane of a wavefront");
 static_assert(offsetof(vdit_attn_args, workspace_bytes) == offsetof(vdit::AttnArgs, workspace_bytes),
@@ -240,9 +241,57 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       auto seg_of = [&](int c) -> vdit::KvSeg {
         return {a.k_chunks[c], a.v_chunks[c], a.chunk_len[c], a.chunk_len[c] * a.n_kv_heads * D};
       };
+      // workspace: [running partial (required)] [key bounds, one run per
+      // chunk] [one float32 partial per chunk (one-launch form)]
+      const size_t req = vdit::ring_workspace_bytes(a), kb = vdit::kbound_bytes(a);
+      const size_t run_floats = size_t(a.B) * size_t(a.n_kv_heads) * vdit::kKeyBoundParts;
       char* bound = nullptr;
-      if (auto st = optional_area(a, vdit::ring_workspace_bytes(a), vdit::kbound_bytes(a), &bound); st != VDIT_OK)
-        return st;
+      if (auto st = optional_area(a, req, kb, &bound); st != VDIT_OK) return st;
+      auto bound_run = [&](int c) -> char* { return bound ? bound + size_t(c) * run_floats * 4 : nullptr; };
+      char* parts = nullptr;
+      if (auto st = optional_area(a, req + kb, vdit::ring_partials_bytes(a), &parts); st != VDIT_OK) return st;
+      if (parts) {
+        // every chunk at once: split s of the launch attends to chunk s
+        vdit::AttnLaunch p = base_launch(a);
+        p.nseg = n;
+        bool all_keys = true;
+        for (int c = 0; c < n; ++c) {
+          p.seg[c] = seg_of(c);
+          all_keys = all_keys && a.chunk_len[c] > 0;
+        }
+        p.nsplit = n;
+        p.seg_split = 1;
+        p.epi = vdit::kEpiRing;  // each chunk writes its float32 partial
+        p.has_prev = 0;
+        p.final_out = 0;
+        p.part_o = reinterpret_cast<float*>(parts);
+        p.part_lse = reinterpret_cast<float*>(
+            parts + vdit::align256(size_t(n) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(D) * 4));
+        if (bound && all_keys && vdit::attn_uses_key_bound(p)) {
+          for (int c = 0; c < n; ++c)
+            if (auto st = from_hip(vdit::launch_key_bound(p.seg[c], p.B, p.Hk, p.D, 0,
+                                                          reinterpret_cast<float*>(bound_run(c)), stream),
+                                   "key bound launch");
+                st != VDIT_OK)
+              return st;
+          p.kbound = reinterpret_cast<const float*>(bound);
+          p.kbound_n = vdit::kKeyBoundBlocks;
+        }
+        if (auto st = from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(RING) launch"); st != VDIT_OK)
+          return st;
+        vdit::SplitMergeLaunch m;
+        m.part_o = p.part_o;
+        m.part_lse = p.part_lse;
+        m.o = a.o;
+        m.lse = a.lse;
+        m.L = a.Lq;
+        m.B = a.B;
+        m.H = a.n_heads;
+        m.D = a.head_dim;
+        m.nsplit = n;
+        m.out_dtype = a.dtype;
+        return from_hip(vdit::launch_split_merge(m, stream), "vdit_attn_fwd(RING) merge");
+      }
       if (n == 1) {
         vdit::AttnLaunch p = base_launch(a);
         if (a.chunk_len[0] > 0) {
@@ -261,7 +310,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         if (a.chunk_len[c] > 0) {
           p.nseg = 1;
           p.seg[0] = seg_of(c);
-          if (auto st = add_key_bound(p, p.seg[0], bound, stream); st != VDIT_OK) return st;
+          if (auto st = add_key_bound(p, p.seg[0], bound_run(c), stream); st != VDIT_OK) return st;
         }
         p.epi = vdit::kEpiRing;
         p.part_o = part_o;

@@ -169,12 +169,17 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     q_end = min(p.Lq, q_begin + BM);
     sg = p.seg[0];
     if (p.nseg == 0) sg.len = 0;
-    if (p.nsplit > 1) {  // keys [split * split_keys, +split_keys) of the segment
-      const int64_t k0 = split * p.split_keys;
-      const int64_t n = min(p.split_keys, sg.len - k0);
-      sg.k = static_cast<const uint16_t*>(sg.k) + k0 * p.Hk * D;
-      sg.v = static_cast<const uint16_t*>(sg.v) + k0 * p.Hk * D;
-      sg.len = n > 0 ? n : 0;
+    if (p.nsplit > 1) {
+      if (p.seg_split) {  // split s attends to key segment s (a ring chunk), with its own key bound
+        sg = p.seg[split];
+        chunk_id = split;
+      } else {  // keys [split * split_keys, +split_keys) of the segment
+        const int64_t k0 = split * p.split_keys;
+        const int64_t n = min(p.split_keys, sg.len - k0);
+        sg.k = static_cast<const uint16_t*>(sg.k) + k0 * p.Hk * D;
+        sg.v = static_cast<const uint16_t*>(sg.v) + k0 * p.Hk * D;
+        sg.len = n > 0 ? n : 0;
+      }
       part_o += split * (int64_t(p.B) * p.Lq * p.Hq * D);
       part_lse += split * (int64_t(p.B) * p.Hq * p.Lq);
     }

@@ -332,12 +332,14 @@ inline CheckResult check_attn(const AttnArgs& a) {
 }
 
 // Key-norm bound of the bounded-score softmax (bf16): 64 partial maxima per
-// (batch, kv head), and per chunk in the chunk-hybrid mode.  Optional in
-// every mode.
+// (batch, kv head), and per chunk in the chunk-hybrid and ring modes.
+// Optional in every mode.
 constexpr int kKeyBoundParts = 64;
 inline size_t kbound_bytes(const AttnArgs& a) {
   if (a.dtype != 0) return 0;
-  const size_t runs = a.mode == 3 ? size_t(hybrid_layout(a).n_chunks) : 1;
+  const size_t runs = a.mode == 3   ? size_t(hybrid_layout(a).n_chunks)
+                      : a.mode == 1 ? size_t(a.n_kv_chunks > 1 ? a.n_kv_chunks : 1)
+                                    : 1;
   return align256(runs * size_t(a.B) * size_t(a.n_kv_heads) * kKeyBoundParts * 4);
 }
 
@@ -355,11 +357,28 @@ inline size_t attn_required_bytes(const AttnArgs& a) {
 // part, then the key-norm bound, then (FULL, ROLLING) the key-split
 // partials.  Everything past the required part is optional and used when
 // the workspace holds it.
+// RING (bf16, 2..kRingOneLaunchMax chunks) in one launch: every chunk's float32
+// partial at once (work items chunk x query tile x head, so the last round
+// of workgroups is less empty than with one launch per chunk), then the
+// split merge.  Optional: without room for the partials the chunks are
+// folded one launch at a time into the required running partial.
+constexpr int kRingOneLaunchMax = 8;  // key segments one attention launch takes
+inline bool ring_one_launch(const AttnArgs& a) {
+  return a.mode == 1 && a.dtype == 0 && a.n_kv_chunks >= 2 && a.n_kv_chunks <= kRingOneLaunchMax;
+}
+inline size_t ring_partials_bytes(const AttnArgs& a) {
+  if (!ring_one_launch(a)) return 0;
+  SplitPlan s;
+  s.nsplit = a.n_kv_chunks;
+  return split_workspace_bytes(s, a.B, a.Lq, a.n_heads, a.head_dim);
+}
+
 inline size_t attn_workspace_bytes(const AttnArgs& a, int cus) {
   size_t n = attn_required_bytes(a) + kbound_bytes(a);
   if (a.mode == 0 || a.mode == 2)
     n += split_workspace_bytes(split_plan(a.dtype, a.B, a.Lq, a.n_heads, attn_keys(a), cus), a.B, a.Lq,
                                a.n_heads, a.head_dim);
+  n += ring_partials_bytes(a);
   return n;
 }
 

@@ -57,9 +57,11 @@ struct AttnLaunch {
   // writes its partial to part_o / part_lse offset by s whole partials
   int32_t nsplit;
   int64_t split_keys;
+  int32_t seg_split;  // 1: split s attends to the whole segment seg[s] (nsplit <= nseg)
   // bounded-score softmax: kbound[((r * B + b) * Hk + hk) * kbound_n + i]
   // are partial maxima of the squared norms of the keys a workgroup attends
-  // to (r: its hybrid chunk, else 0); NULL: online maximum
+  // to (r: its hybrid chunk, or its segment under seg_split, else 0); NULL:
+  // online maximum
   const float* kbound;
   int32_t kbound_n;
 };
