@@ -692,6 +692,82 @@ def test_hybrid_5b_full():
     assert rs <= 1e-2
 
 
+# ------------------------------------------------------------ randomised --
+
+def _random_case(i):
+    """Seeded configuration i: mode, dtype, head dim, GQA ratio and ragged sizes."""
+    r = np.random.default_rng(5000 + i)
+    mode = ["full", "ring", "rolling", "hybrid"][i % 4]
+    dtype = "bf16" if r.random() < 0.75 else "f32"
+    D = int(r.choice([64, 128]))
+    Hk = int(r.choice([1, 2, 3]))
+    Hq = Hk * int(r.choice([1, 2, 4, 8]))
+    return r, mode, dtype, D, Hq, Hk
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_randomised_configurations(i):
+    r, mode, dtype, D, Hq, Hk = _random_case(i)
+    B = int(r.choice([1, 2]))
+    seed = 6000 + 10 * i
+    if mode == "full":
+        Lq, Lkv = int(r.integers(1, 700)), int(r.integers(0, 1500))
+        log(f"random {i}: full {dtype} D={D} B={B} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+        q = raw((B, Lq, Hq, D), seed, dtype); k = raw((B, Lkv, Hk, D), seed + 1, dtype); v = raw((B, Lkv, Hk, D), seed + 2, dtype)
+        kd = to_dev(k) if Lkv else torch.empty((B, 0, Hk, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+        vd = to_dev(v) if Lkv else kd
+        o, lse = V.vdit_attn_fwd(to_dev(q), kd, vd)
+        torch.cuda.synchronize()
+        if Lkv == 0:
+            assert (from_dev(o) == 0).all() and np.isneginf(from_dev(lse)).all()
+            return
+        wo, wl = O.attention(q.values, k.values, v.values)
+    elif mode == "ring":
+        Lq = int(r.integers(1, 500))
+        lens = [int(x) for x in r.integers(0, 300, size=int(r.integers(1, 11)))]
+        lens[int(r.integers(0, len(lens)))] = max(1, lens[0])  # at least one non-empty chunk
+        log(f"random {i}: ring {dtype} D={D} B={B} Lq={Lq} chunks={lens} Hq={Hq} Hk={Hk}")
+        q = raw((B, Lq, Hq, D), seed, dtype)
+        ks = [raw((B, n, Hk, D), seed + 1 + c, dtype) for c, n in enumerate(lens)]
+        vs = [raw((B, n, Hk, D), seed + 50 + c, dtype) for c, n in enumerate(lens)]
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        dev = lambda t, n: to_dev(t) if n else torch.empty((B, 0, Hk, D), dtype=dt, device="cuda")
+        o, lse = V.vdit_attn_fwd(to_dev(q), mode="ring", k_chunks=[dev(x, n) for x, n in zip(ks, lens)],
+                                 v_chunks=[dev(x, n) for x, n in zip(vs, lens)])
+        torch.cuda.synchronize()
+        wo, wl = O.attention(q.values, np.concatenate([x.values for x in ks], 1), np.concatenate([x.values for x in vs], 1))
+    elif mode == "rolling":
+        L, W, F = int(r.integers(8, 300)), int(r.integers(1, 5)), int(r.integers(1, 7))
+        log(f"random {i}: rolling {dtype} D={D} B={B} L={L} slots={W} frames={F} Hq={Hq} Hk={Hk}")
+        qf = raw((F, B, L, Hq, D), seed, dtype); kf = raw((F, B, L, Hk, D), seed + 1, dtype); vf = raw((F, B, L, Hk, D), seed + 2, dtype)
+        qd, kd, vd = to_dev(qf), to_dev(kf), to_dev(vf)
+        kc = torch.zeros((B, W, L, Hk, D), dtype=qd.dtype, device="cuda"); vc = torch.zeros_like(kc)
+        for f in range(F):
+            o, lse = V.vdit_attn_fwd(qd[f].contiguous(), kd[f].contiguous(), vd[f].contiguous(), mode="rolling",
+                                     k_cache=kc, v_cache=vc, frame=f)
+        torch.cuda.synchronize()
+        win = list(O.rolling_window(F - 1, W))
+        wo, wl = O.attention(qf.values[F - 1], np.concatenate([kf.values[u] for u in win], 1),
+                             np.concatenate([vf.values[u] for u in win], 1))
+    else:
+        L, C = int(r.integers(1, 400)), int(r.integers(1, 150))
+        Ov = int(r.choice([0, int(r.integers(1, 2 * C))]))
+        ctx = int(r.integers(0, Ov + 1))
+        log(f"random {i}: hybrid {dtype} D={D} B={B} L={L} chunk={C} overlap={Ov} ctx={ctx} Hq={Hq} Hk={Hk}")
+        q = raw((B, L, Hq, D), seed, dtype); k = raw((B, ctx + L, Hk, D), seed + 1, dtype); v = raw((B, ctx + L, Hk, D), seed + 2, dtype)
+        s0 = (0.05 * r.standard_normal((B, Hk, D, D))).astype(np.float32)
+        z0 = np.abs(r.standard_normal((B, Hk, D))).astype(np.float32)
+        sd = torch.from_numpy(s0).cuda(); zd = torch.from_numpy(z0).cuda()
+        o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), mode="hybrid", chunk_tokens=C, state_s=sd,
+                                 state_z=zd, overlap_tokens=Ov, ctx_tokens=ctx)
+        torch.cuda.synchronize()
+        wo, wl, ws_, wz = O.hybrid_explicit(q.values, k.values, v.values, C, s0=s0, z0=z0, overlap=Ov, ctx=ctx)
+        rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
+        assert rs <= 1e-5, rs
+    check(o, wo, dtype, f"O random {i}")
+    check_lse(lse, wl, dtype, f"LSE random {i}")
+
+
 # ----------------------------------------------------------------- errors --
 
 def test_invalid_arguments_raise():
