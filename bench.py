@@ -118,8 +118,10 @@ def bench_full(args):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    rope_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    rope_each = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_each = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    rope_ms = sum(rope_each) / args.steps
+    attn_ms = sum(attn_each) / args.steps
     ms_step = wall * 1e3 / args.steps
     flops = WL.flops_full(w.tokens, w.tokens, w.heads, w.head_dim)
     rope_bytes = 2 * 2 * w.tokens * w.heads * w.head_dim * 2  # q,k read + write, bf16
@@ -141,6 +143,8 @@ def bench_full(args):
                    "head_dim": w.head_dim, "rope_pairs": list(w.pairs), "mode": "full",
                    "step": "rmsnorm+3d_rope(q,k) -> full attention", "parallelism": "none (1 GPU)"},
         "attn_ms": round(attn_ms, 4),
+        "attn_ms_median": round(attn_each[len(attn_each) // 2], 4),
+        "attn_ms_min": round(attn_each[0], 4),
         "rope_ms": round(rope_ms, 4),
         "pct_bf16_peak_step": round(100 * flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "rope_GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
@@ -334,8 +338,8 @@ def traffic_from(run_root: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the oracle's timed sample")
