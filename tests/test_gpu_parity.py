@@ -5,6 +5,9 @@ Inputs come from the seeded generators in ``workloads``; expected values from
 full-size workloads are checked on seeded samples of query rows (each row
 against every key) in the launch configuration the benchmark times.
 """
+import os
+import subprocess
+
 import numpy as np
 import pytest
 import torch
@@ -690,6 +693,37 @@ def test_hybrid_5b_full():
     # the oracle's rotated k is unrounded float64 while the library's k is the
     # bf16-rounded output of vdit_rope_qk: the state inherits that rounding
     assert rs <= 1e-2
+
+
+# -------------------------------------------------------- C consumer ------
+
+def test_c_abi_consumer_program(tmp_path):
+    # tests/host/c_consumer.c uses the library as a C program would (hipMalloc,
+    # its own stream, workspace from vdit_attn_workspace_bytes, statuses):
+    # RMSNorm + 3D-RoPE, FULL and a two-chunk RING, checked against the oracle
+    from video_diffusion_transformer_rmsnorm_amd import build as B
+    if not os.path.exists(B.CONSUMER):
+        pytest.fail(f"{B.CONSUMER} is not built (run __graft_entry__.build())")
+    grid, pairs, Hq, Hk, D, split = (3, 10, 17), (22, 21, 21), 4, 2, 128, 200
+    L = grid[0] * grid[1] * grid[2]
+    log(f"C consumer: L={L} Hq={Hq} Hk={Hk} D={D}, ring split at {split}")
+    rng = np.random.default_rng(211)
+    q = WL.draw((1, L, Hq, D), rng, "bf16"); k = WL.draw((1, L, Hk, D), rng, "bf16"); v = WL.draw((1, L, Hk, D), rng, "bf16")
+    for name, t in (("q.bin", q), ("k.bin", k), ("v.bin", v)):
+        np.ascontiguousarray(t.bits).tofile(str(tmp_path / name))
+    (tmp_path / "meta.txt").write_text(f"{L} {Hq} {Hk} {D} {grid[0]} {grid[1]} {grid[2]} {pairs[0]} {pairs[1]} {pairs[2]} {split}\n")
+    r = subprocess.run([B.CONSUMER, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c_consumer ok" in r.stdout, r.stdout + r.stderr
+    bf = lambda name, shape: WL.bf16_bits_to_f64(np.fromfile(str(tmp_path / name), dtype=np.uint16)).reshape(shape)
+    f32 = lambda name, shape: np.fromfile(str(tmp_path / name), dtype=np.float32).astype(np.float64).reshape(shape)
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs)
+    check(bf("qr.bin", (1, L, Hq, D)), wq, "bf16", "q rotated (C)")
+    check(bf("kr.bin", (1, L, Hk, D)), wk, "bf16", "k rotated (C)")
+    wo, wl = O.attention(wq, wk, v.values)
+    check(bf("o_full.bin", (1, L, Hq, D)), wo, "bf16", "O full (C)")
+    check_lse(f32("lse_full.bin", (1, Hq, L)), wl, "bf16", "LSE full (C)")
+    check(bf("o_ring.bin", (1, L, Hq, D)), wo, "bf16", "O ring (C)")
+    check_lse(f32("lse_ring.bin", (1, Hq, L)), wl, "bf16", "LSE ring (C)")
 
 
 # ------------------------------------------------------------ randomised --

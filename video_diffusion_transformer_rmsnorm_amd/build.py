@@ -64,5 +64,30 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+CONSUMER_SRC = os.path.join(ROOT, "tests", "host", "c_consumer.c")
+CONSUMER = os.path.join(ROOT, "tests", "host", "c_consumer")
+
+
+def build_consumer(verbose: bool = False) -> str:
+    """Compile the plain C test program that links libvdit.so (the C ABI
+    used without Python); returns its path.  The library must be built."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    rel = os.path.relpath(PKG, os.path.dirname(CONSUMER))
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), CONSUMER_SRC, "-o", CONSUMER, "-L", PKG, "-lvdit",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,$ORIGIN/{rel}",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {CONSUMER}")
+    return CONSUMER
+
+
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_consumer(verbose=True)
