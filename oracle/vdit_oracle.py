@@ -6,6 +6,12 @@ shares no code with it: this file uses numpy only and writes every step as
 its plain mathematical definition, in float64, with no tiling, online softmax
 or fusion.
 
+How it is pinned (tests/test_oracle_pins.py): every function is checked
+against something other than itself -- closed forms, invariances the pages
+state, brute-force loops on tiny inputs, hand-derived rotations and torch
+float64 attention.  Against the pages themselves parity is unpinned: no page
+prints a worked numerical example to compare with.
+
 Layouts follow the library: q, k, v, o are ``[B, L, H, D]`` row-major;
 log-sum-exp values are ``[B, H, L]``; linear-attention state is ``s [B, Hk, D, D]``
 (index order: feature of phi(k), value channel) and ``z [B, Hk, D]``.
