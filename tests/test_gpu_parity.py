@@ -695,6 +695,54 @@ def test_hybrid_5b_full():
     assert rs <= 1e-2
 
 
+# ----------------------------------------------------------- graphs ------
+
+def test_graph_capture_replays_equal_eager():
+    # The library neither allocates, synchronises nor issues memsets, so its
+    # calls can be captured: FULL with the key split (several kernels), the
+    # one-launch RING and the hybrid with overlap (state reset by a fill
+    # kernel inside the graph).  Every replay, with eager work between them,
+    # must equal the eager results bit for bit (no atomics anywhere).
+    log("graph capture: FULL (split), RING (one launch), hybrid (overlap), 3 replays")
+    qf = to_dev(raw((1, 1000, 2, 128), 221, "bf16"))
+    kf = to_dev(raw((1, 5000, 1, 128), 222, "bf16")); vf = to_dev(raw((1, 5000, 1, 128), 223, "bf16"))
+    kc = [to_dev(raw((1, n, 2, 64), 224 + i, "bf16")) for i, n in enumerate((300, 450))]
+    vc = [to_dev(raw((1, n, 2, 64), 226 + i, "bf16")) for i, n in enumerate((300, 450))]
+    qr = to_dev(raw((1, 700, 4, 64), 228, "bf16"))
+    qh = to_dev(raw((1, 260, 2, 128), 229, "bf16"))
+    kh = to_dev(raw((1, 260, 2, 128), 230, "bf16")); vh = to_dev(raw((1, 260, 2, 128), 231, "bf16"))
+    sd = torch.zeros((1, 2, 128, 128), device="cuda"); zd = torch.zeros((1, 2, 128), device="cuda")
+
+    def run():
+        o1, l1 = V.vdit_attn_fwd(qf, kf, vf)
+        o2, l2 = V.vdit_attn_fwd(qr, mode="ring", k_chunks=kc, v_chunks=vc)
+        sd.zero_(); zd.zero_()
+        o3, l3 = V.vdit_attn_fwd(qh, kh, vh, mode="hybrid", chunk_tokens=64, state_s=sd, state_z=zd,
+                                 overlap_tokens=32)
+        return [o1, l1, o2, l2, o3, l3, sd, zd]
+
+    eager = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    for rep in range(3):
+        V.vdit_attn_fwd(qf, kf, vf)  # eager work between replays
+        torch.cuda.synchronize()
+        for t in outs:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), (rep, j, float((a.float() - b.float()).abs().max()))
+
+
 # -------------------------------------------------------- C consumer ------
 
 def test_c_abi_consumer_program(tmp_path):
