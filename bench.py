@@ -262,13 +262,18 @@ def bench_other(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e in evs:
+        e[0].record()
         step()
+        e[1].record()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    each = sorted(a.elapsed_time(b) for a, b in evs)
     return {"metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "step_ms_median": round(each[len(each) // 2], 4), "step_ms_min": round(each[0], 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
             "data": "synthetic", "config": {"workload": w.name, "mode": w.mode, "tokens": w.tokens,
                                             "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
