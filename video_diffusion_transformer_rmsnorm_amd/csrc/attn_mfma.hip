@@ -115,6 +115,19 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// PV step at which the exponentials of the k-th of npb pairs moved among the
+// PV MFMAs are issued (packed one step later), spread over the steps before
+// the first one that reads the last pair (3 * db of 4 * db).
+__host__ __device__ constexpr int pv_pair_step(int k, int npb, int db) { return (k * (3 * db - 1)) / npb; }
+// Every moved pair is packed before its first reader: the pairs of the third
+// quarter of P (the first npb - 4 moved, if any) by PV step 2 * db, the rest
+// by step 3 * db.
+__host__ __device__ constexpr bool pv_pairs_in_time(int npb, int db) {
+  for (int k = 0; k < npb; ++k)
+    if (pv_pair_step(k, npb, db) + 1 >= (k < npb - 4 ? 2 * db : 3 * db)) return false;
+  return true;
+}
+
 // QB blocks of 32 queries per wavefront.  QB = 1: two wavefronts per SIMD
 // (<= 256 registers each); QB = 2: one wavefront per SIMD with 512 registers,
 // every K / V^T operand read from LDS feeding two MFMAs (half the LDS traffic
@@ -471,10 +484,12 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // order and pinned with scheduling fences after every MFMA step, so it does
   // not depend on the scheduler's pattern matching.  Region A: step st issues
   // the K operand read for step st + KPREF, the MFMA(s) of step st, and its
-  // share of this tile's exponentials (pairs packed to bf16 as they finish,
-  // their sum folded into a running total).  Region B: step st issues the
-  // transposed V reads for step st + VPREF, the PV MFMA(s) of step st and a
-  // slice of the next tile's lane maximum.
+  // share of this tile's exponentials; each pair of exponentials is packed to
+  // bf16 and added to a running total one step after it is issued, so the
+  // transcendental latency passes under the next MFMA instead of stalling the
+  // wavefront.  Region B: step st issues the transposed V reads for step
+  // st + VPREF, the PV MFMA(s) of step st and a slice of the next tile's lane
+  // maximum.
   // Exponential pairs (2 scores, one packed bf16 pair of P) of this tile:
   // pairs [0, NPA) go to region A, spread evenly over its MFMA steps; the
   // last NPB pairs (second key half) to region B, each placed before the
@@ -484,16 +499,26 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   constexpr int NPA = NPAIR - NPB;
   static_assert(NPB >= 0 && NPB <= 8, "pairs moved to region B");
   float run[QB];
-  // p for pair pr of query block ... -> P, running sum.  Bounded-score
+  // p of pair pr (2 scores of one query block) into pe.  Bounded-score
   // wavefronts hold scores already in log2 units (Q pre-scaled by c2, no
   // shift): p = 2^s straight from the accumulator.
-  auto exp_pair = [&](int pr, f32x16 (*S)[QB], bf16x8 (*P)[QB][2], auto fastc) {
+  float pe[NPAIR][2];
+  auto exp_issue = [&](int pr, f32x16 (*S)[QB], auto fastc) {
     constexpr bool FAST = decltype(fastc)::value;
+    const int el = 2 * pr;
+    const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15;
+    const float x0 = S[kb2][qb][i], x1 = S[kb2][qb][i + 1];
+    pe[pr][0] = fast_exp2(FAST ? x0 : fmaf(x0, c2, -m2[qb]));
+    pe[pr][1] = fast_exp2(FAST ? x1 : fmaf(x1, c2, -m2[qb]));
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(pe[pr][0]), "+v"(pe[pr][1]));
+#endif
+  };
+  // pe of pair pr -> its bf16 pair in P, and into the running sum
+  auto exp_finish = [&](int pr, bf16x8 (*P)[QB][2]) {
     const int el = 2 * pr;  // (qb, kb, hh, j) in that order
     const int qb = el >> 5, kb2 = (el >> 4) & 1, i = el & 15, hh = i >> 3, j = i & 7;
-    const float x0 = S[kb2][qb][i], x1 = S[kb2][qb][i + 1];
-    const float e0 = fast_exp2(FAST ? x0 : fmaf(x0, c2, -m2[qb]));
-    const float e1 = fast_exp2(FAST ? x1 : fmaf(x1, c2, -m2[qb]));
+    const float e0 = pe[pr][0], e1 = pe[pr][1];
     const __bf16 b0 = static_cast<__bf16>(e0), b1 = static_cast<__bf16>(e1);
     P[kb2][qb][hh][j] = b0;
     P[kb2][qb][hh][j + 1] = b1;
@@ -536,9 +561,15 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
         Sn[st & 1][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], Qr[qb][st >> 1], Sn[st & 1][qb], 0, 0, 0);
 #pragma unroll
       for (int pr = 0; pr < NPA; ++pr)
-        if ((pr * NSTEP) / NPA == st) exp_pair(pr, S, P, fastc);
+        if (st > 0 && (pr * NSTEP) / NPA == st - 1) exp_finish(pr, P);
+#pragma unroll
+      for (int pr = 0; pr < NPA; ++pr)
+        if ((pr * NSTEP) / NPA == st) exp_issue(pr, S, fastc);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int pr = 0; pr < NPA; ++pr)
+      if ((pr * NSTEP) / NPA == NSTEP - 1) exp_finish(pr, P);
   };
   auto region_b = [&](int buf, f32x16 (*S)[QB], bf16x8 (*P)[QB][2], f32x16 (*Sn)[QB], float* mx, auto domaxc) {
     constexpr bool DOMAX = decltype(domaxc)::value;
@@ -546,6 +577,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     constexpr int PER = 32 / NSTEP;  // scores of one query block folded into the max per step
     constexpr int VP = VDIT_ATTN_VPREF < NSTEP ? VDIT_ATTN_VPREF : NSTEP;
     constexpr int LASTB = 3 * DB;    // first PV step that reads the last pair
+    // second-half pair NPA + k: exponentials issued at step bstep(k), packed
+    // at bstep(k) + 1, which comes before its first reader (PV step 2 * DB
+    // for the first quarter, 3 * DB after; a step issues its MFMA first)
+    auto bstep = [](int k) { return pv_pair_step(k, NPB, DB); };
+    static_assert(pv_pairs_in_time(NPB, DB), "an exponential pair packed after its PV reader");
     const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
     i16x8 va[NSTEP];
     auto vread = [&](int st) {
@@ -567,11 +603,12 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       for (int qb = 0; qb < QB; ++qb)
         O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[st]), P[kk >> 1][qb][kk & 1],
                                                             O[db][qb], 0, 0, 0);
-      // second-half pairs: pair NPA + k at step k * LASTB / NPB, before its
-      // first reader (PV step 2 * DB for the first quarter, 3 * DB after)
 #pragma unroll
       for (int k = 0; k < NPB; ++k)
-        if ((k * LASTB) / NPB == st) exp_pair(NPA + k, S, P, std::integral_constant<bool, !DOMAX>{});
+        if (st > 0 && bstep(k) == st - 1) exp_finish(NPA + k, P);
+#pragma unroll
+      for (int k = 0; k < NPB; ++k)
+        if (bstep(k) == st) exp_issue(NPA + k, S, std::integral_constant<bool, !DOMAX>{});
       if constexpr (DOMAX) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
