@@ -60,6 +60,9 @@
 #ifndef VDIT_ATTN_DOT2
 #define VDIT_ATTN_DOT2 0  // row sums by v_dot2_f32_bf16 over the packed bf16 p (slower: a serial accumulate)
 #endif
+#ifndef VDIT_ATTN_VEARLY
+#define VDIT_ATTN_VEARLY 4  // region A steps (from its end) over which the first V^T reads of region B are issued
+#endif
 #ifndef VDIT_ATTN_KPREF
 #define VDIT_ATTN_KPREF 3  // K operand reads issued ahead of their MFMA
 #endif
@@ -487,9 +490,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // share of this tile's exponentials; each pair of exponentials is packed to
   // bf16 and added to a running total one step after it is issued, so the
   // transcendental latency passes under the next MFMA instead of stalling the
-  // wavefront.  Region B: step st issues the transposed V reads for step
-  // st + VPREF, the PV MFMA(s) of step st and a slice of the next tile's lane
-  // maximum.
+  // wavefront; its last VEARLY steps also issue the first VPREF transposed V
+  // reads of region B (the V tile is complete since the previous barrier), so
+  // region B starts without waiting on LDS.  Region B: step st issues the
+  // transposed V reads for step st + VPREF, the PV MFMA(s) of step st and a
+  // slice of the next tile's lane maximum.
   // Exponential pairs (2 scores, one packed bf16 pair of P) of this tile:
   // pairs [0, NPA) go to region A, spread evenly over its MFMA steps; the
   // last NPB pairs (second key half) to region B, each placed before the
@@ -534,7 +539,17 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     asm volatile("" : "+v"(run[qb]));  // keep the sum in this step (no sinking)
 #endif
   };
-  auto region_a = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2], auto fastc) {
+  constexpr int VPB = 4 * DB;
+  constexpr int VP = VDIT_ATTN_VPREF < VPB ? VDIT_ATTN_VPREF : VPB;
+  static_assert(VDIT_ATTN_VEARLY >= 1 && VDIT_ATTN_VEARLY <= 2 * KS, "early V^T reads within region A");
+  auto vread_buf = [&](int vbuf, int st) {
+    const char* Vl = lds + 2 * KTILE_B + vbuf * TILE_B;
+    const int kk = st / DB, db = st % DB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk) * ROWB));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk + 4) * ROWB));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto region_a = [&](int buf, f32x16 (*Sn)[QB], f32x16 (*S)[QB], bf16x8 (*P)[QB][2], auto fastc, int vbuf, i16x8* vpre) {
     constexpr int NSTEP = 2 * KS;
     constexpr int KP = VDIT_ATTN_KPREF < NSTEP ? VDIT_ATTN_KPREF : NSTEP;
     const char* Kl = lds + buf * KTILE_B + kaddr;
@@ -565,33 +580,30 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
       for (int pr = 0; pr < NPA; ++pr)
         if ((pr * NSTEP) / NPA == st) exp_issue(pr, S, fastc);
+      // the first V^T operands of region B
+#pragma unroll
+      for (int v = 0; v < VP; ++v)
+        if (st == NSTEP - VDIT_ATTN_VEARLY + v * VDIT_ATTN_VEARLY / VP) vpre[v] = vread_buf(vbuf, v);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int pr = 0; pr < NPA; ++pr)
       if ((pr * NSTEP) / NPA == NSTEP - 1) exp_finish(pr, P);
   };
-  auto region_b = [&](int buf, f32x16 (*S)[QB], bf16x8 (*P)[QB][2], f32x16 (*Sn)[QB], float* mx, auto domaxc) {
+  auto region_b = [&](int buf, f32x16 (*S)[QB], bf16x8 (*P)[QB][2], f32x16 (*Sn)[QB], float* mx, auto domaxc, const i16x8* vpre) {
     constexpr bool DOMAX = decltype(domaxc)::value;
     constexpr int NSTEP = 4 * DB;
     constexpr int PER = 32 / NSTEP;  // scores of one query block folded into the max per step
-    constexpr int VP = VDIT_ATTN_VPREF < NSTEP ? VDIT_ATTN_VPREF : NSTEP;
     constexpr int LASTB = 3 * DB;    // first PV step that reads the last pair
     // second-half pair NPA + k: exponentials issued at step bstep(k), packed
     // at bstep(k) + 1, which comes before its first reader (PV step 2 * DB
     // for the first quarter, 3 * DB after; a step issues its MFMA first)
     auto bstep = [](int k) { return pv_pair_step(k, NPB, DB); };
     static_assert(pv_pairs_in_time(NPB, DB), "an exponential pair packed after its PV reader");
-    const char* Vl = lds + 2 * KTILE_B + buf * TILE_B;
     i16x8 va[NSTEP];
-    auto vread = [&](int st) {
-      const int kk = st / DB, db = st % DB;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk) * ROWB));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vl + vaddr[db] + (16 * kk + 4) * ROWB));
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
+    auto vread = [&](int st) { return vread_buf(buf, st); };
 #pragma unroll
-    for (int st = 0; st < VP; ++st) va[st] = vread(st);
+    for (int st = 0; st < VP; ++st) va[st] = vpre[st];
     float m[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m[qb] = -INFINITY;
@@ -664,9 +676,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       f32x16 Sn[2][QB];
       bf16x8 P[2][QB][2];
       __builtin_amdgcn_sched_barrier(0);
-      region_a(1 - P0, Sn, S, P, fastc);
+      i16x8 vpre[VP];
+      region_a(1 - P0, Sn, S, P, fastc, P0, vpre);
       // region B: O^T += V^T P^T || lane max of tile t+1's scores
-      region_b(P0, S, P, Sn, mx, std::integral_constant<bool, !FAST>{});
+      region_b(P0, S, P, Sn, mx, std::integral_constant<bool, !FAST>{}, vpre);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
