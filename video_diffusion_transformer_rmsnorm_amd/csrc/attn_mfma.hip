@@ -20,7 +20,7 @@
 //    (bits 2 and 3 of the row index swapped) so that accumulator registers
 //    8h..8h+7 of a lane hold 8 consecutive keys: converted to bf16 they are
 //    directly the B operand of O^T = V^T P^T.
-//  * K/V tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4
+//  * K/V tiles of 64 keys move HBM -> LDS with buffer_load_dwordx4 ... lds
 //    (no staging registers, no LDS store instructions).  Each 16-byte chunk
 //    of a row is placed at an XOR-swizzled position chosen by the source
 //    address, so the operand reads are bank-conflict free.  V stays
@@ -31,7 +31,10 @@
 //    cores compute S^T of tile j+1, then O^T += V_j^T P_j^T; K_{j+2} and
 //    V_{j+1} stream into the free buffers meanwhile.  One barrier per tile.
 //    Two wavefronts share each SIMD (<= 256 VGPRs), so one's exp/max work
-//    overlaps the other's matrix products.
+//    overlaps the other's matrix products; within a wavefront, exponentials
+//    are packed one MFMA step after they are issued and the first V^T reads
+//    of a tile are issued before its PV products start, so neither the
+//    transcendental nor the LDS latency stalls the wavefront.
 //  * Bounded-score softmax where a key-norm pre-pass bounds every score of
 //    the wavefront's queries: p = 2^(c2 s) needs no running maximum, and
 //    with Q pre-scaled by c2 the exponent comes straight from the MFMA
