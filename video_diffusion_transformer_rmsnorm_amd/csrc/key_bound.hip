@@ -16,7 +16,7 @@
 namespace vdit {
 namespace {
 
-constexpr int kBoundThreads = 256;
+constexpr int kBoundThreads = 1024;  // 16 wavefronts: more loads in flight per CU (64 workgroups per head)
 
 template <int D>
 __global__ __launch_bounds__(kBoundThreads) void key_bound_kernel(KvSeg seg, int32_t B, int32_t Hk, int64_t part_len,
