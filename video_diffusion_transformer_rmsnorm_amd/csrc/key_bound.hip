@@ -16,13 +16,13 @@
 namespace vdit {
 namespace {
 
-constexpr int kBoundThreads = 1024;  // 16 wavefronts: more loads in flight per CU (64 workgroups per head)
-
-template <int D>
-__global__ __launch_bounds__(kBoundThreads) void key_bound_kernel(KvSeg seg, int32_t B, int32_t Hk, int64_t part_len,
-                                                                  float* out) {
+// NT threads per workgroup: 1024 (more loads in flight per CU) when each
+// workgroup has at least 192 keys to reduce (64 workgroups per run), else
+// 256.
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void key_bound_kernel(KvSeg seg, int32_t B, int32_t Hk, int64_t part_len, float* out) {
   constexpr int TPR = D / 8;                  // lanes per key row
-  constexpr int RPP = kBoundThreads / TPR;    // rows per pass
+  constexpr int RPP = NT / TPR;               // rows per pass
   const int i = blockIdx.x % kKeyBoundBlocks;
   const int64_t rbh = blockIdx.x / kKeyBoundBlocks;  // (r * B + b) * Hk + hk
   const int hk = int(rbh % Hk);
@@ -47,13 +47,13 @@ __global__ __launch_bounds__(kBoundThreads) void key_bound_kernel(KvSeg seg, int
   }
 #pragma unroll
   for (int o = TPR; o < 64; o <<= 1) best = fmaxf(best, __shfl_xor(best, o));
-  __shared__ float wmax[kBoundThreads / 64];
+  __shared__ float wmax[NT / 64];
   if ((tid & 63) == 0) wmax[tid >> 6] = best;
   __syncthreads();
   if (tid == 0) {
     float m = wmax[0];
 #pragma unroll
-    for (int w = 1; w < kBoundThreads / 64; ++w) m = fmaxf(m, wmax[w]);
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, wmax[w]);
     out[rbh * kKeyBoundBlocks + i] = m;
   }
 }
@@ -66,12 +66,15 @@ hipError_t launch_key_bound(const KvSeg& seg, int32_t B, int32_t Hk, int32_t D, 
   const int64_t parts = part_len > 0 ? (seg.len + part_len - 1) / part_len : 0;
   const int64_t nblk = parts * B * Hk * kKeyBoundBlocks;
   if (nblk == 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL((key_bound_kernel<128>), dim3(static_cast<unsigned>(nblk)), dim3(kBoundThreads), 0, s, seg, B, Hk,
-                       part_len, out);
-  else
-    hipLaunchKernelGGL((key_bound_kernel<64>), dim3(static_cast<unsigned>(nblk)), dim3(kBoundThreads), 0, s, seg, B, Hk,
-                       part_len, out);
+  const bool wide = part_len / kKeyBoundBlocks >= 192;
+  const dim3 grid(static_cast<unsigned>(nblk));
+  if (D == 128) {
+    if (wide) hipLaunchKernelGGL((key_bound_kernel<128, 1024>), grid, dim3(1024), 0, s, seg, B, Hk, part_len, out);
+    else hipLaunchKernelGGL((key_bound_kernel<128, 256>), grid, dim3(256), 0, s, seg, B, Hk, part_len, out);
+  } else {
+    if (wide) hipLaunchKernelGGL((key_bound_kernel<64, 1024>), grid, dim3(1024), 0, s, seg, B, Hk, part_len, out);
+    else hipLaunchKernelGGL((key_bound_kernel<64, 256>), grid, dim3(256), 0, s, seg, B, Hk, part_len, out);
+  }
   return hipGetLastError();
 }
 
