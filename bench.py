@@ -364,7 +364,7 @@ def main():
         print(json.dumps(t), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the layer's sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
