@@ -121,6 +121,36 @@ def test_rms_norm_validation_errors_return_before_any_gpu_call(lib):
     assert st == V.VDIT_ERR_INVALID_ARG and "eps" in msg
 
 
+def test_last_error_is_per_thread(lib):
+    """vdit_last_error() is thread-local (vdit.h): two threads fail in
+    different ways between the same two barriers, and each reads back its own
+    message afterwards."""
+    import threading
+    fake = 1 << 20  # never dereferenced: validation fails first
+    calls = {
+        "head_dim": lambda: lib.vdit_rms_norm(fake, fake, 1, 100, 3, 96, 0, None, 1e-6, None),
+        "eps": lambda: lib.vdit_rms_norm(fake, fake, 1, 100, 3, 64, 0, None, -1.0, None),
+    }
+    bar = threading.Barrier(2)
+    bad = []
+
+    def run(word):
+        for _ in range(200):
+            st = calls[word]()
+            bar.wait()
+            bar.wait()
+            msg = lib.vdit_last_error().decode()
+            if st == V.VDIT_OK or word not in msg:
+                bad.append((word, st, msg))
+
+    th = [threading.Thread(target=run, args=(w,)) for w in calls]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not bad, bad[:3]
+
+
 def test_attn_validation_errors(lib):
     a = V.VditAttnArgs()
     a.mode, a.dtype, a.B, a.n_heads, a.n_kv_heads, a.head_dim = 0, 0, 1, 12, 5, 128
