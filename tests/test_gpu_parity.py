@@ -273,6 +273,32 @@ def test_attention_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_concurrent_streams_equal_serial():
+    """No shared mutable state between calls: FULL (with its key split and
+    key-norm pass) and RING calls issued on two streams at once give the
+    same bits as the same calls one after the other."""
+    log("two streams: FULL and RING concurrently == serially")
+    q = raw((1, 900, 4, 128), 61, "bf16"); k = raw((1, 2100, 4, 128), 62, "bf16"); v = raw((1, 2100, 4, 128), 63, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    kc = [kd[:, :1000], kd[:, 1000:]]; vc = [vd[:, :1000], vd[:, 1000:]]
+    o_full, l_full = V.vdit_attn_fwd(qd, kd, vd)
+    o_ring, l_ring = V.vdit_attn_fwd(qd, mode="ring", k_chunks=kc, v_chunks=vc)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream()); s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            a = V.vdit_attn_fwd(qd, kd, vd)
+        with torch.cuda.stream(s2):
+            b = V.vdit_attn_fwd(qd, mode="ring", k_chunks=kc, v_chunks=vc)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for (oa, la), (ob, lb) in outs:
+        assert torch.equal(oa, o_full) and torch.equal(la, l_full)
+        assert torch.equal(ob, o_ring) and torch.equal(lb, l_ring)
+
+
 # --------------------------------------------------------------------- ring --
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
