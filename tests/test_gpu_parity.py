@@ -263,6 +263,37 @@ def test_wan13b_structured_inputs_sampled_rows():
     check_lse(from_dev(lse)[:, :, rows], wl, "bf16", "LSE (structured, sampled)")
 
 
+def test_offsets_beyond_2_31_elements():
+    """64-bit offsets: q and o hold more than 2^31 bf16 elements (4.4 GB
+    each): 65 x 256 x 256 = 4,259,840 tokens, 8 heads, D = 64, attending to
+    192 keys.  q is a seeded 4096-token block repeated along the sequence
+    (token i holds block row i mod 4096), rotated in place at its own grid
+    position; rows at the start, past 2^31 bytes and at the very end are
+    checked against the oracle."""
+    T, Hg, Wg = 65, 256, 256
+    L, H, D, Lk, blk = T * Hg * Wg, 8, 64, 192, 4096
+    pairs = (12, 10, 10)
+    assert L * H * D > 2 ** 31
+    log(f"64-bit offsets: {L} tokens x {H} heads x {D} (q {L * H * D * 2 / 1e9:.2f} GB)")
+    qb = raw((1, blk, H, D), 71, "bf16"); k = raw((1, Lk, H, D), 72, "bf16"); v = raw((1, Lk, H, D), 73, "bf16")
+    qd = to_dev(qb).repeat(1, L // blk + 1, 1, 1)[:, :L].contiguous()
+    kd, vd = to_dev(k), to_dev(v)
+    V.vdit_rope_qk(qd, None, V.make_grid(T, Hg, Wg, pairs), q_out=qd)
+    kgrid = (3, 8, 8)
+    V.vdit_rope_qk(None, kd, V.make_grid(*kgrid, pairs), k_out=kd)
+    o, lse = V.vdit_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4095, 4096, 2 ** 21 - 1, 2 ** 21, 2 ** 21 + 77, 2 ** 22 - 1, 2 ** 22, L - 4097, L - 2, L - 1])
+    rows_d = torch.from_numpy(rows).to("cuda")
+    _, wk = O.rope_qk(k.values, k.values, kgrid, pairs)
+    wq = np.concatenate([O.rope_qk(qb.values[:, r % blk:r % blk + 1], qb.values[:, :1], (T, Hg, Wg), pairs,
+                                   token0=int(r))[0] for r in rows], axis=1)
+    check(from_dev(qd.index_select(1, rows_d)), wq, "bf16", "rotated q (sampled rows)")
+    wo, wl = O.attention(wq, wk, v.values)
+    check(from_dev(o.index_select(1, rows_d)), wo, "bf16", "O (sampled rows)")
+    check_lse(from_dev(lse.index_select(2, rows_d)), wl, "bf16", "LSE (sampled rows)")
+
+
 def test_attention_deterministic():
     log("determinism: two FULL runs bitwise equal")
     q = raw((1, 600, 4, 128), 51, "bf16"); k = raw((1, 700, 4, 128), 52, "bf16"); v = raw((1, 700, 4, 128), 53, "bf16")
