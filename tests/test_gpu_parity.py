@@ -294,6 +294,31 @@ def test_offsets_beyond_2_31_elements():
     check_lse(from_dev(lse.index_select(2, rows_d)), wl, "bf16", "LSE (sampled rows)")
 
 
+def test_keys_beyond_2_31_elements():
+    """64-bit key offsets: k and v hold more than 2^31 bf16 elements (4.4 GB
+    each): a seeded 4096-key block repeated to 4,260,840 keys (8 heads,
+    D = 64), attended by 64 queries (the call takes the key split).  The
+    first L mod 4096 block keys occur 1041 times, the rest 1040 times, so the
+    exact result is the LSE merge of the two key sets' attention with
+    ln(multiplicity) added to each LSE (the oracle's own attention and
+    merge)."""
+    L, H, D, blk, Lq = 65 * 256 * 256 + 1000, 8, 64, 4096, 64
+    reps, rem = divmod(L, blk)
+    assert rem > 0
+    assert L * H * D > 2 ** 31
+    log(f"64-bit key offsets: {Lq} queries x {L} keys x {H} heads x {D}")
+    q = raw((1, Lq, H, D), 74, "bf16"); kb = raw((1, blk, H, D), 75, "bf16"); vb = raw((1, blk, H, D), 76, "bf16")
+    kd = to_dev(kb).repeat(1, reps + 1, 1, 1)[:, :L].contiguous()
+    vd = to_dev(vb).repeat(1, reps + 1, 1, 1)[:, :L].contiguous()
+    o, lse = V.vdit_attn_fwd(to_dev(q), kd, vd)
+    torch.cuda.synchronize()
+    oa, la = O.attention(q.values, kb.values[:, :rem], vb.values[:, :rem])
+    ob, lb = O.attention(q.values, kb.values[:, rem:], vb.values[:, rem:])
+    wo, wl = O.lse_merge(oa, la + np.log(reps + 1), ob, lb + np.log(reps))
+    check(o, wo, "bf16", "O")
+    check_lse(lse, wl, "bf16", "LSE")
+
+
 def test_attention_deterministic():
     log("determinism: two FULL runs bitwise equal")
     q = raw((1, 600, 4, 128), 51, "bf16"); k = raw((1, 700, 4, 128), 52, "bf16"); v = raw((1, 700, 4, 128), 53, "bf16")
