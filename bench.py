@@ -18,6 +18,7 @@ attention kernel alone, timed with HIP events on the stream it runs on;
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -98,13 +99,18 @@ def bench_full(args):
     grid = V.make_grid(*w.grid, w.pairs)
     stream = torch.cuda.current_stream()
 
+    # the step's keys come out of vdit_rope_qk RMS-normalised (gain 1): their
+    # norms are at most sqrt(D) up to bf16 rounding, which lets the attention
+    # call skip its own pass over the keys (same results, see vdit.h)
+    knorm = key_norm_bound(w.head_dim)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         V.vdit_rope_qk(qd, kd, grid, q_out=qr, k_out=kr)
         if ev is not None:
             ev[1].record(stream)
-        V.vdit_attn_fwd(qr, kr, vd, o=o, lse=lse)
+        V.vdit_attn_fwd(qr, kr, vd, o=o, lse=lse, key_norm_max=knorm)
         if ev is not None:
             ev[2].record(stream)
 
@@ -192,6 +198,12 @@ def measured_peaks(attn_tflops: float, rope_gbps: float, reps: int = 10):
             "copy_1GiB_GBps": round(copy, 1), "rope_frac_of_copy": round(rope_gbps / copy, 4)}
 
 
+def key_norm_bound(head_dim: int) -> float:
+    """Bound on the norm of keys RMS-normalised with gain 1 and stored in
+    bf16: sqrt(head_dim), widened for the rounding of each element."""
+    return math.sqrt(head_dim) * (1.0 + 2.0 ** -7)
+
+
 def bench_other(args):
     """Reference timings of the other workloads (not the headline line)."""
     import numpy as np
@@ -223,7 +235,9 @@ def bench_other(args):
         kc = torch.zeros((1, w.n_slots, w.tokens, w.kv_heads, w.head_dim), dtype=qd.dtype, device=dev)
         vc = torch.zeros_like(kc)
         for f in range(w.n_slots):
-            kc[:, f].copy_(kd[f:f + 1]); vc[:, f].copy_(vd[f:f + 1])
+            # the cache starts full of normalised, rotated keys, as the steps leave it
+            V.vdit_rope_qk(None, kd[f:f + 1], grid, k_out=kc[:, f])
+            vc[:, f].copy_(vd[f:f + 1])
         flops = WL.flops_full(w.tokens, w.tokens * w.n_slots, w.heads, w.head_dim)
         frame = [w.n_slots]
         t_step = w.grid[0]
@@ -242,7 +256,8 @@ def bench_other(args):
                 V.vdit_rms_norm(vd[i:i + 1], out=vc[:, slot])
             else:
                 vc[:, slot].copy_(vd[i:i + 1])
-            V.vdit_attn_fwd(qi, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
+            V.vdit_attn_fwd(qi, mode="rolling", k_cache=kc, v_cache=vc, frame=f,
+                            key_norm_max=key_norm_bound(w.head_dim))
             frame[0] += 1
     elif w.mode == "hybrid":
         s = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device=dev)

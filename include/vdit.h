@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define VDIT_ABI_VERSION 2
+#define VDIT_ABI_VERSION 3
 
 typedef enum {
   VDIT_OK = 0,
@@ -185,6 +185,18 @@ typedef enum {
  * ranges whose float32 partials live in the workspace and are merged with
  * the log-sum-exp combination of vdit_lse_merge; without a large enough
  * workspace they run unsplit (same result up to rounding order).
+ *
+ * key_norm_max: 0, or a bound the caller guarantees on the Euclidean norm of
+ * every key of the call.  bf16 calls bound each query's scores by
+ * |q_i| max_j |k_j| (Cauchy-Schwarz) and, where that bound keeps every
+ * exponent within 32 binary orders of magnitude, run the softmax of those
+ * queries without a running maximum; max_j |k_j| otherwise comes from one
+ * pass over the keys (into the workspace, when it is large enough).  A
+ * positive key_norm_max replaces that pass: for keys RMS-normalised with
+ * gain 1 by vdit_rope_qk, sqrt(head_dim) * (1 + 2^-7) covers the bf16
+ * rounding.  A value larger than needed costs only the faster path; one
+ * below the true maximum breaks the contract and the results are undefined
+ * (they may overflow).  Negative or non-finite: VDIT_ERR_INVALID_ARG.
  */
 typedef struct {
   int32_t mode;  /* vdit_attn_mode */
@@ -213,6 +225,8 @@ typedef struct {
   size_t workspace_bytes;
   int64_t overlap_tokens;      /* CHUNK_HYBRID (0 in the other modes) */
   int64_t ctx_tokens;          /* CHUNK_HYBRID (0 in the other modes) */
+  float key_norm_max;          /* 0 = computed (see above) */
+  int32_t reserved1;
 } vdit_attn_args;
 
 /* Bytes of device workspace vdit_attn_fwd needs (RING, CHUNK_HYBRID) or can

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vdit_abi_version() == V.ABI_VERSION == 2
+    assert lib.vdit_abi_version() == V.ABI_VERSION == 3
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -164,6 +164,11 @@ def test_attn_validation_errors(lib):
     st = lib.vdit_attn_fwd(ctypes.byref(a), None)
     assert st == V.VDIT_ERR_INVALID_ARG and "state" in lib.vdit_last_error().decode()
     assert lib.vdit_attn_fwd(None, None) == V.VDIT_ERR_INVALID_ARG
+    a.mode, a.chunk_tokens = 0, 0
+    for bad in (-1.0, float("nan"), float("inf")):
+        a.key_norm_max = bad
+        st = lib.vdit_attn_fwd(ctypes.byref(a), None)
+        assert st == V.VDIT_ERR_INVALID_ARG and "key_norm_max" in lib.vdit_last_error().decode()
 
 
 def test_workspace_sizes(lib):

@@ -5,6 +5,7 @@ Inputs come from the seeded generators in ``workloads``; expected values from
 full-size workloads are checked on seeded samples of query rows (each row
 against every key) in the launch configuration the benchmark times.
 """
+import math
 import os
 import subprocess
 
@@ -225,6 +226,45 @@ def test_full_attention_bounded_and_online_softmax(D, Lq):
     for o, lse, tag in ((o_b, lse_b, "bounded"), (o_o, lse_o, "online")):
         check(from_dev(o)[:, rows], wo, "bf16", f"O ({tag}, sampled rows)")
         check_lse(from_dev(lse)[:, :, rows], wl, "bf16", f"LSE ({tag}, sampled rows)")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_caller_key_norm_bound(D):
+    """key_norm_max replaces the key-norm pass.  Keys RMS-normalised and
+    rotated by vdit_rope_qk have |k| <= sqrt(D) (1 + 2^-7); with that bound
+    every wavefront takes the same path as with the computed one, so FULL,
+    RING (one launch) and ROLLING give the same bits.  A bound far above the
+    keys' norms sends every wavefront to the online maximum: checked against
+    the oracle."""
+    L, H = 9001, 16
+    pairs = (22, 21, 21) if D == 128 else (12, 10, 10)
+    grid = (9, 31, 33)
+    log(f"caller key-norm bound: D={D} L={L} H={H}")
+    q, k, v = WL.draw_qkv((1, L, H, D), (1, L, H, D), 91, "bf16")
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*grid, pairs))
+    vd = to_dev(v)
+    kb = math.sqrt(D) * (1 + 2.0 ** -7)
+    o0, l0 = V.vdit_attn_fwd(qr, kr, vd)
+    o1, l1 = V.vdit_attn_fwd(qr, kr, vd, key_norm_max=kb)
+    kc, vc = [kr[:, :4000], kr[:, 4000:]], [vd[:, :4000], vd[:, 4000:]]
+    r0, rl0 = V.vdit_attn_fwd(qr, mode="ring", k_chunks=kc, v_chunks=vc)
+    r1, rl1 = V.vdit_attn_fwd(qr, mode="ring", k_chunks=kc, v_chunks=vc, key_norm_max=kb)
+    # rolling: 3 slots of 3000 tokens, frame 4 (two earlier frames in the window)
+    kcache = kr[:, :9000].reshape(1, 3, 3000, H, D).contiguous()
+    vcache = vd[:, :9000].reshape(1, 3, 3000, H, D).contiguous()
+    qf = qr[:, :3000].contiguous()
+    f0, fl0 = V.vdit_attn_fwd(qf, mode="rolling", k_cache=kcache, v_cache=vcache, frame=4)
+    f1, fl1 = V.vdit_attn_fwd(qf, mode="rolling", k_cache=kcache, v_cache=vcache, frame=4, key_norm_max=kb)
+    o2, l2 = V.vdit_attn_fwd(qr, kr, vd, key_norm_max=1.0e4)
+    torch.cuda.synchronize()
+    for x, y in ((o0, o1), (l0, l1), (r0, r1), (rl0, rl1), (f0, f1), (fl0, fl1)):
+        assert torch.equal(x, y)
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs)
+    rows = np.unique(np.concatenate([WL.sample_rows(L, 96, seed=92), [0, L - 1]]))
+    wo, wl = O.attention(wq[:, rows], wk, v.values)
+    check(from_dev(o2)[:, rows], wo, "bf16", "O (bound 1e4: online maximum, sampled rows)")
+    check_lse(from_dev(l2)[:, :, rows], wl, "bf16", "LSE (bound 1e4, sampled rows)")
+    check(from_dev(o1)[:, rows], wo, "bf16", "O (caller bound, sampled rows)")
 
 
 def _sampled_attention(qr64, kr64, v64, rows, scale=None):

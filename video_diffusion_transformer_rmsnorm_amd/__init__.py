@@ -21,7 +21,7 @@ VDIT_BF16, VDIT_F32 = 0, 1
 VDIT_ROPE_NO_NORM = 1
 VDIT_ROPE_NO_Q_NORM = 2
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol include/vdit.h declares.
 EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_workspace_bytes",
@@ -55,6 +55,7 @@ class VditAttnArgs(ctypes.Structure):
         ("state_s", ctypes.c_void_p), ("state_z", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("overlap_tokens", ctypes.c_int64), ("ctx_tokens", ctypes.c_int64),
+        ("key_norm_max", ctypes.c_float), ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -193,7 +194,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
                   scale: float = 0.0, k_chunks=None, v_chunks=None, k_cache=None, v_cache=None,
                   frame: int = 0, chunk_tokens: int = 0, state_s=None, state_z=None, workspace=None,
                   n_kv_heads: Optional[int] = None, overlap_tokens: int = 0, ctx_tokens: int = 0,
-                  stream=None):
+                  key_norm_max: float = 0.0, stream=None):
     """One attention call.  Returns (o, lse) (lse None unless wanted).
 
     full:    k, v [B,Lkv,Hk,D].
@@ -204,6 +205,8 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     hybrid:  k, v [B,ctx_tokens+Lq,Hk,D]; chunk_tokens; state_s [B,Hk,D,D], state_z [B,Hk,D]
              float32 (in/out); overlap_tokens keys before each chunk join its softmax
              window; the first ctx_tokens (<= overlap_tokens) keys precede the first query.
+    key_norm_max: 0, or a guaranteed bound on every key's norm, which replaces the
+             library's pass over the keys (see vdit.h).
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (k_cache, "k_cache"),
@@ -243,6 +246,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     else:
         hk = k.shape[2]
         a = _attn_args(q, k, v, mode, o, lse, scale, n_kv_heads or hk, k.shape[1])
+    a.key_norm_max = key_norm_max
     need = vdit_attn_workspace_bytes(a)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

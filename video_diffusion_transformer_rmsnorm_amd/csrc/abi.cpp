@@ -19,6 +19,8 @@ static_assert(offsetof(vdit_attn_args, workspace_bytes) == offsetof(vdit::AttnAr
               "vdit_attn_args layout mirror");
 static_assert(offsetof(vdit_attn_args, ctx_tokens) == offsetof(vdit::AttnArgs, ctx_tokens),
               "vdit_attn_args layout mirror");
+static_assert(offsetof(vdit_attn_args, key_norm_max) == offsetof(vdit::AttnArgs, key_norm_max),
+              "vdit_attn_args layout mirror");
 
 namespace {
 
@@ -85,11 +87,17 @@ vdit_status optional_area(const vdit::AttnArgs& a, size_t off, size_t bytes, cha
   return VDIT_OK;
 }
 
-// Bounded-score softmax: key-norm maxima of the launch's keys into the
-// workspace area `area` (bf16 only), or nothing when there is no area.
+// Bounded-score softmax: the caller's key-norm bound when given, else the
+// key-norm maxima of the launch's keys into the workspace area `area` (bf16
+// only), or nothing when there is no area.
 vdit_status add_key_bound(vdit::AttnLaunch& p, const vdit::KvSeg& keys, char* area, hipStream_t stream,
-                          int64_t part_len = 0) {
-  if (!area || keys.len <= 0 || !vdit::attn_uses_key_bound(p)) return VDIT_OK;
+                          float key_norm_max, int64_t part_len = 0) {
+  if (keys.len <= 0 || !vdit::attn_uses_key_bound(p)) return VDIT_OK;
+  if (key_norm_max > 0.f) {
+    p.kbound_sq = key_norm_max * key_norm_max;
+    return VDIT_OK;
+  }
+  if (!area) return VDIT_OK;
   float* out = reinterpret_cast<float*>(area);
   if (auto st = from_hip(vdit::launch_key_bound(keys, p.B, p.Hk, p.D, part_len, out, stream), "key bound launch");
       st != VDIT_OK)
@@ -122,7 +130,7 @@ vdit_status launch_plain(vdit::AttnLaunch p, const vdit::AttnArgs& a, hipStream_
         ws + vdit::align256(size_t(sp.nsplit) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * 4));
   }
   if (p.nseg)
-    if (auto st = add_key_bound(p, p.seg[0], bound, stream); st != VDIT_OK) return st;
+    if (auto st = add_key_bound(p, p.seg[0], bound, stream, a.key_norm_max); st != VDIT_OK) return st;
   if (auto st = from_hip(launch_attn(p, a.dtype, stream), what); st != VDIT_OK) return st;
   if (!ws) return VDIT_OK;
   vdit::SplitMergeLaunch m;
@@ -267,7 +275,9 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         p.part_o = reinterpret_cast<float*>(parts);
         p.part_lse = reinterpret_cast<float*>(
             parts + vdit::align256(size_t(n) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(D) * 4));
-        if (bound && all_keys && vdit::attn_uses_key_bound(p)) {
+        if (a.key_norm_max > 0.f && all_keys && vdit::attn_uses_key_bound(p)) {
+          p.kbound_sq = a.key_norm_max * a.key_norm_max;
+        } else if (bound && all_keys && vdit::attn_uses_key_bound(p)) {
           for (int c = 0; c < n; ++c)
             if (auto st = from_hip(vdit::launch_key_bound(p.seg[c], p.B, p.Hk, p.D, 0,
                                                           reinterpret_cast<float*>(bound_run(c)), stream),
@@ -297,7 +307,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         if (a.chunk_len[0] > 0) {
           p.nseg = 1;
           p.seg[0] = seg_of(0);
-          if (auto st = add_key_bound(p, p.seg[0], bound, stream); st != VDIT_OK) return st;
+          if (auto st = add_key_bound(p, p.seg[0], bound, stream, a.key_norm_max); st != VDIT_OK) return st;
         }
         return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(RING) launch");
       }
@@ -310,7 +320,8 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         if (a.chunk_len[c] > 0) {
           p.nseg = 1;
           p.seg[0] = seg_of(c);
-          if (auto st = add_key_bound(p, p.seg[0], bound_run(c), stream); st != VDIT_OK) return st;
+          if (auto st = add_key_bound(p, p.seg[0], bound_run(c), stream, a.key_norm_max); st != VDIT_OK)
+            return st;
         }
         p.epi = vdit::kEpiRing;
         p.part_o = part_o;
@@ -398,7 +409,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       // overlapping windows run on the online maximum
       if (a.overlap_tokens == 0)
         if (auto st = add_key_bound(p, vdit::KvSeg{a.k, a.v, a.Lq, a.Lq * a.n_kv_heads * D}, bound, stream,
-                                    a.chunk_tokens);
+                                    a.key_norm_max, a.chunk_tokens);
             st != VDIT_OK)
           return st;
       return from_hip(launch_attn(p, a.dtype, stream), "vdit_attn_fwd(CHUNK_HYBRID) launch");

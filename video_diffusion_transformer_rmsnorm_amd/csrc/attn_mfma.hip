@@ -329,12 +329,16 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // (8- and 4-wavefront kernels; the 2-wavefront kernel, for problems too
   // small to fill the chip, keeps a single loop)
   bool fast = false;
-  if (NW >= VDIT_ATTN_BOUND_MIN_NW && p.kbound != nullptr) {
-    // the partial maxima (at most 64): one per lane, then a wavefront max
-    const float* kbp = p.kbound + ((chunk_id * p.B + b) * p.Hk + hk) * p.kbound_n;
-    float kmax2 = lane < p.kbound_n ? kbp[lane] : 0.f;
+  if (NW >= VDIT_ATTN_BOUND_MIN_NW && (p.kbound != nullptr || p.kbound_sq > 0.f)) {
+    // the caller's bound, or the partial maxima (at most 64): one per lane,
+    // then a wavefront max
+    float kmax2 = p.kbound_sq;
+    if (p.kbound != nullptr) {
+      const float* kbp = p.kbound + ((chunk_id * p.B + b) * p.Hk + hk) * p.kbound_n;
+      kmax2 = lane < p.kbound_n ? kbp[lane] : 0.f;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, o));
+      for (int o = 1; o < 64; o <<= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, o));
+    }
     bool ok = kmax2 < 3.0e38f;
     float mb[QB];
 #pragma unroll

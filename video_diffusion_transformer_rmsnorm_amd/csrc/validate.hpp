@@ -5,6 +5,7 @@
 // caller writes nothing and reports the returned message.
 #pragma once
 
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -138,6 +139,8 @@ struct AttnArgs {
   size_t workspace_bytes;
   int64_t overlap_tokens;
   int64_t ctx_tokens;
+  float key_norm_max;
+  int32_t reserved1;
 };
 
 constexpr int kMaxRingChunks = 64;
@@ -252,6 +255,8 @@ inline CheckResult check_attn(const AttnArgs& a) {
   }
   if (a.lse && !aligned16(a.lse)) return CheckResult::bad("lse must be 16-byte aligned");
   if (!empty_q && overlaps(a.q, nq, a.o, nq)) return CheckResult::bad("o overlaps q");
+  if (!(a.key_norm_max >= 0.f) || !std::isfinite(a.key_norm_max))
+    return CheckResult::bad("key_norm_max must be finite and >= 0");
   if (a.mode != 3 && (a.overlap_tokens != 0 || a.ctx_tokens != 0))
     return CheckResult::bad("overlap_tokens and ctx_tokens belong to CHUNK_HYBRID (0 otherwise)");
   switch (a.mode) {

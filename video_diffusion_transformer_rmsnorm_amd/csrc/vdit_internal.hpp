@@ -64,6 +64,9 @@ struct AttnLaunch {
   // online maximum
   const float* kbound;
   int32_t kbound_n;
+  // caller's bound on max_j |k_j|^2 (key_norm_max^2), used instead of
+  // kbound when kbound is null and this is > 0
+  float kbound_sq;
 };
 
 // Partial maxima of squared key norms (bf16 keys), per run of part_len keys
