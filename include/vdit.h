@@ -194,9 +194,10 @@ typedef enum {
  * pass over the keys (into the workspace, when it is large enough).  A
  * positive key_norm_max replaces that pass: for keys RMS-normalised with
  * gain 1 by vdit_rope_qk, sqrt(head_dim) * (1 + 2^-7) covers the bf16
- * rounding.  A value larger than needed costs only the faster path; one
- * below the true maximum breaks the contract and the results are undefined
- * (they may overflow).  Negative or non-finite: VDIT_ERR_INVALID_ARG.
+ * rounding.  A value above the true maximum is safe (it can only send more
+ * queries to the running-maximum path); one below it breaks the contract
+ * and the results are undefined (they may overflow).  Negative or
+ * non-finite: VDIT_ERR_INVALID_ARG.  Ignored by float32 calls.
  */
 typedef struct {
   int32_t mode;  /* vdit_attn_mode */
