@@ -133,14 +133,22 @@ typedef enum {
  *
  * VDIT_ATTN_RING: one device's share of ring attention (ReGenVC:
  *   End-to-End Real-Time Generative Video Coding at Ultra-Low Bitrate,
- *   unified sequence parallelism paragraph): the key/value sequence arrives
- *   as n_kv_chunks chunks, attended to in order; each chunk's partial is
- *   folded into a float32 running partial in `workspace` with the
- *   log-sum-exp merge of vdit_lse_merge, fused into the attention kernel's
- *   epilogue, and the last chunk writes o (dtype) and lse.  k_chunks[c],
- *   v_chunks[c] (host arrays of device pointers) are [B, chunk_len[c],
- *   n_kv_heads, D]; chunk_len (host) must sum to Lkv; k and v are unused.
- *   Equal to FULL over the concatenated chunks up to rounding order.
+ *   unified sequence parallelism paragraph): the key/value sequence is
+ *   given as n_kv_chunks chunks whose partials are combined with the
+ *   log-sum-exp merge of vdit_lse_merge.  k_chunks[c], v_chunks[c] (host
+ *   arrays of device pointers) are [B, chunk_len[c], n_kv_heads, D];
+ *   chunk_len (host) must sum to Lkv; k and v are unused.  Equal to FULL
+ *   over the concatenated chunks up to rounding order.  Two forms:
+ *   - fold (the ring's own order): one launch per chunk, in chunk order,
+ *     each folding its partial into a float32 running partial in
+ *     `workspace` (the merge is fused into the attention epilogue); the
+ *     last chunk writes o and lse.  Chunk c is read only by launch c.  Taken
+ *     for float32, for more than 8 chunks, with the VDIT_ATTN_RING_FOLD flag,
+ *     or when the workspace holds only the running partial.
+ *   - one launch (bf16, 2..8 chunks, the default when the workspace holds a
+ *     float32 partial per chunk): every chunk is attended to in one launch,
+ *     whose workgroups cover (chunk, query tile, head), and the partials are
+ *     merged afterwards; every chunk must be in place when the launch runs.
  *
  * VDIT_ATTN_ROLLING: frame-by-frame decode with a rolling KV cache of
  *   n_slots frames (FlashDecoder Sec. 3.3).  k_cache, v_cache are
@@ -175,16 +183,21 @@ typedef enum {
  *   over the whole sequence.  Needs `workspace` of
  *   vdit_attn_workspace_bytes().
  *
- * lse: [B, n_heads, Lq] float32 or NULL.  o must not overlap q, k, v, the
- * caches or the workspace.  workspace: device scratch of at least
- * vdit_attn_workspace_bytes(args) bytes (may be NULL when that is 0);
- * its contents need no initialisation and are clobbered.  RING (with more
- * than one chunk) and CHUNK_HYBRID require it.  For FULL and ROLLING it is
- * optional: bf16 calls with too few queries to occupy the device (fewer
- * than two 128-query blocks per compute unit) split the keys into up to 8
- * ranges whose float32 partials live in the workspace and are merged with
- * the log-sum-exp combination of vdit_lse_merge; without a large enough
- * workspace they run unsplit (same result up to rounding order).
+ * lse: [B, n_heads, Lq] float32 or NULL.  The ranges a call writes (o,
+ * lse, the workspace_bytes bytes at workspace, the rolling caches, the
+ * hybrid state) must not overlap one another or any other tensor of the
+ * call (tensors that are only read may overlap); the one exception is a
+ * ROLLING call with B = 1 passing the cache slot itself as k, v.  All of
+ * this is checked before anything is enqueued.  workspace: 16-byte aligned
+ * device scratch of at least vdit_attn_workspace_bytes(args) bytes (may be
+ * NULL when that is 0); its contents need no initialisation and are
+ * clobbered.  RING (with more than one chunk) and CHUNK_HYBRID require it.
+ * For FULL and ROLLING it is optional: bf16 calls with too few queries to
+ * occupy the device (fewer than two 128-query blocks per compute unit)
+ * split the keys into up to 8 ranges whose float32 partials live in the
+ * workspace and are merged with the log-sum-exp combination of
+ * vdit_lse_merge; without a large enough workspace they run unsplit (same
+ * result up to rounding order).
  *
  * key_norm_max: 0, or a bound the caller guarantees on the Euclidean norm of
  * every key of the call.  bf16 calls bound each query's scores by
@@ -194,10 +207,14 @@ typedef enum {
  * pass over the keys (into the workspace, when it is large enough).  A
  * positive key_norm_max replaces that pass: for keys RMS-normalised with
  * gain 1 by vdit_rope_qk, sqrt(head_dim) * (1 + 2^-7) covers the bf16
- * rounding.  A value above the true maximum is safe (it can only send more
- * queries to the running-maximum path); one below it breaks the contract
- * and the results are undefined (they may overflow).  Negative or
- * non-finite: VDIT_ERR_INVALID_ARG.  Ignored by float32 calls.
+ * rounding.  A value above the true maximum can only send more queries to
+ * the running-maximum path.  One below it costs time, not correctness: a
+ * true bound keeps every row sum of the bounded path within [2^-64, 2^64],
+ * and a wavefront whose row sums leave that range (overflow, or its largest
+ * terms lost to underflow) is detected when its workgroup has seen all its
+ * keys; the workgroup then runs its keys again with that wavefront on the
+ * running maximum.  Negative or non-finite: VDIT_ERR_INVALID_ARG.  Ignored
+ * by float32 calls.
  */
 typedef struct {
   int32_t mode;  /* vdit_attn_mode */

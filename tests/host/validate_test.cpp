@@ -105,6 +105,52 @@ int main() {
   AttnArgs f = a; f.overlap_tokens = 4;
   EXPECT(check_attn(f).code == Check::invalid, "overlap outside the hybrid mode");
 
+  // placement: every range a call writes (o, lse, workspace, caches, state)
+  // overlaps none of its other tensors, checked before anything is enqueued
+  {
+    AttnArgs r = a; r.mode = 2; r.n_slots = 5; r.frame = 3; r.k_cache = P(10ull << 28); r.v_cache = P(11ull << 28);
+    r.workspace = P((10ull << 28) + 4096); r.workspace_bytes = 1 << 20;  // inside k_cache
+    EXPECT(check_attn(r).code == Check::invalid, "rolling: workspace overlaps the cache");
+    r.workspace = P(15ull << 28);
+    EXPECT(bool(check_attn(r)), "rolling: separate workspace");
+    r.workspace = P((15ull << 28) + 8);
+    EXPECT(check_attn(r).code == Check::invalid, "rolling: misaligned workspace");
+    r.workspace = nullptr; r.workspace_bytes = 0;
+    // the new frame may be the cache slot itself (B = 1) ...
+    const size_t frame_bytes = size_t(r.Lq) * r.n_kv_heads * r.head_dim * 2;
+    r.k = P((10ull << 28) + 3 * frame_bytes); r.v = P((11ull << 28) + 3 * frame_bytes);
+    EXPECT(bool(check_attn(r)), "rolling: frame given as its own slot (B = 1)");
+    // ... but not another part of the cache, nor the slot when B > 1
+    r.k = P((10ull << 28) + 2 * frame_bytes);
+    EXPECT(check_attn(r).code == Check::invalid, "rolling: frame inside another slot");
+    r.k = P((10ull << 28) + 3 * frame_bytes); r.B = 2;
+    r.k_cache = P(10ull << 28); r.v_cache = P(12ull << 28); r.v = P((12ull << 28) + 3 * frame_bytes);
+    EXPECT(check_attn(r).code == Check::invalid, "rolling: slot alias with B = 2");
+    r = a; r.mode = 2; r.n_slots = 5; r.frame = 3; r.k_cache = P(10ull << 28); r.v_cache = P(11ull << 28);
+    r.k = P(16ull << 28); r.v = P(17ull << 28); r.lse = reinterpret_cast<float*>(P((16ull << 28) + 256));
+    EXPECT(check_attn(r).code == Check::invalid, "rolling: lse overlaps the new keys");
+
+    AttnArgs h = a; h.mode = 3; h.chunk_tokens = 30;
+    h.state_s = reinterpret_cast<float*>(P(12ull << 28)); h.state_z = reinterpret_cast<float*>(P(13ull << 28));
+    h.workspace = P((12ull << 28) + 1024); h.workspace_bytes = hybrid_layout(h).total;
+    EXPECT(check_attn(h).code == Check::invalid, "hybrid: workspace overlaps the state");
+    h.workspace = P(14ull << 28); h.workspace_bytes = hybrid_layout(h).total + (1 << 20);
+    EXPECT(bool(check_attn(h)), "hybrid: separate, larger workspace");
+    h.state_z = reinterpret_cast<float*>(P((2ull << 28) + 512));  // inside k
+    EXPECT(check_attn(h).code == Check::invalid, "hybrid: state overlaps k");
+    h.state_z = reinterpret_cast<float*>(P((12ull << 28) + 4096));  // inside state_s
+    EXPECT(check_attn(h).code == Check::invalid, "hybrid: state_z overlaps state_s");
+    h.state_z = reinterpret_cast<float*>(P(13ull << 28));
+    h.workspace_bytes = hybrid_layout(h).total + (1ull << 28) + 1;  // reaches o
+    h.o = P(15ull << 28);
+    EXPECT(check_attn(h).code == Check::invalid, "hybrid: workspace reaches o");
+
+    AttnArgs f = a; f.lse = reinterpret_cast<float*>(P((3ull << 28) + 64));
+    EXPECT(check_attn(f).code == Check::invalid, "full: lse overlaps v");
+    f.lse = nullptr; f.k = f.v = f.q;  // read-only tensors may alias each other
+    EXPECT(bool(check_attn(f)), "full: q, k, v the same tensor");
+  }
+
   // key split plan (256 compute units)
   {
     SplitPlan sp = split_plan(0, 1, 2040, 16, 5 * 2040, 256);  // rolling decode frame: 256 workgroups of 128 queries

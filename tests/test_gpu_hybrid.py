@@ -1,0 +1,141 @@
+"""GPU parity of the chunk-hybrid mode at full size, with inputs on which both
+partials of the joint normalisation carry weight.
+
+With phi = elu + 1 on RMS-normalised q and k and the default 1/sqrt(D) scale,
+the linear partial outweighs the softmax partial about a hundred to one after
+the first chunk, so an error in the softmax part of chunks >= 1 hardly moves
+the merged output.  The softmax scale multiplies only the softmax scores
+(phi takes q and k unscaled), so a larger scale shifts the weight towards the
+softmax partial: each test below runs the default scale (linear-heavy) and a
+scale at which the softmax partial holds between a fifth and nineteen
+twentieths of the weight in every chunk after the first (the short last
+chunk aside).  tests/test_hybrid_sensitivity.py shows on the CPU, from the
+oracle alone, that planted mistakes in either partial exceed the parity bar
+at these shapes and scales.
+
+The oracle receives the library's own rotated bf16 q and k (the rotation is
+checked on its own elsewhere), so the recurrent state can be held to a
+relative error of 1e-5 at full size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import video_diffusion_transformer_rmsnorm_amd as V
+import workloads as WL
+from parity import check, check_lse, from_dev, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+STATE_REL = 1e-5
+
+
+def _state_reference(k64, v64, end):
+    """sum_j phi(k_j) v_j^T and sum_j phi(k_j) over keys [0, end) ([B, H, D, D], [B, H, D])."""
+    fk = O.phi(k64[:, :end])                                   # [B, n, H, D]
+    s = np.matmul(fk.transpose(0, 2, 3, 1), v64[:, :end].transpose(0, 2, 1, 3))
+    return s, fk.sum(axis=1)
+
+
+def _softmax_weight_per_chunk(l_s, l_l, L, C):
+    ws = np.exp(l_s - np.logaddexp(l_s, l_l))                  # [B, H, L]
+    return [float(ws[:, :, c0:c0 + C].mean()) for c0 in range(0, L, C)]
+
+
+def _hybrid_full(w, scale, inputs, B=1, key_norm_max=0.0):
+    """RMSNorm + 3D-RoPE and one CHUNK_HYBRID call over the whole grid; O, LSE
+    (all rows) and the final state against the oracle fed the library's own
+    rotated q, k.  Returns the oracle's mean softmax weight per chunk."""
+    q, k, v = inputs
+    D, C, Ov = w.head_dim, w.chunk_tokens, w.overlap_tokens
+    H = q.values.shape[2]
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*w.grid, w.pairs))
+    sd = torch.zeros((B, H, D, D), device="cuda")
+    zd = torch.zeros((B, H, D), device="cuda")
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v), mode="hybrid", chunk_tokens=C, state_s=sd, state_z=zd,
+                             overlap_tokens=Ov, scale=scale, key_norm_max=key_norm_max)
+    torch.cuda.synchronize()
+    q64, k64 = from_dev(qr), from_dev(kr)
+    o_s, l_s, o_l, l_l = O.hybrid_partials(q64, k64, v.values, C, scale=scale, overlap=Ov)
+    wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
+    check(o, wo, "bf16", f"O hybrid, scale {scale:.4f} (all rows)")
+    check_lse(lse, wl, "bf16", f"LSE hybrid, scale {scale:.4f}")
+    ws_, wz = _state_reference(k64, v.values, w.tokens - Ov)
+    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
+    rz = np.linalg.norm(from_dev(zd) - wz) / np.linalg.norm(wz)
+    log(f"  state relF s={rs:.3e} z={rz:.3e}")
+    assert rs <= STATE_REL and rz <= STATE_REL, (rs, rz)
+    weights = _softmax_weight_per_chunk(l_s, l_l, w.tokens, C)
+    log("  mean softmax weight per chunk: " + " ".join(f"{x:.3f}" for x in weights))
+    return weights
+
+
+def _balanced(weights, lo=0.2, hi=0.97):
+    """Chunks 1 .. n-2 (not the first, which is pure softmax, nor the short last one)."""
+    mid = weights[1:-1]
+    assert all(lo <= x <= hi for x in mid), weights
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("number,scale", [(5, None), (5, 0.35), (8, None), (8, 0.32)])
+def test_hybrid_full_size_both_partials(number, scale):
+    w = WL.WORKLOADS[number]
+    sc = scale if scale is not None else 1.0 / math.sqrt(w.head_dim)
+    log(f"{w.name}: chunk {w.chunk_tokens}, overlap {w.overlap_tokens}, scale {sc:.4f}, all rows")
+    weights = _hybrid_full(w, sc, WL.workload_inputs(w))
+    if scale is None:
+        assert max(weights[1:]) < 0.05, weights  # the linear partial dominates
+    else:
+        _balanced(weights)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("bound", ["computed", "caller"])
+def test_hybrid_wide_workgroups_bounded_scores(bound):
+    """B = 4, 8 heads on the 31 x 15 x 26 grid in chunks of 1170: 5 query
+    tiles of 256 x 11 chunks x 8 heads x 4 batches = 1760 workgroups, which
+    fill 256 compute units in nearly even rounds, so the 256-query kernel with
+    the bounded-score softmax runs (its queries are pre-scaled in registers;
+    the linear partial must see them unscaled)."""
+    w = WL.WORKLOADS[5]
+    B, H = 4, 8
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg256 = math.ceil(w.chunk_tokens / 256) * math.ceil(w.tokens / w.chunk_tokens) * H * B
+    rounds = math.ceil(wg256 / cus)
+    assert wg256 >= 2 * cus and (rounds * cus - wg256) * 100 <= 6 * rounds * cus, (wg256, cus)
+    log(f"hybrid B={B} H={H}: {wg256} workgroups of 256 queries on {cus} CUs, bound {bound}")
+    rng = np.random.default_rng(1505)
+    shape = (B, w.tokens, H, w.head_dim)
+    inputs = tuple(WL.draw(shape, rng, "bf16") for _ in range(3))
+    knm = math.sqrt(w.head_dim) * (1 + 2.0 ** -7) if bound == "caller" else 0.0
+    weights = _hybrid_full(w, 1.0 / math.sqrt(w.head_dim), inputs, B=B, key_norm_max=knm)
+    assert max(weights[1:]) < 0.05, weights
+
+
+def test_hybrid_small_both_partials_visible():
+    """A small case (several tiles, a ragged last chunk, GQA) at the balanced
+    scale, with an incoming state: both partials carry weight in every chunk."""
+    D, L, C, Hq, Hk, scale = 128, 700, 160, 4, 2, 0.35
+    log(f"hybrid small, scale {scale}: L={L} chunk={C} Hq={Hq} Hk={Hk}")
+    rng = np.random.default_rng(1601)
+    q = WL.draw((1, L, Hq, D), rng, "bf16"); k = WL.draw((1, L, Hk, D), rng, "bf16"); v = WL.draw((1, L, Hk, D), rng, "bf16")
+    g = V.make_grid(7, 10, 10, (22, 21, 21))
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), g)
+    s0 = (0.02 * rng.standard_normal((1, Hk, D, D))).astype(np.float32)
+    z0 = (20.0 + np.abs(rng.standard_normal((1, Hk, D)))).astype(np.float32)
+    sd = torch.from_numpy(s0).cuda(); zd = torch.from_numpy(z0).cuda()
+    o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v), mode="hybrid", chunk_tokens=C, state_s=sd, state_z=zd, scale=scale)
+    torch.cuda.synchronize()
+    q64, k64 = from_dev(qr), from_dev(kr)
+    o_s, l_s, o_l, l_l = O.hybrid_partials(q64, k64, v.values, C, scale=scale, s0=s0, z0=z0)
+    wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
+    check(o, wo, "bf16", "O hybrid"); check_lse(lse, wl, "bf16", "LSE hybrid")
+    weights = _softmax_weight_per_chunk(l_s, l_l, L, C)
+    log("  mean softmax weight per chunk: " + " ".join(f"{x:.3f}" for x in weights))
+    assert all(0.05 <= x <= 0.95 for x in weights), weights
+    ws_, wz = _state_reference(k64, v.values, L)
+    rs = np.linalg.norm(from_dev(sd) - (s0 + ws_)) / np.linalg.norm(s0 + ws_)
+    assert rs <= STATE_REL, rs

@@ -786,11 +786,8 @@ def test_hybrid_overlap_full_c4_o2():
     wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
     check(o, wo, "bf16", "O hybrid (all rows)")
     check_lse(lse, wl, "bf16", "LSE hybrid")
-    e = w.tokens - w.overlap_tokens
-    ws_ = np.einsum("blhd,blhe->bhde", O.phi(wk[:, :e]), v.values[:, :e])
-    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
-    log(f"  state relF={rs:.3e}")
-    assert rs <= 1e-2  # as in the no-overlap case: the library's k is the bf16-rounded rotation
+    # (the state is checked to 1e-5 on the library's own rotated keys in
+    # test_gpu_hybrid.py; here the oracle rotates in float64, end to end)
 
 
 @pytest.mark.slow
@@ -808,13 +805,8 @@ def test_hybrid_5b_full():
     wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
     check(o, wo, "bf16", "O hybrid (all rows)")
     check_lse(lse, wl, "bf16", "LSE hybrid")
-    fk = O.phi(wk)
-    ws_ = np.einsum("blhd,blhe->bhde", fk, v.values)
-    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
-    log(f"  state relF={rs:.3e}")
-    # the oracle's rotated k is unrounded float64 while the library's k is the
-    # bf16-rounded output of vdit_rope_qk: the state inherits that rounding
-    assert rs <= 1e-2
+    # (the state is checked to 1e-5 on the library's own rotated keys in
+    # test_gpu_hybrid.py; here the oracle rotates in float64, end to end)
 
 
 # ----------------------------------------------------------- graphs ------

@@ -70,21 +70,12 @@ hipError_t launch_attn(const vdit::AttnLaunch& p, int dtype, hipStream_t s) {
   return dtype == VDIT_BF16 ? vdit::launch_attn_bf16(p, s) : vdit::launch_attn_f32(p, s);
 }
 
-size_t q_bytes(const vdit::AttnArgs& a) {
-  return size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(a.head_dim) * vdit::esize(a.dtype);
-}
-
 // Optional workspace area [off, off + bytes): usable when the caller's
-// workspace holds it.  A workspace that holds it but is misplaced (unaligned
-// or overlapping o) is an error.
-vdit_status optional_area(const vdit::AttnArgs& a, size_t off, size_t bytes, char** area) {
-  *area = nullptr;
-  if (bytes == 0 || !a.workspace || a.workspace_bytes < off + bytes) return VDIT_OK;
-  if (!vdit::aligned16(a.workspace)) return fail(VDIT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (vdit::overlaps(a.workspace, off + bytes, a.o, q_bytes(a)))
-    return fail(VDIT_ERR_INVALID_ARG, "workspace overlaps o");
-  *area = static_cast<char*>(a.workspace) + off;
-  return VDIT_OK;
+// workspace holds it, else NULL.  (Its alignment and placement were checked
+// with the other arguments, before anything was enqueued.)
+char* optional_area(const vdit::AttnArgs& a, size_t off, size_t bytes) {
+  if (bytes == 0 || !a.workspace || a.workspace_bytes < off + bytes) return nullptr;
+  return static_cast<char*>(a.workspace) + off;
 }
 
 // Bounded-score softmax: the caller's key-norm bound when given, else the
@@ -113,12 +104,10 @@ vdit_status add_key_bound(vdit::AttnLaunch& p, const vdit::KvSeg& keys, char* ar
 vdit_status launch_plain(vdit::AttnLaunch p, const vdit::AttnArgs& a, hipStream_t stream, const char* what) {
   const int64_t keys = p.nseg ? p.seg[0].len : 0;
   const size_t kb = vdit::kbound_bytes(a);
-  char* bound = nullptr;
-  if (auto st = optional_area(a, 0, kb, &bound); st != VDIT_OK) return st;
+  char* bound = optional_area(a, 0, kb);
   const vdit::SplitPlan sp = vdit::split_plan(a.dtype, a.B, a.Lq, a.n_heads, keys, vdit::device_cus());
   const size_t need = vdit::split_workspace_bytes(sp, a.B, a.Lq, a.n_heads, a.head_dim);
-  char* ws = nullptr;
-  if (auto st = optional_area(a, kb, need, &ws); st != VDIT_OK) return st;
+  char* ws = optional_area(a, kb, need);
   if (ws) {
     p.nsplit = sp.nsplit;
     p.split_keys = sp.split_keys;
@@ -253,11 +242,9 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       // chunk] [one float32 partial per chunk (one-launch form)]
       const size_t req = vdit::ring_workspace_bytes(a), kb = vdit::kbound_bytes(a);
       const size_t run_floats = size_t(a.B) * size_t(a.n_kv_heads) * vdit::kKeyBoundParts;
-      char* bound = nullptr;
-      if (auto st = optional_area(a, req, kb, &bound); st != VDIT_OK) return st;
+      char* bound = optional_area(a, req, kb);
       auto bound_run = [&](int c) -> char* { return bound ? bound + size_t(c) * run_floats * 4 : nullptr; };
-      char* parts = nullptr;
-      if (auto st = optional_area(a, req + kb, vdit::ring_partials_bytes(a), &parts); st != VDIT_OK) return st;
+      char* parts = optional_area(a, req + kb, vdit::ring_partials_bytes(a));
       if (parts) {
         // every chunk at once: split s of the launch attends to chunk s
         vdit::AttnLaunch p = base_launch(a);
@@ -403,8 +390,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       p.hk = a.k;
       p.hv = a.v;
       p.nseg = 1;
-      char* bound = nullptr;
-      if (auto st = optional_area(a, lay.total, vdit::kbound_bytes(a), &bound); st != VDIT_OK) return st;
+      char* bound = optional_area(a, lay.total, vdit::kbound_bytes(a));
       // a bound per chunk (so a chunk's result does not depend on the others);
       // overlapping windows run on the online maximum
       if (a.overlap_tokens == 0)

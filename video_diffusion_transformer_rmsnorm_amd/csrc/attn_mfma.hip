@@ -46,6 +46,7 @@
 //    instruction immediates (the loop is unrolled by two over the buffer
 //    parity).  Workgroup ids are remapped so each XCD walks a contiguous
 //    range of (head, query-tile) work.
+#include <atomic>
 #include <type_traits>
 
 #include "attn_epilogue.hpp"
@@ -225,20 +226,25 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   const int64_t rs = int64_t(p.Hk) * ROWB;  // bytes between consecutive keys
 
   // ------------------------------------------------------------ Q in VGPRs --
+  // (reloaded unscaled by the hybrid epilogue and by a rerun of the main loop)
   bf16x8 Qr[QB][KS];
   const int64_t qw0 = q_begin + wave * 32 * QB;
+  auto load_q = [&]() {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int64_t qrow = qw0 + 32 * qb + r;
-    const bool ok = qrow < q_end;
-    const uint16_t* src = static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.Lq + (ok ? qrow : q_begin)) * p.Hq + h) * D;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int64_t qrow = qw0 + 32 * qb + r;
+      const bool ok = qrow < q_end;
+      const uint16_t* src =
+          static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.Lq + (ok ? qrow : q_begin)) * p.Hq + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 u = *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g);
-      if (!ok) u = make_uint4(0, 0, 0, 0);
-      Qr[qb][ks] = __builtin_bit_cast(bf16x8, u);
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = *reinterpret_cast<const uint4*>(src + 16 * ks + 8 * g);
+        if (!ok) u = make_uint4(0, 0, 0, 0);
+        Qr[qb][ks] = __builtin_bit_cast(bf16x8, u);
+      }
     }
-  }
+  };
+  load_q();
 
   // ---------------------------------------------------- per-lane addresses --
   // direct loads.  K: instruction u (= wave + NW*i) fills padded slots
@@ -703,8 +709,53 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   };
   if (ntiles > 0) {
     if constexpr (NW >= VDIT_ATTN_BOUND_MIN_NW) {
-      if (fast) main_loop(std::true_type{});
-      else main_loop(std::false_type{});
+      const bool bounded = p.kbound != nullptr || p.kbound_sq > 0.f;  // workgroup-uniform
+      for (;;) {
+        if (fast) main_loop(std::true_type{});
+        else main_loop(std::false_type{});
+        if (!bounded) break;
+        // With a true bound every p of a bounded-score row lies in
+        // [2^-32, 2^32] (up to rounding), so its row sum lies in
+        // [2^-64, 2^64] for fewer than 2^31 keys.  A sum outside that range
+        // means a key_norm_max below the keys' real norms: the row may have
+        // overflowed or lost its largest terms to underflow.  Such a
+        // wavefront reloads its queries unscaled and the workgroup runs its
+        // tiles again, that wavefront on the running maximum (the others
+        // repeat their own path, with identical results, to keep the
+        // barriers matched).  A valid bound never takes this branch.
+        bool bad = false;
+        if (fast) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float lt = lsum[qb] + other_half(lsum[qb]);
+            bad = bad || !(lt >= 0x1p-64f && lt <= 0x1p64f);
+          }
+        }
+        bad = __ballot(bad) != 0;
+        // the main loop ended on a barrier after its last LDS read and with
+        // no tile load in flight: the tile buffers are free for the flags
+        int* flags = reinterpret_cast<int*>(lds);
+        if (lane == 0) flags[wave] = bad ? 1 : 0;
+        __syncthreads();
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any |= flags[w];
+        __syncthreads();
+        if (!any) break;
+        if (bad) {
+          fast = false;
+          load_q();
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          m2[qb] = fast ? 0.f : -INFINITY;
+          lsum[qb] = 0.f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[db][qb][i] = 0.f;
+        }
+      }
     } else {
       main_loop(std::false_type{});
     }
@@ -761,7 +812,9 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   }
 
   // chunk-hybrid: O_lin^T = S_c^T phi(Q)^T on the matrix cores (S_c^T held as
-  // bf16 hi + lo planes), den = phi(q)^T z_c in float32
+  // bf16 hi + lo planes), den = phi(q)^T z_c in float32.  phi takes the
+  // queries as stored: the bounded-score path scaled the registers by c2.
+  load_q();
   const int64_t sidx = (chunk_id * p.B + b) * p.Hk + hk;
   const int64_t plane = p.n_chunks * p.B * p.Hk * D * D;
   const uint16_t* st_hi = static_cast<const uint16_t*>(p.st) + sidx * D * D;
@@ -840,15 +893,17 @@ hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
 }  // namespace
 
 int device_cus() {
-  static int cus[64] = {0};
+  // one entry per device, filled on first use; threads that race on an empty
+  // entry all store the same attribute value (relaxed atomics: no torn reads)
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 namespace {

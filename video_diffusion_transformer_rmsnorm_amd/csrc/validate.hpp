@@ -238,6 +238,83 @@ inline int64_t attn_keys(const AttnArgs& a) {
   return a.Lkv;
 }
 
+// A device range one call touches: written ranges (outputs, caches, the
+// state, the workspace) may overlap no other range of the call; ranges that
+// are only read may overlap each other.
+struct Region {
+  const void* p;
+  size_t n;
+  const char* name;
+  bool written;
+};
+
+inline CheckResult check_disjoint(const Region* r, int n) {
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < i; ++j)
+      if ((r[i].written || r[j].written) && overlaps(r[i].p, r[i].n, r[j].p, r[j].n))
+        return CheckResult::bad(std::string(r[i].name) + " overlaps " + r[j].name);
+  return CheckResult::good();
+}
+
+// Aliasing and workspace placement of an attention call (run after the
+// mode's own checks, before anything is launched): the workspace, when given,
+// is 16-byte aligned and, like o, lse, the rolling caches and the hybrid
+// state, overlaps none of the call's other tensors.  The one permitted
+// alias: a ROLLING call with B = 1 may pass the cache slot itself as k / v
+// (the insert is then skipped).
+inline CheckResult check_attn_regions(const AttnArgs& a) {
+  const size_t es = esize(a.dtype), D = size_t(a.head_dim), B = size_t(a.B);
+  const size_t nq = B * size_t(a.Lq) * size_t(a.n_heads) * D * es;
+  const size_t nl = B * size_t(a.n_heads) * size_t(a.Lq) * 4;
+  const size_t row = size_t(a.n_kv_heads) * D * es;  // bytes per key of one batch
+  if (a.workspace && a.workspace_bytes > 0 && !aligned16(a.workspace))
+    return CheckResult::bad("workspace must be 16-byte aligned");
+  Region r[2 * kMaxRingChunks + 8];
+  int n = 0;
+  r[n++] = {a.q, nq, "q", false};
+  r[n++] = {a.o, nq, "o", true};
+  if (a.lse) r[n++] = {a.lse, nl, "lse", true};
+  if (a.workspace) r[n++] = {a.workspace, a.workspace_bytes, "workspace", true};
+  switch (a.mode) {
+    case 0:
+    case 3: {
+      const size_t nk = B * size_t(a.Lkv) * row;
+      r[n++] = {a.k, nk, "k", false};
+      r[n++] = {a.v, nk, "v", false};
+      if (a.mode == 3) {
+        r[n++] = {a.state_s, B * size_t(a.n_kv_heads) * D * D * 4, "state_s", true};
+        r[n++] = {a.state_z, B * size_t(a.n_kv_heads) * D * 4, "state_z", true};
+      }
+      break;
+    }
+    case 1:
+      for (int c = 0; c < a.n_kv_chunks && c < kMaxRingChunks; ++c) {
+        r[n++] = {a.k_chunks[c], B * size_t(a.chunk_len[c]) * row, "a key chunk", false};
+        r[n++] = {a.v_chunks[c], B * size_t(a.chunk_len[c]) * row, "a value chunk", false};
+      }
+      break;
+    case 2: {
+      const size_t frame = size_t(a.Lq) * row;  // one slot of one batch
+      const size_t nc = size_t(a.n_slots) * B * frame;
+      r[n++] = {a.k_cache, nc, "k_cache", true};
+      r[n++] = {a.v_cache, nc, "v_cache", true};
+      const int64_t slot = a.n_slots > 0 ? a.frame % a.n_slots : 0;
+      for (int which = 0; which < 2; ++which) {
+        const void* src = which ? a.v : a.k;
+        const char* cache = static_cast<const char*>(which ? a.v_cache : a.k_cache);
+        if (!src) continue;
+        if (cache && src == cache + size_t(slot) * frame) {
+          if (a.B == 1) continue;  // the slot itself: nothing to copy
+          return CheckResult::bad("ROLLING: k / v may be the cache slot only when B = 1");
+        }
+        r[n++] = {src, B * frame, which ? "v" : "k", false};
+      }
+      break;
+    }
+  }
+  return check_disjoint(r, n);
+}
+
 inline CheckResult check_attn(const AttnArgs& a) {
   if (auto r = check_dtype(a.dtype); !r) return r;
   if (auto r = check_head_dim(a.head_dim); !r) return r;
@@ -290,8 +367,6 @@ inline CheckResult check_attn(const AttnArgs& a) {
       if (need && !empty_q) {
         if (!a.workspace || a.workspace_bytes < need)
           return CheckResult::bad("RING workspace too small (see vdit_attn_workspace_bytes)");
-        if (!aligned16(a.workspace)) return CheckResult::bad("workspace must be 16-byte aligned");
-        if (overlaps(a.workspace, need, a.o, nq)) return CheckResult::bad("workspace overlaps o");
       }
       break;
     }
@@ -304,6 +379,7 @@ inline CheckResult check_attn(const AttnArgs& a) {
           return CheckResult::bad("caches must be 16-byte aligned");
         if ((a.k == nullptr) != (a.v == nullptr))
           return CheckResult::bad("ROLLING: k and v must both be set or both be NULL");
+        if (!aligned16(a.k) || !aligned16(a.v)) return CheckResult::bad("k and v must be 16-byte aligned");
         const size_t nc = size_t(a.n_slots) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_kv_heads) * D * es;
         if (overlaps(a.o, nq, a.k_cache, nc) || overlaps(a.o, nq, a.v_cache, nc))
           return CheckResult::bad("o overlaps a cache");
@@ -327,13 +403,11 @@ inline CheckResult check_attn(const AttnArgs& a) {
         const size_t need = hybrid_layout(a).total;
         if (!a.workspace || a.workspace_bytes < need)
           return CheckResult::bad("CHUNK_HYBRID workspace too small (see vdit_attn_workspace_bytes)");
-        if (!aligned16(a.workspace)) return CheckResult::bad("workspace must be 16-byte aligned");
-        if (overlaps(a.workspace, need, a.o, nq)) return CheckResult::bad("workspace overlaps o");
       }
       break;
     }
   }
-  return CheckResult::good();
+  return check_attn_regions(a);
 }
 
 // Key-norm bound of the bounded-score softmax (bf16): 64 partial maxima per
