@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define VDIT_ABI_VERSION 3
+#define VDIT_ABI_VERSION 4
 
 typedef enum {
   VDIT_OK = 0,
@@ -143,8 +143,9 @@ typedef enum {
  *     each folding its partial into a float32 running partial in
  *     `workspace` (the merge is fused into the attention epilogue); the
  *     last chunk writes o and lse.  Chunk c is read only by launch c.  Taken
- *     for float32, for more than 8 chunks, with the VDIT_ATTN_RING_FOLD flag,
- *     or when the workspace holds only the running partial.
+ *     for float32, for more than 8 chunks, with the VDIT_ATTN_RING_FOLD flag
+ *     (vdit_attn_workspace_bytes then counts no one-launch partials), or
+ *     when the workspace holds only the running partial.
  *   - one launch (bf16, 2..8 chunks, the default when the workspace holds a
  *     float32 partial per chunk): every chunk is attended to in one launch,
  *     whose workgroups cover (chunk, query tile, head), and the partials are
@@ -182,6 +183,18 @@ typedef enum {
  *   (the next call's context), so calling once per chunk equals one call
  *   over the whole sequence.  Needs `workspace` of
  *   vdit_attn_workspace_bytes().
+ *   phi_coef (host array read during the call, or NULL): the review's ledger
+ *   gives phi_q, phi_k as learnable polynomials of degree 3 (Appendix A.3.1
+ *   as quoted there) without coefficients.  With phi_coef = (a0, a1, a2, a3,
+ *   b0, b1, b2, b3), phi_q(x) = a0 + a1 x + a2 x^2 + a3 x^3 on each element
+ *   of q and phi_k(x) = b0 + b1 x + b2 x^2 + b3 x^3 on each element of k
+ *   replace elu + 1 (the state then sums phi_k(k) v^T and phi_k(k)).  The
+ *   normaliser phi_q(q)^T z_c must be positive for the linear term to take
+ *   part: choose coefficients that keep both maps positive on the values
+ *   fed (after an RMSNorm with gain 1 every element lies in
+ *   [-sqrt(D), sqrt(D)]); a row whose normaliser is not positive gets the
+ *   softmax partial alone.  Coefficients must be finite.  NULL in the other
+ *   modes.
  *
  * lse: [B, n_heads, Lq] float32 or NULL.  The ranges a call writes (o,
  * lse, the workspace_bytes bytes at workspace, the rolling caches, the
@@ -235,7 +248,7 @@ typedef struct {
   void* v_cache;               /* ROLLING */
   int64_t frame;               /* ROLLING */
   int32_t n_slots;             /* ROLLING */
-  int32_t reserved0;
+  uint32_t flags;              /* VDIT_ATTN_* flags below (0: none) */
   int64_t chunk_tokens;        /* CHUNK_HYBRID */
   float* state_s;              /* CHUNK_HYBRID */
   float* state_z;              /* CHUNK_HYBRID */
@@ -245,7 +258,12 @@ typedef struct {
   int64_t ctx_tokens;          /* CHUNK_HYBRID (0 in the other modes) */
   float key_norm_max;          /* 0 = computed (see above) */
   int32_t reserved1;
+  const float* phi_coef;       /* CHUNK_HYBRID (host, 8 floats) or NULL = elu + 1 */
 } vdit_attn_args;
+
+/* vdit_attn_args.flags */
+#define VDIT_ATTN_RING_FOLD 1u /* RING: fold the chunks one launch at a time, in
+                                  order, even where one launch could take them all */
 
 /* Bytes of device workspace vdit_attn_fwd needs (RING, CHUNK_HYBRID) or can
  * use (FULL, ROLLING: the key split) for these arguments on the current

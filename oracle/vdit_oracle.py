@@ -311,6 +311,31 @@ def phi(x: np.ndarray) -> np.ndarray:
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
+def phi_poly(x: np.ndarray, coef: Sequence[float]) -> np.ndarray:
+    """Degree-3 polynomial feature map c0 + c1 x + c2 x^2 + c3 x^3, element-wise.
+
+    The MobileWan review's ledger gives the linear attention's feature maps
+    phi_q and phi_k as learnable polynomials of degree 3 (Appendix A.3.1 as
+    the ledger quotes it) and no coefficients; here they are inputs.  For the
+    normaliser phi_q(q)^T z to stay positive the coefficients must keep the
+    polynomial positive on the values it is fed.
+    """
+    x = np.asarray(x, np.float64)
+    c = [float(a) for a in coef]
+    return c[0] + c[1] * x + c[2] * x ** 2 + c[3] * x ** 3
+
+
+def _feature_maps(phi_coef):
+    """(phi_q, phi_k): elu + 1 for both when phi_coef is None, else the two
+    cubics of phi_coef = (a0, a1, a2, a3, b0, b1, b2, b3)."""
+    if phi_coef is None:
+        return phi, phi
+    c = [float(a) for a in phi_coef]
+    if len(c) != 8:
+        raise ValueError("phi_coef holds 4 coefficients for phi_q, then 4 for phi_k")
+    return (lambda x: phi_poly(x, c[:4])), (lambda x: phi_poly(x, c[4:]))
+
+
 def _chunks(L: int, chunk_tokens: int):
     return [(c0, min(c0 + chunk_tokens, L)) for c0 in range(0, L, chunk_tokens)]
 
@@ -364,7 +389,7 @@ def _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap):
 
 
 def hybrid_explicit(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
-                    s0=None, z0=None, overlap: int = 0, ctx: int = 0):
+                    s0=None, z0=None, overlap: int = 0, ctx: int = 0, phi_coef=None):
     """Chunk-hybrid attention, explicit form (MobileWan review, Sec. 3.2).
 
     Query token i in chunk c = [c*C, (c+1)*C) attends with softmax to the keys
@@ -378,15 +403,17 @@ def hybrid_explicit(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
     the first query.  The incoming state (s0, z0) stands for keys before this
     call; the earlier-key sums are formed directly from all earlier keys (no
     running state).  The returned state adds every key but the last
-    `overlap`.  Returns (o, lse, s_final, z_final).
+    `overlap`.  phi_coef (8 floats) replaces elu + 1 by the degree-3
+    polynomials phi_q, phi_k (see phi_poly).  Returns (o, lse, s_final, z_final).
     """
     q, k, v, scale, s0, z0 = _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap)
     B, L, Hq, D = q.shape
     Hk = k.shape[2]
     o = np.zeros((B, L, Hq, D))
     lse = np.zeros((B, Hq, L))
-    fq = phi(q)
-    fk = phi(k)
+    phi_q, phi_k = _feature_maps(phi_coef)
+    fq = phi_q(q)
+    fk = phi_k(k)
     for b in range(B):
         for h in range(Hq):
             kh = _kv_head(h, Hq, Hk)
@@ -408,24 +435,25 @@ def hybrid_explicit(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
 
 
 def hybrid_recurrent(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
-                     s0=None, z0=None, overlap: int = 0, ctx: int = 0):
+                     s0=None, z0=None, overlap: int = 0, ctx: int = 0, phi_coef=None):
     """Chunk-hybrid attention run as an RNN over chunks (MobileWan review,
     Sec. 3.2, Eqs. 5-10 as described): for each chunk, first absorb into the
     running state (s_t, z_t) the keys that now fall before the chunk's
     softmax window (s += phi(k_j) v_j^T, z += phi(k_j)), then read it for the
     cross-chunk term; at the end absorb all keys but the last `overlap`.
-    Window, context and overlap as in hybrid_explicit.  Returns (o, lse, s, z)."""
+    Window, context, overlap and phi_coef as in hybrid_explicit.  Returns (o, lse, s, z)."""
     q, k, v, scale, s, z = _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap)
     B, L, Hq, D = q.shape
     Hk = k.shape[2]
     o = np.zeros((B, L, Hq, D))
     lse = np.zeros((B, Hq, L))
+    phi_q, phi_k = _feature_maps(phi_coef)
     pos = 0  # keys absorbed so far
 
     def absorb(upto):
         nonlocal s, z, pos
         if upto > pos:
-            fk = phi(k[:, pos:upto])
+            fk = phi_k(k[:, pos:upto])
             s = s + np.einsum("blhd,blhe->bhde", fk, v[:, pos:upto])
             z = z + fk.sum(axis=1)
             pos = upto
@@ -434,7 +462,7 @@ def hybrid_recurrent(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
         w0, w1 = _window(c0, c1, ctx, overlap)
         absorb(w0)
         os_, ls_ = attention(q[:, c0:c1], k[:, w0:w1], v[:, w0:w1], scale)
-        fq = phi(q[:, c0:c1])
+        fq = phi_q(q[:, c0:c1])
         for b in range(B):
             for h in range(Hq):
                 kh = _kv_head(h, Hq, Hk)
@@ -448,16 +476,18 @@ def hybrid_recurrent(q, k, v, chunk_tokens: int, scale: Optional[float] = None,
 
 
 def hybrid_partials(q, k, v, chunk_tokens: int, scale: Optional[float] = None, s0=None, z0=None,
-                    overlap: int = 0, ctx: int = 0):
+                    overlap: int = 0, ctx: int = 0, phi_coef=None):
     """The two partials of the hybrid, per token: softmax (o_s, lse_s) over the
     token's window and linear (o_l, lse_l) over the keys before it, with
-    lse_l = ln(phi(q)^T z) (-inf when z = 0).  Used to check each partial on its own."""
+    lse_l = ln(phi_q(q)^T z) (-inf when that is not positive, e.g. z = 0).
+    Used to check each partial on its own."""
     q, k, v, scale, s0, z0 = _hybrid_args(q, k, v, scale, s0, z0, ctx, overlap)
     B, L, Hq, D = q.shape
     Hk = k.shape[2]
     o_s = np.zeros((B, L, Hq, D)); l_s = np.zeros((B, Hq, L))
     o_l = np.zeros((B, L, Hq, D)); l_l = np.full((B, Hq, L), -np.inf)
-    fq = phi(q); fk = phi(k)
+    phi_q, phi_k = _feature_maps(phi_coef)
+    fq = phi_q(q); fk = phi_k(k)
     for c0, c1 in _chunks(L, chunk_tokens):
         w0, w1 = _window(c0, c1, ctx, overlap)
         oc, lc = attention(q[:, c0:c1], k[:, w0:w1], v[:, w0:w1], scale)
@@ -479,5 +509,5 @@ def hybrid_partials(q, k, v, chunk_tokens: int, scale: Optional[float] = None, s
 __all__ = [
     "grid_positions", "rmsnorm", "rope_frequencies", "rope_angles", "rope_rotate", "rope_qk",
     "attention", "attention_probs", "lse_merge", "ring_attention", "rolling_window",
-    "rolling_frame", "phi", "hybrid_explicit", "hybrid_recurrent", "hybrid_partials",
+    "rolling_frame", "phi", "phi_poly", "hybrid_explicit", "hybrid_recurrent", "hybrid_partials",
 ]

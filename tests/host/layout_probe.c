@@ -11,7 +11,7 @@ int main(void) {
   OFF(mode); OFF(dtype); OFF(B); OFF(n_heads); OFF(n_kv_heads); OFF(head_dim);
   OFF(Lq); OFF(Lkv); OFF(scale); OFF(n_kv_chunks); OFF(q); OFF(k); OFF(v); OFF(o); OFF(lse);
   OFF(k_chunks); OFF(v_chunks); OFF(chunk_len); OFF(k_cache); OFF(v_cache); OFF(frame);
-  OFF(n_slots); OFF(reserved0); OFF(chunk_tokens); OFF(state_s); OFF(state_z); OFF(workspace);
-  OFF(workspace_bytes); OFF(overlap_tokens); OFF(ctx_tokens); OFF(key_norm_max); OFF(reserved1);
+  OFF(n_slots); OFF(flags); OFF(chunk_tokens); OFF(state_s); OFF(state_z); OFF(workspace);
+  OFF(workspace_bytes); OFF(overlap_tokens); OFF(ctx_tokens); OFF(key_norm_max); OFF(reserved1); OFF(phi_coef);
   return 0;
 }

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.vdit_abi_version() == V.ABI_VERSION == 3
+    assert lib.vdit_abi_version() == V.ABI_VERSION == 4
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -169,6 +169,25 @@ def test_attn_validation_errors(lib):
         a.key_norm_max = bad
         st = lib.vdit_attn_fwd(ctypes.byref(a), None)
         assert st == V.VDIT_ERR_INVALID_ARG and "key_norm_max" in lib.vdit_last_error().decode()
+    a.key_norm_max = 0.0
+    # flags: unknown bits, and the ring-only fold flag outside RING
+    for flags, word in ((2, "unknown"), (V.VDIT_ATTN_RING_FOLD, "RING")):
+        a.flags = flags
+        st = lib.vdit_attn_fwd(ctypes.byref(a), None)
+        assert st == V.VDIT_ERR_INVALID_ARG and word in lib.vdit_last_error().decode()
+    a.flags = 0
+    # polynomial feature maps: hybrid only, finite
+    coef = (ctypes.c_float * 8)(1, 0.1, 0.01, 0.001, 1, 0.1, 0.01, 0.001)
+    a.phi_coef = ctypes.cast(coef, ctypes.c_void_p)
+    st = lib.vdit_attn_fwd(ctypes.byref(a), None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "CHUNK_HYBRID" in lib.vdit_last_error().decode()
+    a.mode, a.chunk_tokens = 3, 16
+    a.state_s, a.state_z = 5 << 20, 6 << 20
+    coef[5] = float("nan")
+    st = lib.vdit_attn_fwd(ctypes.byref(a), None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "finite" in lib.vdit_last_error().decode()
+    with pytest.raises(ValueError):
+        V.vdit_attn_fwd(None, phi_coef=(1.0, 2.0))
 
 
 def test_workspace_sizes(lib):
@@ -186,6 +205,10 @@ def test_workspace_sizes(lib):
         align(2 * o_bytes) + align(2 * lse_bytes)
     a.dtype = 1  # float32: the fold form only, no key bound
     assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes)
+    a.dtype = 0
+    a.flags = V.VDIT_ATTN_RING_FOLD  # the fold form on request: no one-launch partials
+    assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes) + align(2 * 10 * 64 * 4)
+    a.flags = 0
     a.dtype, a.n_kv_chunks = 0, 9  # more chunks than one launch takes: fold form
     assert V.vdit_attn_workspace_bytes(a) == align(o_bytes) + align(lse_bytes) + align(9 * 10 * 64 * 4)
     a.n_kv_chunks = 1

@@ -39,7 +39,7 @@ def test_rejected_rolling_call_leaves_the_cache_alone():
     # the same call with a proper workspace inserts the frame and matches the oracle
     o, lse = V.vdit_attn_fwd(q, k, v, mode="rolling", k_cache=kc, v_cache=vc, frame=1)
     torch.cuda.synchronize()
-    assert torch.equal(kc[:, 1], k[0]) and torch.equal(vc[:, 1], v[0])
+    assert torch.equal(kc[0, 1], k[0]) and torch.equal(vc[0, 1], v[0])
     K = np.concatenate([from_dev(k0[:, 0]), from_dev(k)], 1); Vv = np.concatenate([from_dev(v0[:, 0]), from_dev(v)], 1)
     wo, wl = O.attention(from_dev(q), K, Vv)
     check(o, wo, "bf16", "O rolling after the rejected calls"); check_lse(lse, wl, "bf16", "LSE")
@@ -52,13 +52,19 @@ def test_rejected_hybrid_call_leaves_the_state_alone():
     log(f"rejected CHUNK_HYBRID call: L={L} H={H} D={D} chunk={C}")
     q, k, v = (to_dev(raw((1, L, H, D), s)) for s in (311, 312, 313))
     rng = np.random.default_rng(314)
-    sd = torch.from_numpy((0.05 * rng.standard_normal((1, H, D, D))).astype(np.float32)).cuda()
-    zd = torch.from_numpy(np.abs(rng.standard_normal((1, H, D))).astype(np.float32)).cuda()
-    s0, z0 = sd.clone(), zd.clone()
-    with pytest.raises(V.VditError, match="overlaps"):
-        V.vdit_attn_fwd(q, k, v, mode="hybrid", chunk_tokens=C, state_s=sd, state_z=zd,
-                        workspace=sd.view(torch.uint8).reshape(-1))
+    s_init = torch.from_numpy((0.05 * rng.standard_normal((1, H, D, D))).astype(np.float32)).cuda()
+    z_init = torch.from_numpy(np.abs(rng.standard_normal((1, H, D))).astype(np.float32)).cuda()
     big = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    # a workspace large enough, with the state inside it
+    s_in_ws = big[1 << 20:(1 << 20) + s_init.numel() * 4].view(torch.float32).view(s_init.shape)
+    s_in_ws.copy_(s_init)
+    zd = z_init.clone()
+    with pytest.raises(V.VditError, match="overlaps"):
+        V.vdit_attn_fwd(q, k, v, mode="hybrid", chunk_tokens=C, state_s=s_in_ws, state_z=zd, workspace=big)
+    torch.cuda.synchronize()
+    assert torch.equal(s_in_ws, s_init) and torch.equal(zd, z_init)
+    sd = s_init.clone()
+    s0, z0 = sd.clone(), zd.clone()
     o_in_ws = big[:q.numel() * 2].view(torch.bfloat16).view(q.shape)
     with pytest.raises(V.VditError, match="overlaps"):
         V.vdit_attn_fwd(q, k, v, mode="hybrid", chunk_tokens=C, state_s=sd, state_z=zd, o=o_in_ws, workspace=big)
@@ -74,11 +80,13 @@ def test_rejected_hybrid_call_leaves_the_state_alone():
 
 @pytest.mark.parametrize("D", [128, 64])
 def test_understated_key_norm_bound_still_correct(D):
-    """key_norm_max far below the keys' norms: keys of norm ~20 sqrt(D) under a
-    claimed bound of sqrt(D).  The bounded-score rows overflow, are detected
-    by their row sums and are recomputed on the running maximum; FULL (256-
-    and 128-query shapes), RING in one launch and ROLLING all match the
-    oracle."""
+    """key_norm_max far below the keys' norms.  Every key gets 20 u and every
+    query u added, for one direction u of norm sqrt(D): the keys' norms grow to
+    ~20 sqrt(D) while a bound of sqrt(D) is claimed, and every score gains the
+    same 20 |u|^2 (softmax is unchanged by it, the bounded path overflows).
+    The overflowing rows are detected by their row sums and recomputed on the
+    running maximum; FULL (256- and 128-query shapes), RING in one launch and
+    ROLLING all match the oracle."""
     H = 8
     pairs = (22, 21, 21) if D == 128 else (12, 10, 10)
     log(f"understated key_norm_max: D={D}")
@@ -86,7 +94,10 @@ def test_understated_key_norm_bound_still_correct(D):
         grid = (1, 1, L)
         q, k, v = (raw((1, L, H, D), 320 + s + L) for s in range(3))
         qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), V.make_grid(*grid, pairs))
-        kr.mul_(20.0)  # exact in bf16 up to one rounding; the oracle gets these values
+        u = np.random.default_rng(330).standard_normal(D)
+        u = torch.from_numpy(u * math.sqrt(D) / np.linalg.norm(u)).to(qr.dtype).cuda()
+        qr.add_(u)
+        kr.add_(20.0 * u)  # rounded to bf16; the oracle gets these values
         vd = to_dev(v)
         knm = math.sqrt(D)
         o, lse = V.vdit_attn_fwd(qr, kr, vd, key_norm_max=knm)

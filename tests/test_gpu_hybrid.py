@@ -33,9 +33,9 @@ pytestmark = pytest.mark.gpu
 STATE_REL = 1e-5
 
 
-def _state_reference(k64, v64, end):
-    """sum_j phi(k_j) v_j^T and sum_j phi(k_j) over keys [0, end) ([B, H, D, D], [B, H, D])."""
-    fk = O.phi(k64[:, :end])                                   # [B, n, H, D]
+def _state_reference(k64, v64, end, phi_coef=None):
+    """sum_j phi_k(k_j) v_j^T and sum_j phi_k(k_j) over keys [0, end) ([B, H, D, D], [B, H, D])."""
+    fk = O.phi(k64[:, :end]) if phi_coef is None else O.phi_poly(k64[:, :end], phi_coef[4:])
     s = np.matmul(fk.transpose(0, 2, 3, 1), v64[:, :end].transpose(0, 2, 1, 3))
     return s, fk.sum(axis=1)
 
@@ -45,7 +45,7 @@ def _softmax_weight_per_chunk(l_s, l_l, L, C):
     return [float(ws[:, :, c0:c0 + C].mean()) for c0 in range(0, L, C)]
 
 
-def _hybrid_full(w, scale, inputs, B=1, key_norm_max=0.0):
+def _hybrid_full(w, scale, inputs, B=1, key_norm_max=0.0, phi_coef=None):
     """RMSNorm + 3D-RoPE and one CHUNK_HYBRID call over the whole grid; O, LSE
     (all rows) and the final state against the oracle fed the library's own
     rotated q, k.  Returns the oracle's mean softmax weight per chunk."""
@@ -56,14 +56,14 @@ def _hybrid_full(w, scale, inputs, B=1, key_norm_max=0.0):
     sd = torch.zeros((B, H, D, D), device="cuda")
     zd = torch.zeros((B, H, D), device="cuda")
     o, lse = V.vdit_attn_fwd(qr, kr, to_dev(v), mode="hybrid", chunk_tokens=C, state_s=sd, state_z=zd,
-                             overlap_tokens=Ov, scale=scale, key_norm_max=key_norm_max)
+                             overlap_tokens=Ov, scale=scale, key_norm_max=key_norm_max, phi_coef=phi_coef)
     torch.cuda.synchronize()
     q64, k64 = from_dev(qr), from_dev(kr)
-    o_s, l_s, o_l, l_l = O.hybrid_partials(q64, k64, v.values, C, scale=scale, overlap=Ov)
+    o_s, l_s, o_l, l_l = O.hybrid_partials(q64, k64, v.values, C, scale=scale, overlap=Ov, phi_coef=phi_coef)
     wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
     check(o, wo, "bf16", f"O hybrid, scale {scale:.4f} (all rows)")
     check_lse(lse, wl, "bf16", f"LSE hybrid, scale {scale:.4f}")
-    ws_, wz = _state_reference(k64, v.values, w.tokens - Ov)
+    ws_, wz = _state_reference(k64, v.values, w.tokens - Ov, phi_coef)
     rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
     rz = np.linalg.norm(from_dev(zd) - wz) / np.linalg.norm(wz)
     log(f"  state relF s={rs:.3e} z={rz:.3e}")
@@ -139,3 +139,48 @@ def test_hybrid_small_both_partials_visible():
     ws_, wz = _state_reference(k64, v.values, L)
     rs = np.linalg.norm(from_dev(sd) - (s0 + ws_)) / np.linalg.norm(s0 + ws_)
     assert rs <= STATE_REL, rs
+
+
+# ------------------------------------------------- polynomial feature maps --
+
+@pytest.mark.parametrize("dtype,D,L,C,Ov,Hq,Hk", [
+    ("bf16", 128, 300, 72, 0, 2, 2), ("bf16", 64, 260, 64, 100, 4, 2), ("bf16", 128, 200, 50, 30, 4, 1),
+    ("f32", 64, 100, 24, 12, 2, 1), ("f32", 128, 70, 16, 0, 2, 2),
+])
+def test_hybrid_polynomial_phi_small(dtype, D, L, C, Ov, Hq, Hk):
+    # degree-3 phi_q, phi_k (MobileWan review ledger, Appendix A.3.1) with
+    # synthetic coefficients; raw N(0,1) inputs, an incoming state
+    coef = WL.poly_phi_coefficients(D)
+    log(f"hybrid, cubic feature maps {dtype} D={D} L={L} chunk={C} overlap={Ov} Hq={Hq} Hk={Hk}")
+    rng = np.random.default_rng(1701 + D + L)
+    q = WL.draw((1, L, Hq, D), rng, dtype); k = WL.draw((1, L, Hk, D), rng, dtype); v = WL.draw((1, L, Hk, D), rng, dtype)
+    s0 = (0.05 * rng.standard_normal((1, Hk, D, D))).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((1, Hk, D))).astype(np.float32)
+    sd = torch.from_numpy(s0).cuda(); zd = torch.from_numpy(z0).cuda()
+    o, lse = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), mode="hybrid", chunk_tokens=C, state_s=sd,
+                             state_z=zd, overlap_tokens=Ov, phi_coef=coef)
+    torch.cuda.synchronize()
+    wo, wl, ws_, wz = O.hybrid_recurrent(q.values, k.values, v.values, C, s0=s0, z0=z0, overlap=Ov, phi_coef=coef)
+    check(o, wo, dtype, "O hybrid (cubic maps)"); check_lse(lse, wl, dtype, "LSE hybrid (cubic maps)")
+    rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
+    rz = np.linalg.norm(from_dev(zd) - wz) / np.linalg.norm(wz)
+    log(f"  state relF s={rs:.3e} z={rz:.3e}")
+    assert rs <= STATE_REL and rz <= STATE_REL
+    # the maps matter: elu + 1 gives a different output
+    o_elu, _ = V.vdit_attn_fwd(to_dev(q), to_dev(k), to_dev(v), mode="hybrid", chunk_tokens=C,
+                               state_s=torch.from_numpy(s0).cuda(), state_z=torch.from_numpy(z0).cuda(),
+                               overlap_tokens=Ov)
+    torch.cuda.synchronize()
+    assert float((o_elu.float() - o.float()).abs().max()) > 1e-2
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("number,scale", [(5, None), (5, 0.35), (8, None)])
+def test_hybrid_polynomial_phi_full_size(number, scale):
+    w = WL.WORKLOADS[number]
+    sc = scale if scale is not None else 1.0 / math.sqrt(w.head_dim)
+    coef = WL.poly_phi_coefficients(w.head_dim)
+    log(f"{w.name} with cubic feature maps: chunk {w.chunk_tokens}, overlap {w.overlap_tokens}, scale {sc:.4f}")
+    weights = _hybrid_full(w, sc, WL.workload_inputs(w), phi_coef=coef)
+    if scale is not None:
+        _balanced(weights)

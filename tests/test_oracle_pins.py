@@ -451,10 +451,14 @@ def test_phi_is_elu_plus_one():
     assert np.allclose(O.phi(np.linspace(-5, 5, 101)), t.numpy(), atol=1e-15)
 
 
-def _hybrid_brute(q, k, v, C, scale, overlap=0):
+def _elu1(x):
+    return x + 1 if x > 0 else math.exp(x)
+
+
+def _hybrid_brute(q, k, v, C, scale, overlap=0, fmap_q=_elu1, fmap_k=_elu1):
     # Full L x L weight matrix by loops: key in the query's chunk or in the
     # `overlap` tokens before that chunk -> e^{s_ij}; any earlier key ->
-    # phi(q_i).phi(k_j); later key -> 0.  O = W V / W 1.
+    # phi_q(q_i).phi_k(k_j); later key -> 0.  O = W V / W 1.
     B, L, H, D = q.shape
     out = np.zeros_like(q)
     for h in range(H):
@@ -466,8 +470,8 @@ def _hybrid_brute(q, k, v, C, scale, overlap=0):
                     s = scale * math.fsum(q[0, i, h, d] * k[0, j, h, d] for d in range(D))
                     wts.append(math.exp(s))
                 elif j < start - overlap:
-                    fq = [q[0, i, h, d] + 1 if q[0, i, h, d] > 0 else math.exp(q[0, i, h, d]) for d in range(D)]
-                    fk = [k[0, j, h, d] + 1 if k[0, j, h, d] > 0 else math.exp(k[0, j, h, d]) for d in range(D)]
+                    fq = [fmap_q(q[0, i, h, d]) for d in range(D)]
+                    fk = [fmap_k(k[0, j, h, d]) for d in range(D)]
                     wts.append(math.fsum(a * b for a, b in zip(fq, fk)))
                 else:
                     wts.append(0.0)
@@ -475,6 +479,85 @@ def _hybrid_brute(q, k, v, C, scale, overlap=0):
             for d in range(D):
                 out[0, i, h, d] = math.fsum(wts[j] * v[0, j, h, d] for j in range(L)) / den
     return out
+
+
+# Degree-3 feature maps (MobileWan review, ledger: polynomial phi_q, phi_k of
+# degree 3, Appendix A.3.1).  Synthetic coefficients, positive on [-3, 3].
+POLY = (1.0, 0.3, 0.05, 0.004, 0.8, -0.2, 0.06, 0.003)
+
+
+def test_phi_poly_coefficient_order():
+    # c0 + c1 x + c2 x^2 + c3 x^3 at hand-computed points
+    assert O.phi_poly(np.array([2.0]), (1.0, 0.5, 0.25, 0.125))[0] == 4.0
+    assert O.phi_poly(np.array([-2.0]), (1.0, 0.5, 0.25, 0.125))[0] == 0.0
+    assert O.phi_poly(np.array([3.0]), (0.0, 0.0, 0.0, 1.0))[0] == 27.0
+    assert O.phi_poly(np.array([3.0]), (0.0, 0.0, 1.0, 0.0))[0] == 9.0
+    x = np.linspace(-4, 4, 33)
+    assert np.allclose(O.phi_poly(x, POLY[4:]), np.polynomial.polynomial.polyval(x, POLY[4:]), atol=1e-14)
+
+
+@pytest.mark.parametrize("overlap", [0, 3])
+def test_hybrid_polynomial_phi_matches_brute_force(overlap):
+    r = RNG(70 + overlap)
+    q = r.standard_normal((1, 11, 2, 4)); k = r.standard_normal((1, 11, 2, 4))
+    v = r.standard_normal((1, 11, 2, 4))
+    fq = lambda x: float(np.polynomial.polynomial.polyval(x, POLY[:4]))
+    fk = lambda x: float(np.polynomial.polynomial.polyval(x, POLY[4:]))
+    want = _hybrid_brute(q, k, v, 4, 0.5, overlap, fq, fk)
+    o_e, _, _, _ = O.hybrid_explicit(q, k, v, 4, 0.5, overlap=overlap, phi_coef=POLY)
+    o_r, _, _, _ = O.hybrid_recurrent(q, k, v, 4, 0.5, overlap=overlap, phi_coef=POLY)
+    assert np.allclose(o_e, want, atol=1e-12)
+    assert np.allclose(o_r, want, atol=1e-12)
+    # phi_q and phi_k are not interchangeable, and differ from elu + 1
+    swapped = POLY[4:] + POLY[:4]
+    o_s, _, _, _ = O.hybrid_explicit(q, k, v, 4, 0.5, overlap=overlap, phi_coef=swapped)
+    o_elu, _, _, _ = O.hybrid_explicit(q, k, v, 4, 0.5, overlap=overlap)
+    assert np.abs(o_s - want).max() > 1e-4 and np.abs(o_elu - want).max() > 1e-4
+
+
+def test_hybrid_polynomial_phi_closed_forms():
+    r = RNG(73)
+    B, L, H, D, C = 1, 12, 2, 8, 4
+    q = r.standard_normal((B, L, H, D)); k = r.standard_normal((B, L, H, D))
+    v = r.standard_normal((B, L, H, D))
+    # constant maps phi_q = a, phi_k = b: every earlier key weighs D a b, so the
+    # linear partial is the mean of the earlier values and its LSE ln(n D a b)
+    a, b = 0.7, 1.3
+    _, _, o_l, l_l = O.hybrid_partials(q, k, v, C, phi_coef=(a, 0, 0, 0, b, 0, 0, 0))
+    for c0 in range(C, L, C):
+        assert np.allclose(o_l[:, c0:c0 + C], v[:, :c0].mean(axis=1, keepdims=True), atol=1e-13)
+        assert np.allclose(l_l[:, :, c0:c0 + C], math.log(c0 * D * a * b), atol=1e-13)
+    # pure cubes: phi_q(q).phi_k(k) = sum_d q_d^3 k_d^3
+    _, _, o_l, l_l = O.hybrid_partials(q, k, v, C, phi_coef=(0, 0, 0, 1, 0, 0, 0, 1))
+    i, h, c0 = 9, 1, 8
+    w = [math.fsum(q[0, i, h, d] ** 3 * k[0, j, h, d] ** 3 for d in range(D)) for j in range(c0)]
+    den = math.fsum(w)
+    if den > 0:
+        assert abs(l_l[0, h, i] - math.log(den)) < 1e-12
+        for d in range(D):
+            assert abs(o_l[0, i, h, d] - math.fsum(w[j] * v[0, j, h, d] for j in range(c0)) / den) < 1e-12
+    else:  # a normaliser that is not positive drops the linear partial
+        assert np.isneginf(l_l[0, h, i]) and not o_l[0, i, h].any()
+
+
+def test_hybrid_polynomial_recurrent_equals_explicit_and_state():
+    r = RNG(74)
+    B, L, Hq, Hk, D, C, Ov = 2, 29, 4, 2, 8, 7, 3
+    q = r.standard_normal((B, L, Hq, D)); k = r.standard_normal((B, L, Hk, D))
+    v = r.standard_normal((B, L, Hk, D))
+    s0 = r.standard_normal((B, Hk, D, D)) * 0.1; z0 = np.abs(r.standard_normal((B, Hk, D)))
+    e = O.hybrid_explicit(q, k, v, C, s0=s0, z0=z0, overlap=Ov, phi_coef=POLY)
+    rr = O.hybrid_recurrent(q, k, v, C, s0=s0, z0=z0, overlap=Ov, phi_coef=POLY)
+    for x, y in zip(e, rr):
+        assert np.allclose(x, y, atol=1e-11)
+    s_want = s0.copy(); z_want = z0.copy()
+    for bb in range(B):
+        for h in range(Hk):
+            for j in range(L - Ov):
+                fk = np.polynomial.polynomial.polyval(k[bb, j, h], POLY[4:])
+                s_want[bb, h] += np.outer(fk, v[bb, j, h])
+                z_want[bb, h] += fk
+    assert np.allclose(rr[2], s_want, atol=1e-11) and np.allclose(rr[3], z_want, atol=1e-11)
 
 
 def test_hybrid_matches_brute_force_weight_matrix():

@@ -21,7 +21,8 @@ VDIT_BF16, VDIT_F32 = 0, 1
 VDIT_ROPE_NO_NORM = 1
 VDIT_ROPE_NO_Q_NORM = 2
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
-ABI_VERSION = 3
+ABI_VERSION = 4
+VDIT_ATTN_RING_FOLD = 1
 
 # Every symbol include/vdit.h declares.
 EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_workspace_bytes",
@@ -50,12 +51,13 @@ class VditAttnArgs(ctypes.Structure):
         ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("k_chunks", ctypes.c_void_p), ("v_chunks", ctypes.c_void_p), ("chunk_len", ctypes.c_void_p),
         ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
-        ("frame", ctypes.c_int64), ("n_slots", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("frame", ctypes.c_int64), ("n_slots", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("chunk_tokens", ctypes.c_int64),
         ("state_s", ctypes.c_void_p), ("state_z", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("overlap_tokens", ctypes.c_int64), ("ctx_tokens", ctypes.c_int64),
         ("key_norm_max", ctypes.c_float), ("reserved1", ctypes.c_int32),
+        ("phi_coef", ctypes.c_void_p),
     ]
 
 
@@ -194,7 +196,8 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
                   scale: float = 0.0, k_chunks=None, v_chunks=None, k_cache=None, v_cache=None,
                   frame: int = 0, chunk_tokens: int = 0, state_s=None, state_z=None, workspace=None,
                   n_kv_heads: Optional[int] = None, overlap_tokens: int = 0, ctx_tokens: int = 0,
-                  key_norm_max: float = 0.0, stream=None):
+                  key_norm_max: float = 0.0, phi_coef: Optional[Sequence[float]] = None,
+                  ring_fold: bool = False, stream=None):
     """One attention call.  Returns (o, lse) (lse None unless wanted).
 
     full:    k, v [B,Lkv,Hk,D].
@@ -205,10 +208,15 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     hybrid:  k, v [B,ctx_tokens+Lq,Hk,D]; chunk_tokens; state_s [B,Hk,D,D], state_z [B,Hk,D]
              float32 (in/out); overlap_tokens keys before each chunk join its softmax
              window; the first ctx_tokens (<= overlap_tokens) keys precede the first query.
-    key_norm_max: 0, or a guaranteed bound on every key's norm, which replaces the
-             library's pass over the keys (see vdit.h).
+    key_norm_max: 0, or a bound on every key's norm, which replaces the library's pass
+             over the keys (see vdit.h).
+    phi_coef: hybrid only: 8 floats, the cubics phi_q (a0..a3) and phi_k (b0..b3) that
+             replace elu + 1 in the linear term.
+    ring_fold: ring only: fold the chunks one launch at a time (VDIT_ATTN_RING_FOLD).
     """
     import torch
+    if phi_coef is not None and len(phi_coef) != 8:
+        raise ValueError("phi_coef: 4 coefficients of phi_q, then 4 of phi_k")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (k_cache, "k_cache"),
                  (v_cache, "v_cache"), (state_s, "state_s"), (state_z, "state_z"), (workspace, "workspace")):
         _dev(t, n)
@@ -247,6 +255,12 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
         hk = k.shape[2]
         a = _attn_args(q, k, v, mode, o, lse, scale, n_kv_heads or hk, k.shape[1])
     a.key_norm_max = key_norm_max
+    if ring_fold:
+        a.flags |= VDIT_ATTN_RING_FOLD
+    if phi_coef is not None:
+        coef = (ctypes.c_float * 8)(*[float(c) for c in phi_coef])
+        keep.append(coef)
+        a.phi_coef = ctypes.cast(coef, ctypes.c_void_p)
     need = vdit_attn_workspace_bytes(a)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -275,5 +289,5 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-__all__ = ["vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
+__all__ = ["VDIT_ATTN_RING_FOLD", "vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
            "VditGrid", "VditAttnArgs", "VditError", "lib", "EXPORTS", "LIB_PATH"]

@@ -64,6 +64,25 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+PROBES_SRC = os.path.join(CSRC, "probes", "mfma_peak.hip")
+PROBES_LIB = os.path.join(PKG, "libvdit_probes.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """Compile the measurement probes the benchmark uses (not part of the
+    library's ABI) into libvdit_probes.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = PROBES_LIB + ".tmp"
+    cmd = [hipcc(), *COMMON, "-shared", PROBES_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBES_LIB)
+    if verbose:
+        print(f"built {PROBES_LIB}")
+    return PROBES_LIB
+
+
 CONSUMER_SRC = os.path.join(ROOT, "tests", "host", "c_consumer.c")
 CONSUMER = os.path.join(ROOT, "tests", "host", "c_consumer")
 
@@ -90,4 +109,5 @@ def build_consumer(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_probes(verbose=True)
     build_consumer(verbose=True)

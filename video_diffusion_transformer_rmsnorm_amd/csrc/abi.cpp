@@ -21,6 +21,10 @@ static_assert(offsetof(vdit_attn_args, ctx_tokens) == offsetof(vdit::AttnArgs, c
               "vdit_attn_args layout mirror");
 static_assert(offsetof(vdit_attn_args, key_norm_max) == offsetof(vdit::AttnArgs, key_norm_max),
               "vdit_attn_args layout mirror");
+static_assert(offsetof(vdit_attn_args, flags) == offsetof(vdit::AttnArgs, flags), "vdit_attn_args layout mirror");
+static_assert(offsetof(vdit_attn_args, phi_coef) == offsetof(vdit::AttnArgs, phi_coef),
+              "vdit_attn_args layout mirror");
+static_assert(VDIT_ATTN_RING_FOLD == vdit::kAttnRingFold, "flag mirror");
 
 namespace {
 
@@ -68,6 +72,18 @@ vdit::AttnLaunch base_launch(const vdit::AttnArgs& a) {
 
 hipError_t launch_attn(const vdit::AttnLaunch& p, int dtype, hipStream_t s) {
   return dtype == VDIT_BF16 ? vdit::launch_attn_bf16(p, s) : vdit::launch_attn_f32(p, s);
+}
+
+// phi_q (first = 0) or phi_k (first = 4) of a hybrid call: elu + 1 when the
+// caller gives no coefficients.
+vdit::FeatureMap feature_map(const float* coef, int first) {
+  vdit::FeatureMap f;
+  std::memset(&f, 0, sizeof(f));
+  if (coef) {
+    f.poly = 1;
+    for (int i = 0; i < 4; ++i) f.c[i] = coef[first + i];
+  }
+  return f;
 }
 
 // Optional workspace area [off, off + bytes): usable when the caller's
@@ -374,6 +390,8 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       hs.Hk = a.n_kv_heads;
       hs.D = a.head_dim;
       hs.dtype = a.dtype;
+      const vdit::FeatureMap fq = feature_map(a.phi_coef, 0), fk = feature_map(a.phi_coef, 4);
+      hs.phi_k = fk;
       if (auto st = from_hip(vdit::launch_hybrid_state(hs, stream), "vdit_attn_fwd(CHUNK_HYBRID) state");
           st != VDIT_OK)
         return st;
@@ -389,6 +407,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       p.zc = reinterpret_cast<const float*>(ws + lay.off_zc);
       p.hk = a.k;
       p.hv = a.v;
+      p.phi_q = fq;
       p.nseg = 1;
       char* bound = optional_area(a, lay.total, vdit::kbound_bytes(a));
       // a bound per chunk (so a chunk's result does not depend on the others);

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "vdit_internal.hpp"
 
 namespace vdit {
 
@@ -35,5 +36,10 @@ __device__ __forceinline__ MergeW merge_weights(float la, float lb) {
 
 // phi(x) = elu(x) + 1
 __device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+// The linear term's feature map: elu + 1, or the map's cubic (Horner form).
+__device__ __forceinline__ float feature(float x, const FeatureMap& f) {
+  return f.poly ? fmaf(fmaf(fmaf(f.c[3], x, f.c[2]), x, f.c[1]), x, f.c[0]) : phi_elu1(x);
+}
 
 }  // namespace vdit

@@ -836,7 +836,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       bf16x8 f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = phi_elu1(static_cast<float>(Qr[qb][ks][j]));
+        const float x = feature(static_cast<float>(Qr[qb][ks][j]), p.phi_q);
         dn = fmaf(x, zz[j], dn);
         f[j] = static_cast<__bf16>(x);
       }

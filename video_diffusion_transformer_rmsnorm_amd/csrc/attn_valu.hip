@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kValuBM) void attn_valu_kernel(AttnLaunch p, int64_
   float den = 0.f;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    fq[d] = phi_elu1(qv[d]);
+    fq[d] = feature(qv[d], p.phi_q);
     den = fmaf(fq[d], z[d], den);
   }
   const float lse_l = den > 0.f ? logf(den) : -INFINITY;

@@ -4,7 +4,7 @@
 // Sec. 3.2) runs the hybrid attention as an RNN over chunks whose fixed-size
 // state (s_t, z_t) summarises every earlier chunk through causal linear
 // attention: s += phi(K_c)^T V_c, z += sum_j phi(k_j) after chunk c, with
-// phi = elu + 1.  Chunk c's queries need the state *before* it, S_c.  When
+// phi = elu + 1 or the caller's cubic phi_k.  Chunk c's queries need the state *before* it, S_c.  When
 // the softmax windows overlap (the window of chunk c starts `overlap` keys
 // before the chunk), S_c covers the keys before that window instead, so the
 // delta of chunk c runs from the start of its window to the start of the
@@ -66,10 +66,10 @@ __global__ __launch_bounds__(kDeltaThreads) void hybrid_delta_kernel(HybridState
       if (jj < nv) {
         const int64_t off = ((int64_t(b) * p.Lkv + j0 + jj) * p.Hk + hk) * D + d;
         if constexpr (BF16) {
-          kx = phi_elu1(bf16_to_f32(static_cast<const uint16_t*>(p.k)[off]));
+          kx = feature(bf16_to_f32(static_cast<const uint16_t*>(p.k)[off]), p.phi_k);
           vx = bf16_to_f32(static_cast<const uint16_t*>(p.v)[off]);
         } else {
-          kx = phi_elu1(static_cast<const float*>(p.k)[off]);
+          kx = feature(static_cast<const float*>(p.k)[off], p.phi_k);
           vx = static_cast<const float*>(p.v)[off];
         }
       }
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void hybrid_delta_mfma_kernel(HybridStateLaunc
       bf16x8 bh, bl;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float f = phi_elu1(bf16_to_f32(static_cast<uint16_t>(kr[j])));
+        float f = feature(bf16_to_f32(static_cast<uint16_t>(kr[j])), p.phi_k);
         if (16 * kk + 8 * g + j >= nv) f = 0.f;
         zacc += f;
         const __bf16 h = static_cast<__bf16>(f);

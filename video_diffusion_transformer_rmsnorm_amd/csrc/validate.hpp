@@ -131,7 +131,7 @@ struct AttnArgs {
   void* v_cache;
   int64_t frame;
   int32_t n_slots;
-  int32_t reserved0;
+  uint32_t flags;
   int64_t chunk_tokens;
   float* state_s;
   float* state_z;
@@ -141,7 +141,10 @@ struct AttnArgs {
   int64_t ctx_tokens;
   float key_norm_max;
   int32_t reserved1;
+  const float* phi_coef;
 };
+
+constexpr uint32_t kAttnRingFold = 1u;  // VDIT_ATTN_RING_FOLD
 
 constexpr int kMaxRingChunks = 64;
 
@@ -236,6 +239,18 @@ inline int64_t attn_keys(const AttnArgs& a) {
     return nvalid * a.Lq;
   }
   return a.Lkv;
+}
+
+// flags and the hybrid's polynomial feature maps
+inline CheckResult check_attn_options(const AttnArgs& a) {
+  if (a.flags & ~kAttnRingFold) return CheckResult::bad("unknown attention flags");
+  if ((a.flags & kAttnRingFold) && a.mode != 1) return CheckResult::bad("VDIT_ATTN_RING_FOLD belongs to RING");
+  if (a.phi_coef) {
+    if (a.mode != 3) return CheckResult::bad("phi_coef belongs to CHUNK_HYBRID (NULL otherwise)");
+    for (int i = 0; i < 8; ++i)
+      if (!std::isfinite(a.phi_coef[i])) return CheckResult::bad("phi_coef must be finite");
+  }
+  return CheckResult::good();
 }
 
 // A device range one call touches: written ranges (outputs, caches, the
@@ -336,6 +351,7 @@ inline CheckResult check_attn(const AttnArgs& a) {
     return CheckResult::bad("key_norm_max must be finite and >= 0");
   if (a.mode != 3 && (a.overlap_tokens != 0 || a.ctx_tokens != 0))
     return CheckResult::bad("overlap_tokens and ctx_tokens belong to CHUNK_HYBRID (0 otherwise)");
+  if (auto r = check_attn_options(a); !r) return r;
   switch (a.mode) {
     case 0: {  // FULL
       if (a.Lkv > 0 && !empty_q) {
@@ -443,7 +459,8 @@ inline size_t attn_required_bytes(const AttnArgs& a) {
 // folded one launch at a time into the required running partial.
 constexpr int kRingOneLaunchMax = 8;  // key segments one attention launch takes
 inline bool ring_one_launch(const AttnArgs& a) {
-  return a.mode == 1 && a.dtype == 0 && a.n_kv_chunks >= 2 && a.n_kv_chunks <= kRingOneLaunchMax;
+  return a.mode == 1 && a.dtype == 0 && a.n_kv_chunks >= 2 && a.n_kv_chunks <= kRingOneLaunchMax &&
+         !(a.flags & kAttnRingFold);
 }
 inline size_t ring_partials_bytes(const AttnArgs& a) {
   if (!ring_one_launch(a)) return 0;
@@ -480,7 +497,7 @@ inline CheckResult check_attn_shape(const AttnArgs& a) {
   if (b.mode == 1 && (b.n_kv_chunks < 1 || b.n_kv_chunks > kMaxRingChunks))
     return CheckResult::bad("RING needs 1 <= n_kv_chunks <= 64");
   if (b.mode == 3 && b.chunk_tokens < 1) return CheckResult::bad("CHUNK_HYBRID needs chunk_tokens >= 1");
-  return CheckResult::good();
+  return check_attn_options(b);
 }
 
 inline CheckResult check_merge(const void* o_a, const float* lse_a, const void* o_b,

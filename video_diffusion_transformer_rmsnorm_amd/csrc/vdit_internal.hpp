@@ -19,6 +19,13 @@ struct KvSeg {
   int64_t bstride;  // elements between batches
 };
 
+// Feature map of the chunk-hybrid's linear term: elu(x) + 1, or (poly set)
+// the cubic c[0] + c[1] x + c[2] x^2 + c[3] x^3, element-wise.
+struct FeatureMap {
+  float c[4];
+  int32_t poly;
+};
+
 enum Epilogue : int32_t {
   kEpiPlain = 0,   // write normalised O (+ LSE)
   kEpiRing = 1,    // fold into / out of a float32 running partial
@@ -53,6 +60,7 @@ struct AttnLaunch {
   const float* zc;   // [n_chunks][B][Hk][D]
   const void* hk;    // key / value base of the whole sequence (hybrid)
   const void* hv;
+  FeatureMap phi_q;  // applied to the queries (hybrid)
   // key split (plain attention): nsplit ranges of split_keys keys; range s
   // writes its partial to part_o / part_lse offset by s whole partials
   int32_t nsplit;
@@ -160,6 +168,7 @@ struct HybridStateLaunch {
   int32_t nsplit;
   int32_t B, Hk, D;
   int32_t dtype;       // of k, v; also selects the S_c format
+  FeatureMap phi_k;    // applied to the keys
 };
 hipError_t launch_hybrid_state(const HybridStateLaunch& p, hipStream_t s);
 

@@ -102,6 +102,20 @@ WORKLOADS = {
 }
 
 
+def poly_phi_coefficients(head_dim: int) -> tuple:
+    """Synthetic coefficients (a0..a3, b0..b3) of degree-3 feature maps phi_q,
+    phi_k for the chunk-hybrid's linear term (the pages give the degree, not
+    the learned values).  In y = x / R with R = sqrt(head_dim) (1 + 2^-7), the
+    largest element of a row RMS-normalised with gain 1 (and rounded to
+    bf16), they are 1 + y/2 + y^2/4 + y^3/8 and 1 - y/3 + y^2/5 + y^3/10, both
+    between 0.6 and 1.9 on [-1, 1]; returned as float32-representable
+    numbers in powers of x."""
+    R = float(np.sqrt(head_dim)) * (1.0 + 2.0 ** -7)
+    py = (1.0, 1 / 2, 1 / 4, 1 / 8, 1.0, -1 / 3, 1 / 5, 1 / 10)
+    c = [py[i] / R ** (i % 4) for i in range(8)]
+    return tuple(float(np.float32(x)) for x in c)
+
+
 def hybrid_flops(w: "Workload") -> float:
     """Matmul FLOPs of the chunk-hybrid's softmax part: each chunk's queries
     against its window (its own keys plus the overlap before them)."""
@@ -196,5 +210,6 @@ def ceil_div(a: int, b: int) -> int:
 __all__ = [
     "Workload", "WORKLOADS", "Tensor", "draw", "draw_qkv", "workload_inputs",
     "f32_to_bf16_bits", "bf16_bits_to_f64", "flops_full", "hybrid_flops", "sample_rows", "ceil_div",
+    "poly_phi_coefficients",
 ]
 
