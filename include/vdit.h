@@ -225,9 +225,8 @@ typedef enum {
  * true bound keeps every row sum of the bounded path within [2^-64, 2^64],
  * and a wavefront whose row sums leave that range (overflow, or its largest
  * terms lost to underflow) is detected when its workgroup has seen all its
- * keys; the workgroup then runs its keys again with that wavefront on the
- * running maximum.  Negative or non-finite: VDIT_ERR_INVALID_ARG.  Ignored
- * by float32 calls.
+ * keys; the workgroup then runs its keys once more on the running maximum.
+ * Negative or non-finite: VDIT_ERR_INVALID_ARG.  Ignored by float32 calls.
  */
 typedef struct {
   int32_t mode;  /* vdit_attn_mode */

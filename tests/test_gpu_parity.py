@@ -496,12 +496,17 @@ def test_batch_of_two_ring_rolling_hybrid(dtype):
 
 
 @pytest.mark.slow
-def test_ring_shard_14b_sampled_rows():
+@pytest.mark.parametrize("half,fold", [(0, True), (0, False), (1, True)])
+def test_ring_shard_14b_sampled_rows(half, fold):
+    # the query shard is frames 0-9 (the first half) or frames 10-19 (the
+    # second) of the 20 x 30 x 52 grid; the ring folds the two key chunks in
+    # order (the ring step's form) or attends to both in one launch
     w = WL.WORKLOADS[3]
-    log("14B-shaped shard: Q 15600, K/V 2 x 15600, 10 heads, ring of 2 + LSE merge, sampled rows")
+    log(f"14B-shaped shard: Q = half {half} (15600), K/V 2 x 15600, 10 heads, ring of 2 + LSE merge, "
+        f"{'fold' if fold else 'one launch'}, sampled rows")
     q, k, v = WL.workload_inputs(w)
     g = V.make_grid(*w.grid, w.pairs)
-    q0, q1 = w.q_range
+    q0, q1 = half * w.q_range[1], w.q_range[1]
     qd = to_dev(q)[:, q0:q0 + q1].contiguous()
     kd, vd = to_dev(k), to_dev(v)
     qr, _ = V.vdit_rope_qk(qd, None, g, token0=q0)
@@ -510,7 +515,7 @@ def test_ring_shard_14b_sampled_rows():
         _, kc = V.vdit_rope_qk(None, kd[:, s:s + n].contiguous(), g, token0=s)
         kchunks.append(kc)
     vchunks = [vd[:, s:s + n].contiguous() for (s, n) in w.kv_chunks]
-    o, lse = V.vdit_attn_fwd(qr, mode="ring", k_chunks=kchunks, v_chunks=vchunks)
+    o, lse = V.vdit_attn_fwd(qr, mode="ring", k_chunks=kchunks, v_chunks=vchunks, ring_fold=fold)
     torch.cuda.synchronize()
     wq, wk = O.rope_qk(q.values, k.values, w.grid, w.pairs)
     rows = WL.sample_rows(q1, 160, seed=9)
@@ -619,15 +624,15 @@ def test_rolling_kv_norm_gqa_stream(dtype, D, frame_grid, prefill):
 
 @pytest.mark.slow
 def test_rolling_decode_shape_sampled():
+    # the whole 64-frame stream through the 5-slot cache (the ring buffer
+    # wraps twelve times), checked on frames across it
     w = WL.WORKLOADS[4]
-    F = 8
+    F = w.n_frames
     log(f"rolling decode 2040 tokens x 16 heads x 64, 5 slots, {F} frames, sampled rows")
-    q, k, v = WL.workload_inputs(w)
-    sub = lambda t: WL.Tensor(t.values[:F], None if t.bits is None else t.bits[:F], t.dtype)
-    qf, kf, vf = sub(q), sub(k), sub(v)
+    qf, kf, vf = WL.workload_inputs(w)
     outs = _rolling_run(qf, kf, vf, w.grid, w.pairs, w.n_slots, F)
     rows = WL.sample_rows(w.tokens, 96, seed=10)
-    for f in (0, 3, 4, 7):
+    for f in (0, 3, 4, 7, 31, 62, 63):
         wo, wl = _rolling_oracle_rows(qf, kf, vf, f, w, rows)
         check(from_dev(outs[f][0])[:, rows], wo, "bf16", f"O frame {f} (sampled)")
         check_lse(from_dev(outs[f][1])[:, :, rows], wl, "bf16", f"LSE frame {f} (sampled)")

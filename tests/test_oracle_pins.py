@@ -206,12 +206,38 @@ def test_attention_matches_torch_sdpa_f64(Hq, Hk):
     assert np.allclose(lse, logsumexp(s, axis=-1), atol=1e-12)
 
 
+def test_attention_probs_brute_force_and_against_attention():
+    # The softmax weight matrix: rows sum to one (the benchmark spec), each entry is
+    # e^{s_ij} / sum_k e^{s_ik} by loops (scale and GQA head map included),
+    # P V is attention's output and ln of the row normaliser its LSE.
+    r = RNG(15)
+    B, Lq, Lk, Hq, Hk, D, scale = 2, 5, 7, 4, 2, 6, 0.45
+    q = r.standard_normal((B, Lq, Hq, D)); k = r.standard_normal((B, Lk, Hk, D))
+    v = r.standard_normal((B, Lk, Hk, D))
+    P = O.attention_probs(q, k, scale)
+    assert P.shape == (B, Hq, Lq, Lk)
+    assert np.allclose(P.sum(-1), 1.0, atol=1e-14) and (P >= 0).all()
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // (Hq // Hk)
+            for i in range(Lq):
+                e = [math.exp(scale * math.fsum(q[b, i, h, d] * k[b, j, kh, d] for d in range(D))) for j in range(Lk)]
+                z = math.fsum(e)
+                for j in range(Lk):
+                    assert abs(P[b, h, i, j] - e[j] / z) < 1e-14
+    o, lse = O.attention(q, k, v, scale)
+    rep = Hq // Hk
+    pv = np.einsum("bhij,bjhd->bihd", P, np.repeat(v, rep, axis=2))
+    assert np.allclose(pv, o, atol=1e-13)
+    # a score shifted by a constant per row leaves P unchanged: the LSE is the
+    # only row-dependent normaliser, so ln P_ij = s_ij - LSE_i
+    s = scale * np.einsum("bihd,bjhd->bhij", q, np.repeat(k, rep, axis=2))
+    assert np.allclose(np.log(P), s - lse[..., None], atol=1e-12)
+
+
 def test_attention_special_cases():
     r = RNG(12)
     q = r.standard_normal((1, 6, 1, 8))
-    # rows of P sum to one
-    P = O.attention_probs(q, r.standard_normal((1, 9, 1, 8)))
-    assert np.allclose(P.sum(-1), 1.0, atol=1e-14) and (P >= 0).all()
     # identical keys -> mean of V
     k = np.repeat(r.standard_normal((1, 1, 1, 8)), 5, axis=1)
     v = r.standard_normal((1, 5, 1, 8))

@@ -67,11 +67,17 @@ _lib_handle = None
 def lib() -> ctypes.CDLL:
     """Load libvdit.so (once).  Raises if it is missing."""
     global _lib_handle
-    if _lib_handle is not None:
-        return _lib_handle
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m video_diffusion_transformer_rmsnorm_amd.build`")
-    h = ctypes.CDLL(LIB_PATH)
+    if _lib_handle is None:
+        _lib_handle = load(LIB_PATH)
+    return _lib_handle
+
+
+def load(path: str) -> ctypes.CDLL:
+    """A handle on a build of the library at `path` with the ABI's signatures
+    (lib() uses libvdit.so next to this file)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m video_diffusion_transformer_rmsnorm_amd.build`")
+    h = ctypes.CDLL(path)
     vp, i32, i64, f32, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint32
     h.vdit_rope_qk.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, ctypes.POINTER(VditGrid),
                                i64, i64, vp, vp, f32, u32, vp]
@@ -88,7 +94,6 @@ def lib() -> ctypes.CDLL:
     h.vdit_last_error.restype = ctypes.c_char_p
     h.vdit_abi_version.argtypes = []
     h.vdit_abi_version.restype = ctypes.c_int32
-    _lib_handle = h
     return h
 
 

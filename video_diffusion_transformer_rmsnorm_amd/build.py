@@ -39,8 +39,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra, tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -48,20 +48,31 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile all sources and link libvdit.so; returns its path."""
+DEBUG_SYNC_LIB = os.path.join(PKG, "libvdit_debugsync.so")
+
+
+def build(verbose: bool = False, extra=(), lib: str = LIB, tag: str = "") -> str:
+    """Compile all sources and link libvdit.so (or `lib`, objects suffixed
+    `tag`); returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra), tag), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build_debug_sync(verbose: bool = False) -> str:
+    """The self-check build of the library (VDIT_DEBUG_SYNC=1: every pipeline
+    stage of the attention kernel ends on a full wait and a barrier), which
+    the GPU tests compare bit for bit with libvdit.so."""
+    return build(verbose, extra=("-DVDIT_DEBUG_SYNC=1",), lib=DEBUG_SYNC_LIB, tag=".debugsync")
 
 
 PROBES_SRC = os.path.join(CSRC, "probes", "mfma_peak.hip")
@@ -109,5 +120,6 @@ def build_consumer(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_debug_sync(verbose=True)
     build_probes(verbose=True)
     build_consumer(verbose=True)

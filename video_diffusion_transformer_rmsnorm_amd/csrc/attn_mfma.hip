@@ -73,6 +73,9 @@
 #ifndef VDIT_ATTN_VPREF
 #define VDIT_ATTN_VPREF 2  // V^T operand read pairs issued ahead of their MFMA
 #endif
+#ifndef VDIT_DEBUG_SYNC
+#define VDIT_DEBUG_SYNC 0  // 1: self-check build, every pipeline stage ends on a full wait + barrier
+#endif
 
 namespace vdit {
 namespace {
@@ -660,6 +663,17 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
+  // Self-check build (VDIT_DEBUG_SYNC=1): the tile loads of an iteration are
+  // waited for before any of its LDS reads, and each region ends on a
+  // workgroup barrier, so no LDS write can overlap a read of the same bytes
+  // from another stage.  Same arithmetic in the same order: its results must
+  // equal the pipelined build's bit for bit.
+  auto debug_sync = [&]() {
+    if constexpr (VDIT_DEBUG_SYNC != 0) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  };
 
   auto main_loop = [&](auto fastc) {
     constexpr bool FAST = decltype(fastc)::value;
@@ -682,6 +696,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       // stream K_{t+2} into K buffer P0 and V_{t+1} into V buffer 1-P0
       if (t + 2 < ntiles) issue(t + 2, false, P0);
       if (t + 1 < ntiles) issue(t + 1, true, 1 - P0);
+      debug_sync();
       if constexpr (FAST) mask_tail(S, min(kBN, len - t * kBN));
       else row_max(S, mx, min(kBN, len - t * kBN));
       // region A: exps of tile t || S^T of tile t+1 (computed on the last
@@ -691,8 +706,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       __builtin_amdgcn_sched_barrier(0);
       i16x8 vpre[VP];
       region_a(1 - P0, Sn, S, P, fastc, P0, vpre);
+      debug_sync();
       // region B: O^T += V^T P^T || lane max of tile t+1's scores
       region_b(P0, S, P, Sn, mx, std::integral_constant<bool, !FAST>{}, vpre);
+      debug_sync();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -709,20 +726,18 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   };
   if (ntiles > 0) {
     if constexpr (NW >= VDIT_ATTN_BOUND_MIN_NW) {
-      const bool bounded = p.kbound != nullptr || p.kbound_sq > 0.f;  // workgroup-uniform
-      for (;;) {
-        if (fast) main_loop(std::true_type{});
-        else main_loop(std::false_type{});
-        if (!bounded) break;
-        // With a true bound every p of a bounded-score row lies in
-        // [2^-32, 2^32] (up to rounding), so its row sum lies in
-        // [2^-64, 2^64] for fewer than 2^31 keys.  A sum outside that range
-        // means a key_norm_max below the keys' real norms: the row may have
-        // overflowed or lost its largest terms to underflow.  Such a
-        // wavefront reloads its queries unscaled and the workgroup runs its
-        // tiles again, that wavefront on the running maximum (the others
-        // repeat their own path, with identical results, to keep the
-        // barriers matched).  A valid bound never takes this branch.
+      if (fast) main_loop(std::true_type{});
+      else main_loop(std::false_type{});
+      // With a true bound every p of a bounded-score row lies in
+      // [2^-32, 2^32] (up to rounding), so its row sum lies in [2^-64, 2^64]
+      // for fewer than 2^31 keys.  A sum outside that range means a
+      // key_norm_max below the keys' real norms: the row may have overflowed
+      // or lost its largest terms to underflow.  Then the whole workgroup
+      // runs its tiles once more (the barriers must match), every wavefront
+      // on the running maximum with its queries reloaded unscaled.  A valid
+      // bound never takes this branch.  (A second pass rather than a loop
+      // around the first: loop-carried accumulators would spill.)
+      if (p.kbound != nullptr || p.kbound_sq > 0.f) {  // workgroup-uniform
         bool bad = false;
         if (fast) {
 #pragma unroll
@@ -741,19 +756,19 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
         for (int w = 0; w < NW; ++w) any |= flags[w];
         __syncthreads();
-        if (!any) break;
-        if (bad) {
+        if (any) {
           fast = false;
           load_q();
-        }
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          m2[qb] = fast ? 0.f : -INFINITY;
-          lsum[qb] = 0.f;
+          for (int qb = 0; qb < QB; ++qb) {
+            m2[qb] = -INFINITY;
+            lsum[qb] = 0.f;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) O[db][qb][i] = 0.f;
+              for (int i = 0; i < 16; ++i) O[db][qb][i] = 0.f;
+          }
+          main_loop(std::false_type{});
         }
       }
     } else {
