@@ -274,6 +274,24 @@ size_t vdit_attn_workspace_bytes(const vdit_attn_args* args /* host */);
 vdit_status vdit_attn_fwd(const vdit_attn_args* args /* host */, hipStream_t stream);
 
 /*
+ * vdit_attn_fwd_noalloc -- vdit_attn_fwd for callers that cannot allocate
+ * device memory (code under graph capture, serving loops, harnesses that
+ * forbid allocation): the workspace is the library's own device scratch, a
+ * static array of 64 MiB per device (held until the process ends), instead
+ * of a caller's buffer.  args->workspace must be NULL and workspace_bytes 0
+ * (else VDIT_ERR_INVALID_ARG); a call whose required workspace (RING with
+ * several chunks, CHUNK_HYBRID: the part vdit_attn_workspace_bytes reports
+ * beyond the optional key-norm and key-split areas) exceeds 64 MiB fails
+ * with VDIT_ERR_UNSUPPORTED before anything is enqueued.  The optional areas
+ * are used when they fit.  Results are those of vdit_attn_fwd with a
+ * workspace of that size.  Allocates nothing: the scratch's device address
+ * is looked up on the first call on each device.  All calls on one device
+ * share the scratch, so calls that overlap in time on one device (several
+ * streams or threads) race; serialise them.
+ */
+vdit_status vdit_attn_fwd_noalloc(const vdit_attn_args* args /* host */, hipStream_t stream);
+
+/*
  * vdit_lse_merge -- combine two attention partials over disjoint key sets:
  *   L = ln(e^{L_a} + e^{L_b}),  O = e^{L_a - L} O_a + e^{L_b - L} O_b,
  * the online-softmax combination of ring attention (ReGenVC, USP

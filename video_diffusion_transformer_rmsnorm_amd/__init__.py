@@ -25,7 +25,7 @@ ABI_VERSION = 4
 VDIT_ATTN_RING_FOLD = 1
 
 # Every symbol include/vdit.h declares.
-EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_workspace_bytes",
+EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_attn_workspace_bytes",
            "vdit_lse_merge", "vdit_last_error", "vdit_abi_version")
 
 
@@ -86,6 +86,8 @@ def load(path: str) -> ctypes.CDLL:
     h.vdit_rms_norm.restype = ctypes.c_int
     h.vdit_attn_fwd.argtypes = [ctypes.POINTER(VditAttnArgs), vp]
     h.vdit_attn_fwd.restype = ctypes.c_int
+    h.vdit_attn_fwd_noalloc.argtypes = [ctypes.POINTER(VditAttnArgs), vp]
+    h.vdit_attn_fwd_noalloc.restype = ctypes.c_int
     h.vdit_attn_workspace_bytes.argtypes = [ctypes.POINTER(VditAttnArgs)]
     h.vdit_attn_workspace_bytes.restype = ctypes.c_size_t
     h.vdit_lse_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, vp]
@@ -202,7 +204,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
                   frame: int = 0, chunk_tokens: int = 0, state_s=None, state_z=None, workspace=None,
                   n_kv_heads: Optional[int] = None, overlap_tokens: int = 0, ctx_tokens: int = 0,
                   key_norm_max: float = 0.0, phi_coef: Optional[Sequence[float]] = None,
-                  ring_fold: bool = False, stream=None):
+                  ring_fold: bool = False, stream=None, _noalloc: bool = False):
     """One attention call.  Returns (o, lse) (lse None unless wanted).
 
     full:    k, v [B,Lkv,Hk,D].
@@ -266,6 +268,10 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
         coef = (ctypes.c_float * 8)(*[float(c) for c in phi_coef])
         keep.append(coef)
         a.phi_coef = ctypes.cast(coef, ctypes.c_void_p)
+    if _noalloc:
+        _check(lib().vdit_attn_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+        del keep
+        return o, lse
     need = vdit_attn_workspace_bytes(a)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -275,6 +281,15 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     _check(lib().vdit_attn_fwd(ctypes.byref(a), _stream(stream)))
     del keep
     return o, lse
+
+
+def vdit_attn_fwd_noalloc(q, k=None, v=None, mode: str = "full", o=None, lse=None, **kw):
+    """vdit_attn_fwd with the library's own device scratch as the workspace
+    (no workspace argument, nothing allocated by the library; o and lse must
+    be passed, or are allocated here by torch).  Same arguments otherwise."""
+    if kw.get("workspace") is not None:
+        raise ValueError("vdit_attn_fwd_noalloc takes no workspace")
+    return vdit_attn_fwd(q, k, v, mode=mode, o=o, lse=lse, _noalloc=True, **kw)
 
 
 def vdit_lse_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, out_dtype=None, stream=None):
@@ -294,5 +309,5 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-__all__ = ["VDIT_ATTN_RING_FOLD", "vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
+__all__ = ["VDIT_ATTN_RING_FOLD", "vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
            "VditGrid", "VditAttnArgs", "VditError", "lib", "EXPORTS", "LIB_PATH"]

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libvdit.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "rope_qk.hip", "lse_merge.hip", "attn_mfma.hip", "attn_valu.hip", "hybrid_state.hip",
-           "key_bound.hip"]
+           "key_bound.hip", "noalloc.hip"]
 
 # Packed float32 VALU forms are disabled on purpose: the compiler otherwise
 # forms them from ordinary float code.

@@ -154,6 +154,15 @@ vdit_status launch_plain(vdit::AttnLaunch p, const vdit::AttnArgs& a, hipStream_
 
 }  // namespace
 
+namespace vdit {
+// Records msg as the calling thread's vdit_last_error() and returns status
+// (for entry points defined outside this file).
+int report_error(int status, const char* msg) {
+  g_last_error = msg;
+  return status;
+}
+}  // namespace vdit
+
 extern "C" {
 
 const char* vdit_last_error(void) { return g_last_error.c_str(); }

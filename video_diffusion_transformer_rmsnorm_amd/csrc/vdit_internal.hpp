@@ -91,6 +91,9 @@ hipError_t launch_attn_f32(const AttnLaunch& p, hipStream_t s);
 // Compute units of the current device (cached per device).
 int device_cus();
 
+// Sets the calling thread's vdit_last_error() message; returns status.
+int report_error(int status, const char* msg);
+
 // Whether the bf16 kernel chosen for p uses the key-norm bound (p.kbound).
 bool attn_uses_key_bound(const AttnLaunch& p);
 
