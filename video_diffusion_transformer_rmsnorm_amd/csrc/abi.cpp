@@ -99,7 +99,7 @@ char* optional_area(const vdit::AttnArgs& a, size_t off, size_t bytes) {
 // only), or nothing when there is no area.
 vdit_status add_key_bound(vdit::AttnLaunch& p, const vdit::KvSeg& keys, char* area, hipStream_t stream,
                           float key_norm_max, int64_t part_len = 0) {
-  if (keys.len <= 0 || !vdit::attn_uses_key_bound(p)) return VDIT_OK;
+  if (keys.len <= 0 || !vdit::attn_uses_key_bound(p, key_norm_max > 0.f)) return VDIT_OK;
   if (key_norm_max > 0.f) {
     p.kbound_sq = key_norm_max * key_norm_max;
     return VDIT_OK;
@@ -287,9 +287,9 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
         p.part_o = reinterpret_cast<float*>(parts);
         p.part_lse = reinterpret_cast<float*>(
             parts + vdit::align256(size_t(n) * size_t(a.B) * size_t(a.Lq) * size_t(a.n_heads) * size_t(D) * 4));
-        if (a.key_norm_max > 0.f && all_keys && vdit::attn_uses_key_bound(p)) {
+        if (a.key_norm_max > 0.f && all_keys && vdit::attn_uses_key_bound(p, true)) {
           p.kbound_sq = a.key_norm_max * a.key_norm_max;
-        } else if (bound && all_keys && vdit::attn_uses_key_bound(p)) {
+        } else if (bound && all_keys && vdit::attn_uses_key_bound(p, false)) {
           for (int c = 0; c < n; ++c)
             if (auto st = from_hip(vdit::launch_key_bound(p.seg[c], p.B, p.Hk, p.D, 0,
                                                           reinterpret_cast<float*>(bound_run(c)), stream),
@@ -420,8 +420,9 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       p.nseg = 1;
       char* bound = optional_area(a, lay.total, vdit::kbound_bytes(a));
       // a bound per chunk (so a chunk's result does not depend on the others);
-      // overlapping windows run on the online maximum
-      if (a.overlap_tokens == 0)
+      // overlapping windows run on the online maximum unless the caller gives
+      // a bound for every key
+      if (a.overlap_tokens == 0 || a.key_norm_max > 0.f)
         if (auto st = add_key_bound(p, vdit::KvSeg{a.k, a.v, a.Lq, a.Lq * a.n_kv_heads * D}, bound, stream,
                                     a.key_norm_max, a.chunk_tokens);
             st != VDIT_OK)

@@ -739,7 +739,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       // around the first: loop-carried accumulators would spill.)
       if (p.kbound != nullptr || p.kbound_sq > 0.f) {  // workgroup-uniform
         bool bad = false;
-        if (fast) {
+        if (fast && qw0 < q_end) {  // (a wave past the block's end has no rows)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const float lt = lsum[qb] + other_half(lsum[qb]);
@@ -826,15 +826,44 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     return;
   }
 
-  // chunk-hybrid: O_lin^T = S_c^T phi(Q)^T on the matrix cores (S_c^T held as
-  // bf16 hi + lo planes), den = phi(q)^T z_c in float32.  phi takes the
-  // queries as stored: the bounded-score path scaled the registers by c2.
-  load_q();
+  // chunk-hybrid: O_lin^T = S_c^T phi(Q)^T on the matrix cores (S_c^T and
+  // phi(q) in bf16, float32 accumulation), den = phi(q)^T z_c in float32.
+  // phi takes the queries as stored: the bounded-score path scaled the
+  // registers by c2.
+  //
+  // S_c^T of the workgroup's (chunk, batch, kv head) is read from memory once
+  // per workgroup into LDS (the tile buffers are free after the main loop):
+  // row dout at 2 D dout bytes, its 16-byte chunk c at position
+  // c ^ swz_k(dout), so the rows one operand read touches fall in distinct
+  // bank groups.  Every wave then reads its A operands there.
   const int64_t sidx = (chunk_id * p.B + b) * p.Hk + hk;
-  const int64_t plane = p.n_chunks * p.B * p.Hk * D * D;
-  const uint16_t* st_hi = static_cast<const uint16_t*>(p.st) + sidx * D * D;
-  const uint16_t* st_lo = st_hi + plane;
+  const char* st = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.st) + sidx * D * D);
   const float* z = p.zc + sidx * D;
+  {
+    constexpr int SC_BYTES = D * D * 2;
+    static_assert(SC_BYTES <= 2 * KTILE_B + 2 * TILE_B, "S_c fits the tile buffers");
+    constexpr int NCH = D * CPR;             // 16-byte chunks of S_c^T
+    constexpr int PER = NCH / (64 * NW);     // per thread
+    constexpr int BATCH = PER < 8 ? PER : 8;
+    static_assert(PER * 64 * NW == NCH && PER % BATCH == 0, "S_c staging mapping");
+#pragma unroll
+    for (int i0 = 0; i0 < PER; i0 += BATCH) {
+      uint4 buf[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int e = tid + 64 * NW * (i0 + i);
+        buf[i] = *reinterpret_cast<const uint4*>(st + (e / CPR) * ROWB + (e % CPR) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int e = tid + 64 * NW * (i0 + i), row = e / CPR, c = e % CPR;
+        *reinterpret_cast<uint4*>(lds + row * ROWB + ((c ^ swz_k<D>(row)) * 16)) = buf[i];
+      }
+    }
+    __syncthreads();
+  }
+  if (qw0 >= q_end) return;  // a wave with no queries (the last tile of a chunk)
+  load_q();
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lsum[qb] + other_half(lsum[qb]);
@@ -869,12 +898,11 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
       for (int i = 0; i < 16; ++i) A[i] = 0.f;
       const int dout = 32 * db + r;
+      const char* srow = lds + dout * ROWB;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(st_hi + dout * D + 16 * ks + 8 * g);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(st_lo + dout * D + 16 * ks + 8 * g);
-        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, Fq[ks], A, 0, 0, 0);
-        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, Fq[ks], A, 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(srow + (((2 * ks + g) ^ swz_k<D>(dout)) * 16));
+        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Fq[ks], A, 0, 0, 0);
       }
       if (q < q_end) {
 #pragma unroll
@@ -953,11 +981,12 @@ int attn_waves(const AttnLaunch& p) {
 
 // The key-norm pre-pass pays for itself where each query sees many keys:
 // the chunk-hybrid's 128-query workgroups see one chunk (about a thousand
-// keys) and run faster on the online maximum alone.
-bool attn_uses_key_bound(const AttnLaunch& p) {
+// keys) and run faster on the online maximum alone, unless the caller's
+// bound makes the pre-pass unnecessary.
+bool attn_uses_key_bound(const AttnLaunch& p, bool caller_bound) {
   const int nw = attn_waves(p);
   if (VDIT_ATTN_BIG_QB != 1 || nw < VDIT_ATTN_BOUND_MIN_NW) return false;
-  return nw == 8 || p.epi != kEpiHybrid;
+  return nw == 8 || p.epi != kEpiHybrid || caller_bound;
 }
 
 hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {

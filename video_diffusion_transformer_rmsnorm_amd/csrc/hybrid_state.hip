@@ -4,12 +4,13 @@
 // Sec. 3.2) runs the hybrid attention as an RNN over chunks whose fixed-size
 // state (s_t, z_t) summarises every earlier chunk through causal linear
 // attention: s += phi(K_c)^T V_c, z += sum_j phi(k_j) after chunk c, with
-// phi = elu + 1 or the caller's cubic phi_k.  Chunk c's queries need the state *before* it, S_c.  When
-// the softmax windows overlap (the window of chunk c starts `overlap` keys
-// before the chunk), S_c covers the keys before that window instead, so the
-// delta of chunk c runs from the start of its window to the start of the
-// next one (hybrid_delta_range) and the outgoing state leaves out the last
-// `overlap` keys, which the next call receives as context.
+// phi = elu + 1 or the caller's cubic phi_k.  Chunk c's queries need the
+// state *before* it, S_c.  When the softmax windows overlap (the window of
+// chunk c starts `overlap` keys before the chunk), S_c covers the keys
+// before that window instead, so the delta of chunk c runs from the start
+// of its window to the start of the next one (hybrid_delta_range) and the
+// outgoing state leaves out the last `overlap` keys, which the next call
+// receives as context.
 //
 // Instead of a serial loop over chunks this is a two-pass scan:
 //  1. delta pass: every (chunk, token split, batch, kv head) workgroup forms
@@ -18,9 +19,9 @@
 //  2. scan pass: one lane per state element walks the chunks in order,
 //     writing S_c (exclusive prefix, starting from the incoming state) and
 //     adding the chunk's split deltas; it ends by writing the outgoing state.
-//     For bf16 models S_c is written as a bf16 hi + lo pair (the attention
-//     kernel consumes it on the matrix cores with ~16 significant bits);
-//     for float32 models as float32.
+//     For bf16 models S_c is written in bf16 (the operand of the attention
+//     kernel's matrix-core epilogue, next to phi(q) in bf16; the running
+//     state itself stays float32); for float32 models as float32.
 #include "attn_epilogue.hpp"
 #include "device_common.hpp"
 #include "vdit_internal.hpp"
@@ -110,8 +111,10 @@ __device__ __forceinline__ int dswz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// Three workgroups per CU (<= 168 registers): more tile loads in flight for
+// this memory-bound pass.
 template <int D>
-__global__ __launch_bounds__(256) void hybrid_delta_mfma_kernel(HybridStateLaunch p) {
+__global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLaunch p) {
   constexpr int CPR = D / 8;               // 16-byte chunks per row
   constexpr int ROWB = 2 * D;              // bytes per token row
   constexpr int NB = D / 32;               // 32-channel blocks
@@ -243,16 +246,12 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
   const bool is_z = e >= D * D;
   const int dout = is_z ? 0 : e / D, din = is_z ? e - D * D : e % D;
   float run = is_z ? p.z_in[bh * D + din] : p.s_in[bh * D * D + int64_t(din) * D + dout];
-  const int64_t plane = p.n_chunks * int64_t(p.B) * p.Hk * D * D;
   for (int64_t c = 0; c < p.n_chunks; ++c) {
     const int64_t cs = c * p.B * p.Hk + bh;  // [c][b][hk]
     if (is_z) {
       p.zc[cs * D + din] = run;
     } else if constexpr (BF16) {
-      uint16_t* hi = static_cast<uint16_t*>(p.sc) + cs * D * D + e;
-      const uint16_t h = f32_to_bf16(run);
-      hi[0] = h;
-      hi[plane] = f32_to_bf16(run - bf16_to_f32(h));
+      static_cast<uint16_t*>(p.sc)[cs * D * D + e] = f32_to_bf16(run);
     } else {
       static_cast<float*>(p.sc)[cs * D * D + e] = run;
     }

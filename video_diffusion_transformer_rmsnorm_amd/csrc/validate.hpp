@@ -152,7 +152,7 @@ constexpr int kMaxRingChunks = 64;
 // base, each region 256-byte aligned):
 //   dS   [n_chunks][nsplit][B][Hk][D][D] float32   per-split chunk state deltas (transposed: [d_out][d_in])
 //   dz   [n_chunks][nsplit][B][Hk][D]    float32
-//   S_c  [n_chunks][B][Hk][D][D]         float32 (F32 path) or 2 x bf16 hi/lo (BF16 path), transposed
+//   S_c  [n_chunks][B][Hk][D][D]         float32 (F32 path) or bf16 (BF16 path, half the area), transposed
 //   z_c  [n_chunks][B][Hk][D]            float32
 struct HybridLayout {
   int64_t n_chunks = 0;
@@ -183,7 +183,7 @@ inline HybridLayout hybrid_layout(const AttnArgs& a) {
   size_t off = 0;
   h.off_ds = off; off = align256(off + nc * ns * B * Hk * D * D * 4);
   h.off_dz = off; off = align256(off + nc * ns * B * Hk * D * 4);
-  h.off_sc = off; off = align256(off + nc * B * Hk * D * D * 4);  // f32, or hi+lo bf16 (same bytes)
+  h.off_sc = off; off = align256(off + nc * B * Hk * D * D * 4);  // f32 (bf16 uses half)
   h.off_zc = off; off = align256(off + nc * B * Hk * D * 4);
   h.total = off;
   return h;

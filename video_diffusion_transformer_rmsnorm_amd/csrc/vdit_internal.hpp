@@ -56,7 +56,7 @@ struct AttnLaunch {
   int64_t hyb_ctx;
   int64_t hyb_overlap;
   int64_t hyb_lkv;
-  const void* st;    // per chunk state S_c^T [n_chunks][B][Hk][D][D]: bf16 hi,lo pairs or float32
+  const void* st;    // per chunk state S_c^T [n_chunks][B][Hk][D][D]: bf16 or float32
   const float* zc;   // [n_chunks][B][Hk][D]
   const void* hk;    // key / value base of the whole sequence (hybrid)
   const void* hv;
@@ -94,8 +94,9 @@ int device_cus();
 // Sets the calling thread's vdit_last_error() message; returns status.
 int report_error(int status, const char* msg);
 
-// Whether the bf16 kernel chosen for p uses the key-norm bound (p.kbound).
-bool attn_uses_key_bound(const AttnLaunch& p);
+// Whether the bf16 kernel chosen for p uses the key-norm bound (p.kbound or
+// p.kbound_sq); caller_bound: the caller supplies it (no pre-pass needed).
+bool attn_uses_key_bound(const AttnLaunch& p, bool caller_bound);
 
 // Merge of nsplit float32 attention partials ([nsplit][B][L][H][D] normalised
 // O, [nsplit][B][H][L] LSE) into o (out_dtype) and lse (may be NULL).
@@ -164,7 +165,7 @@ struct HybridStateLaunch {
   float* z_out;
   float* ds;           // [n_chunks][nsplit][B][Hk][D][D] transposed (d_out, d_in)
   float* dz;           // [n_chunks][nsplit][B][Hk][D]
-  void* sc;            // per-chunk state, transposed, bf16 hi/lo pairs or float32
+  void* sc;            // per-chunk state, transposed, bf16 or float32
   float* zc;
   int64_t L, chunk, n_chunks;  // L: query tokens (chunks are defined on them)
   int64_t Lkv, ctx, overlap;   // key tokens (= ctx + L), context keys, softmax overlap
