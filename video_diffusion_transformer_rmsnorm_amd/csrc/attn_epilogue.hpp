@@ -34,12 +34,21 @@ __device__ __forceinline__ MergeW merge_weights(float la, float lb) {
   return w;
 }
 
-// phi(x) = elu(x) + 1
-__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// phi(x) = elu(x) + 1; e^x for x <= 0 as 2^(x log2 e) on the hardware exp2
+// (relative error below 1e-6 for |x| < 16, far under the bf16 rounding the
+// map's values go through)
+__device__ __forceinline__ float phi_elu1(float x) {
+  return x > 0.f ? x + 1.f : __builtin_amdgcn_exp2f(x * kLog2e);
+}
 
 // The linear term's feature map: elu + 1, or the map's cubic (Horner form).
+template <bool POLY>
+__device__ __forceinline__ float feature_t(float x, const FeatureMap& f) {
+  if constexpr (POLY) return fmaf(fmaf(fmaf(f.c[3], x, f.c[2]), x, f.c[1]), x, f.c[0]);
+  else return phi_elu1(x);
+}
 __device__ __forceinline__ float feature(float x, const FeatureMap& f) {
-  return f.poly ? fmaf(fmaf(fmaf(f.c[3], x, f.c[2]), x, f.c[1]), x, f.c[0]) : phi_elu1(x);
+  return f.poly ? feature_t<true>(x, f) : feature_t<false>(x, f);
 }
 
 }  // namespace vdit

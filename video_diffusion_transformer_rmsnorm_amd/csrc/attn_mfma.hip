@@ -872,20 +872,24 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     const int64_t q = qw0 + 32 * qb + r;
     bf16x8 Fq[KS];
     float dn = 0.f;
+    auto features = [&](auto polyc) {  // the map chosen once, not per element
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
-      const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
-      const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
-      bf16x8 f;
+      for (int ks = 0; ks < KS; ++ks) {
+        const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
+        const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
+        const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+        bf16x8 f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = feature(static_cast<float>(Qr[qb][ks][j]), p.phi_q);
-        dn = fmaf(x, zz[j], dn);
-        f[j] = static_cast<__bf16>(x);
+        for (int j = 0; j < 8; ++j) {
+          const float x = feature_t<decltype(polyc)::value>(static_cast<float>(Qr[qb][ks][j]), p.phi_q);
+          dn = fmaf(x, zz[j], dn);
+          f[j] = static_cast<__bf16>(x);
+        }
+        Fq[ks] = f;
       }
-      Fq[ks] = f;
-    }
+    };
+    if (p.phi_q.poly) features(std::true_type{});
+    else features(std::false_type{});
     const float den = dn + other_half(dn);
     const float lse_l = den > 0.f ? logf(den) : -INFINITY;
     const MergeW w = merge_weights(lse_s, lse_l);

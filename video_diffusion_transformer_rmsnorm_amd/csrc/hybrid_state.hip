@@ -32,7 +32,7 @@ namespace {
 constexpr int kDeltaThreads = 256;
 constexpr int kDeltaBN = 32;  // tokens per LDS tile
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool POLY>
 __global__ __launch_bounds__(kDeltaThreads) void hybrid_delta_kernel(HybridStateLaunch p) {
   constexpr int NO = D * D / kDeltaThreads;  // outputs per thread
   constexpr int TPR = D / NO;                // threads per d_in row
@@ -67,10 +67,10 @@ __global__ __launch_bounds__(kDeltaThreads) void hybrid_delta_kernel(HybridState
       if (jj < nv) {
         const int64_t off = ((int64_t(b) * p.Lkv + j0 + jj) * p.Hk + hk) * D + d;
         if constexpr (BF16) {
-          kx = feature(bf16_to_f32(static_cast<const uint16_t*>(p.k)[off]), p.phi_k);
+          kx = feature_t<POLY>(bf16_to_f32(static_cast<const uint16_t*>(p.k)[off]), p.phi_k);
           vx = bf16_to_f32(static_cast<const uint16_t*>(p.v)[off]);
         } else {
-          kx = feature(static_cast<const float*>(p.k)[off], p.phi_k);
+          kx = feature_t<POLY>(static_cast<const float*>(p.k)[off], p.phi_k);
           vx = static_cast<const float*>(p.v)[off];
         }
       }
@@ -112,8 +112,9 @@ __device__ __forceinline__ int dswz(int row) {
 }
 
 // Three workgroups per CU (<= 168 registers): more tile loads in flight for
-// this memory-bound pass.
-template <int D>
+// this memory-bound pass.  POLY: the caller's cubic feature map (a template
+// parameter, so the map costs no branch per element).
+template <int D, bool POLY>
 __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLaunch p) {
   constexpr int CPR = D / 8;               // 16-byte chunks per row
   constexpr int ROWB = 2 * D;              // bytes per token row
@@ -167,7 +168,8 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
   const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Lkv * p.Hk + hk) * D;
 
   // tile loads run one tile ahead in registers: tile j+1 is in flight while
-  // tile j is on the matrix cores
+  // tile j is on the matrix cores.  Rows past the split's end load row 0 of
+  // the tile (which exists) and are masked to zero: no branch per row.
   constexpr int NCH = kMDeltaBN * CPR / 256;  // 16-byte chunks per thread per tile
   static_assert(NCH * 256 == kMDeltaBN * CPR, "tile chunks per thread");
   uint4 kpre[NCH], vpre[NCH];
@@ -176,13 +178,13 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int e = tid + 256 * c, row = e / CPR, ch = e % CPR;
-      kpre[c] = make_uint4(0, 0, 0, 0);
-      vpre[c] = kpre[c];
-      if (row < nv) {
-        const int64_t off = (j0 + row) * tok_stride + ch * 8;
-        kpre[c] = *reinterpret_cast<const uint4*>(kg + off);
-        vpre[c] = *reinterpret_cast<const uint4*>(vg + off);
-      }
+      const bool ok = row < nv;
+      const uint32_t m = ok ? 0xffffffffu : 0u;
+      const int64_t off = (j0 + (ok ? row : 0)) * tok_stride + ch * 8;
+      const uint4 kx = *reinterpret_cast<const uint4*>(kg + off);
+      const uint4 vx = *reinterpret_cast<const uint4*>(vg + off);
+      kpre[c] = make_uint4(kx.x & m, kx.y & m, kx.z & m, kx.w & m);
+      vpre[c] = make_uint4(vx.x & m, vx.y & m, vx.z & m, vx.w & m);
     }
   };
   if (t0 < t1) gload(t0);
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
       bf16x8 bh, bl;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float f = feature(bf16_to_f32(static_cast<uint16_t>(kr[j])), p.phi_k);
+        float f = feature_t<POLY>(bf16_to_f32(static_cast<uint16_t>(kr[j])), p.phi_k);
         if (16 * kk + 8 * g + j >= nv) f = 0.f;
         zacc += f;
         const __bf16 h = static_cast<__bf16>(f);
@@ -246,7 +248,14 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
   const bool is_z = e >= D * D;
   const int dout = is_z ? 0 : e / D, din = is_z ? e - D * D : e % D;
   float run = is_z ? p.z_in[bh * D + din] : p.s_in[bh * D * D + int64_t(din) * D + dout];
+  // the deltas (read-only here, never written by this kernel) of this lane's
+  // element: the chunk's sum is formed before the chunk's prefix is stored,
+  // so the loads of a chunk do not wait on the previous chunk's stores
+  const float* __restrict__ dsrc = is_z ? p.dz + bh * D + din : p.ds + bh * D * D + e;
+  const int64_t dstep = int64_t(p.B) * p.Hk * (is_z ? D : D * D);  // between (chunk, split) slots
   for (int64_t c = 0; c < p.n_chunks; ++c) {
+    float d = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) d += __builtin_nontemporal_load(dsrc + (c * p.nsplit + s) * dstep);
     const int64_t cs = c * p.B * p.Hk + bh;  // [c][b][hk]
     if (is_z) {
       p.zc[cs * D + din] = run;
@@ -255,10 +264,7 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
     } else {
       static_cast<float*>(p.sc)[cs * D * D + e] = run;
     }
-    for (int s = 0; s < p.nsplit; ++s) {
-      const int64_t slot = (c * p.nsplit + s) * p.B * p.Hk + bh;
-      run += is_z ? p.dz[slot * D + din] : p.ds[slot * D * D + e];
-    }
+    run += d;
   }
   if (is_z) p.z_out[bh * D + din] = run;
   else p.s_out[bh * D * D + int64_t(din) * D + dout] = run;
@@ -268,10 +274,14 @@ template <int D, bool BF16>
 hipError_t launch_d(const HybridStateLaunch& p, hipStream_t s) {
   const int64_t nblk = p.n_chunks * p.nsplit * p.B * p.Hk;
   if (nblk > 0) {
-    if constexpr (BF16)
-      hipLaunchKernelGGL((hybrid_delta_mfma_kernel<D>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((hybrid_delta_kernel<D, BF16>), dim3(static_cast<unsigned>(nblk)), dim3(kDeltaThreads), 0, s, p);
+    const dim3 grid(static_cast<unsigned>(nblk));
+    if constexpr (BF16) {
+      if (p.phi_k.poly) hipLaunchKernelGGL((hybrid_delta_mfma_kernel<D, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((hybrid_delta_mfma_kernel<D, false>), grid, dim3(256), 0, s, p);
+    } else {
+      if (p.phi_k.poly) hipLaunchKernelGGL((hybrid_delta_kernel<D, BF16, true>), grid, dim3(kDeltaThreads), 0, s, p);
+      else hipLaunchKernelGGL((hybrid_delta_kernel<D, BF16, false>), grid, dim3(kDeltaThreads), 0, s, p);
+    }
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   const int64_t nthr = int64_t(p.B) * p.Hk * (D * D + D);
