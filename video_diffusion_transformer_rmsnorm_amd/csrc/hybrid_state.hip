@@ -238,36 +238,75 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
   if (wave < NB && g == 0) p.dz[slot * D + 32 * nb + r] = zacc;
 }
 
+// Scan pass: each lane walks the chunks for four adjacent elements of one
+// (batch, kv head) state -- [D][D] dS^T elements, then the D of z -- with
+// 16-byte delta loads; four chunks' deltas are loaded before their prefixes
+// are stored, so the loads of a group do not wait on stores.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
-  constexpr int NE = D * D + D;
+  constexpr int NE = D * D + D;  // elements per (batch, kv head): S^T, then z
+  constexpr int NV = NE / 4;
+  static_assert((D * D) % 4 == 0 && D % 4 == 0, "float4 groups stay in S or z");
   const int64_t gt = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t bh = gt / NE;
+  const int64_t bh = gt / NV;
   if (bh >= int64_t(p.B) * p.Hk) return;
-  const int e = int(gt % NE);
+  const int e = int(gt % NV) * 4;
   const bool is_z = e >= D * D;
-  const int dout = is_z ? 0 : e / D, din = is_z ? e - D * D : e % D;
-  float run = is_z ? p.z_in[bh * D + din] : p.s_in[bh * D * D + int64_t(din) * D + dout];
-  // the deltas (read-only here, never written by this kernel) of this lane's
-  // element: the chunk's sum is formed before the chunk's prefix is stored,
-  // so the loads of a chunk do not wait on the previous chunk's stores
-  const float* __restrict__ dsrc = is_z ? p.dz + bh * D + din : p.ds + bh * D * D + e;
+  const int zi = e - D * D;            // first z element (is_z)
+  const int dout = e / D, din = e % D;  // first S^T element (!is_z): din .. din + 3
+  float run[4];
+  if (is_z) {
+    const float4 z4 = *reinterpret_cast<const float4*>(p.z_in + bh * D + zi);
+    run[0] = z4.x; run[1] = z4.y; run[2] = z4.z; run[3] = z4.w;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) run[u] = p.s_in[bh * D * D + int64_t(din + u) * D + dout];  // s is [d_in][d_out]
+  }
+  const float* dsrc = is_z ? p.dz + bh * D + zi : p.ds + bh * D * D + e;
   const int64_t dstep = int64_t(p.B) * p.Hk * (is_z ? D : D * D);  // between (chunk, split) slots
-  for (int64_t c = 0; c < p.n_chunks; ++c) {
-    float d = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) d += __builtin_nontemporal_load(dsrc + (c * p.nsplit + s) * dstep);
+  auto store = [&](int64_t c) {
     const int64_t cs = c * p.B * p.Hk + bh;  // [c][b][hk]
     if (is_z) {
-      p.zc[cs * D + din] = run;
+      *reinterpret_cast<float4*>(p.zc + cs * D + zi) = make_float4(run[0], run[1], run[2], run[3]);
     } else if constexpr (BF16) {
-      static_cast<uint16_t*>(p.sc)[cs * D * D + e] = f32_to_bf16(run);
+      uint2 w;
+      w.x = pack_bf16x2(run[0], run[1]);
+      w.y = pack_bf16x2(run[2], run[3]);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.sc) + cs * D * D + e) = w;
     } else {
-      static_cast<float*>(p.sc)[cs * D * D + e] = run;
+      *reinterpret_cast<float4*>(static_cast<float*>(p.sc) + cs * D * D + e) = make_float4(run[0], run[1], run[2], run[3]);
     }
-    run += d;
+  };
+  auto delta = [&](int64_t c) {
+    float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(dsrc + (c * p.nsplit + s) * dstep);
+      d.x += x.x; d.y += x.y; d.z += x.z; d.w += x.w;
+    }
+    return d;
+  };
+  int64_t c = 0;
+  for (; c + 4 <= p.n_chunks; c += 4) {
+    float4 d[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[u] = delta(c + u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      store(c + u);
+      run[0] += d[u].x; run[1] += d[u].y; run[2] += d[u].z; run[3] += d[u].w;
+    }
   }
-  if (is_z) p.z_out[bh * D + din] = run;
-  else p.s_out[bh * D * D + int64_t(din) * D + dout] = run;
+  for (; c < p.n_chunks; ++c) {
+    const float4 d = delta(c);
+    store(c);
+    run[0] += d.x; run[1] += d.y; run[2] += d.z; run[3] += d.w;
+  }
+  if (is_z) {
+    *reinterpret_cast<float4*>(p.z_out + bh * D + zi) = make_float4(run[0], run[1], run[2], run[3]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p.s_out[bh * D * D + int64_t(din + u) * D + dout] = run[u];
+  }
 }
 
 template <int D, bool BF16>
@@ -284,7 +323,7 @@ hipError_t launch_d(const HybridStateLaunch& p, hipStream_t s) {
     }
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
-  const int64_t nthr = int64_t(p.B) * p.Hk * (D * D + D);
+  const int64_t nthr = int64_t(p.B) * p.Hk * ((D * D + D) / 4);
   hipLaunchKernelGGL((hybrid_scan_kernel<D, BF16>), dim3(static_cast<unsigned>((nthr + 255) / 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
