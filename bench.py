@@ -289,8 +289,9 @@ def bench_full(args):
                      "algorithmic_flops_per_launch": flops},
     }
     del qr, kr, o, lse
-    out["rope_rotated"] = rope_rotated(w, qd, kd, grid)
-    out["measured_peaks"] = measured_peaks(achieved, out["rope_rotated"]["GBps"])
+    if not args.no_peaks:
+        out["rope_rotated"] = rope_rotated(w, qd, kd, grid)
+        out["measured_peaks"] = measured_peaks(achieved, out["rope_rotated"]["GBps"])
     return out
 
 
@@ -618,6 +619,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of the oracle's timed sample (full and ring workloads)")
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the RoPE-over-rotated-buffers and reference-peak measurements (profiler passes)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
