@@ -196,6 +196,36 @@ def test_full_attention_key_split(D):
     check(o_plain, wo, "bf16", "O (unsplit)"); check_lse(lse_plain, wl, "bf16", "LSE (unsplit)")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_full_attention_key_split_two_ranges(D):
+    """12 workgroups of 128 queries (GQA, 4 query heads on 2 KV heads) split
+    the keys into two ranges, [0, 320) and [320, 513): the second ends a
+    whole tile before the first.  The computed key-norm bound, the caller's
+    bound (RMS-normalised keys; the same bits as the computed one) and a
+    workspace too small for bound and partials (online maximum, unsplit) all
+    match the oracle."""
+    Lq, Lkv, Hq, Hk = 300, 513, 4, 2
+    log(f"full attention, key split in two ranges: D={D} Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+    q = raw((1, Lq, Hq, D), 191, "bf16"); k = raw((1, Lkv, Hk, D), 192, "bf16"); v = raw((1, Lkv, Hk, D), 193, "bf16")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    wo, wl = O.attention(q.values, k.values, v.values)
+    o1, l1 = V.vdit_attn_fwd(qd, kd, vd)
+    o2, l2 = V.vdit_attn_fwd(qd, kd, vd, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    check(o1, wo, "bf16", "O (computed bound)"); check_lse(l1, wl, "bf16", "LSE (computed bound)")
+    check(o2, wo, "bf16", "O (online maximum, unsplit)"); check_lse(l2, wl, "bf16", "LSE (online maximum, unsplit)")
+    # RMS-normalised keys under the caller's bound
+    pairs = (22, 21, 21) if D == 128 else (12, 10, 10)
+    qr = V.vdit_rope_qk(qd, None, V.make_grid(1, 1, Lq, pairs))[0]
+    kr2 = V.vdit_rope_qk(None, kd, V.make_grid(1, 1, Lkv, pairs))[1]
+    o3, l3 = V.vdit_attn_fwd(qr, kr2, vd, key_norm_max=math.sqrt(D) * (1 + 2 ** -7))
+    o4, l4 = V.vdit_attn_fwd(qr, kr2, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o4) and torch.equal(l3, l4), "caller's bound and computed bound differ"
+    wo, wl = O.attention(from_dev(qr), from_dev(kr2), v.values)
+    check(o3, wo, "bf16", "O (caller's bound)"); check_lse(l3, wl, "bf16", "LSE (caller's bound)")
+
+
 @pytest.mark.parametrize("D,Lq", [(128, 16347), (64, 16347), (128, 9001), (64, 9001)])
 def test_full_attention_bounded_and_online_softmax(D, Lq):
     # Lq 16347: 256-query workgroups (8 heads x 64 query tiles: two even

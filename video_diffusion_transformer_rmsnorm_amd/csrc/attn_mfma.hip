@@ -170,7 +170,9 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   const int g = lane >> 5, r = lane & 31;
 
   // ---------------------------------------------------------------- work --
-  const int64_t lid = xcd_remap(blockIdx.x, total);
+  // (32-bit index arithmetic: the launch keeps total below 2^31; a 64-bit
+  // division is a long scalar sequence ahead of the first memory request)
+  const uint32_t lid = uint32_t(xcd_remap(blockIdx.x, total));
   const bool hybrid = p.epi == kEpiHybrid;
   int64_t q_begin, q_end, chunk_id = 0;
   int h, b;
@@ -178,17 +180,17 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   float* part_o = p.part_o;
   float* part_lse = p.part_lse;
   if (!hybrid) {
-    const int64_t tiles = (p.Lq + BM - 1) / BM;
-    const int64_t qt = lid % tiles;
-    int64_t rest = lid / tiles;
-    int64_t split = 0;
+    const uint32_t tiles = uint32_t((p.Lq + BM - 1) / BM);
+    const uint32_t qt = lid % tiles;
+    uint32_t rest = lid / tiles;
+    uint32_t split = 0;
     if (p.nsplit > 1) {
       split = rest % p.nsplit;
       rest /= p.nsplit;
     }
-    h = int(rest % p.Hq);
-    b = int(rest / p.Hq);
-    q_begin = qt * BM;
+    h = int(rest % uint32_t(p.Hq));
+    b = int(rest / uint32_t(p.Hq));
+    q_begin = int64_t(qt) * BM;
     q_end = min(p.Lq, q_begin + BM);
     sg = p.seg[0];
     if (p.nseg == 0) sg.len = 0;
@@ -207,15 +209,15 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       part_lse += split * (int64_t(p.B) * p.Hq * p.Lq);
     }
   } else {
-    const int64_t tpc = (p.chunk + BM - 1) / BM;
-    const int64_t t = lid % tpc, rest = lid / tpc;
-    chunk_id = rest % p.n_chunks;
-    const int64_t rest2 = rest / p.n_chunks;
-    h = int(rest2 % p.Hq);
-    b = int(rest2 / p.Hq);
+    const uint32_t tpc = uint32_t((p.chunk + BM - 1) / BM);
+    const uint32_t t = lid % tpc, rest = lid / tpc;
+    chunk_id = rest % uint32_t(p.n_chunks);
+    const uint32_t rest2 = rest / uint32_t(p.n_chunks);
+    h = int(rest2 % uint32_t(p.Hq));
+    b = int(rest2 / uint32_t(p.Hq));
     const int64_t c0 = chunk_id * p.chunk;
     const int64_t c1 = min(p.Lq, c0 + p.chunk);
-    q_begin = c0 + t * BM;
+    q_begin = c0 + int64_t(t) * BM;
     q_end = min(c1, q_begin + BM);
     if (q_begin >= q_end) return;
     // softmax window: the chunk's keys and the hyb_overlap keys before them
@@ -311,6 +313,48 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       for (int i = 0; i < KIW; ++i) {
         const int u = wave + NW * i;
         if (u < KI) buffer_load_lds16(rsrc, (lds_void*)(lb + u * 1024), koff[i]);
+      }
+    }
+  };
+
+  // The first tiles go out before anything waits on Q (the bound below reads
+  // Q's registers), so the two memory latencies overlap.
+  auto issue_first = [&]() {
+    issue(0, false, 0);
+    issue(0, true, 0);
+    if (ntiles > 1) issue(1, false, 1);
+  };
+  bool first_issued = false;
+  if (ntiles > 0) {
+    issue_first();
+    first_issued = true;
+  }
+
+  // Chunk-hybrid epilogue state: S_c^T (bf16 [D][D]) and z_c of the chunk go
+  // straight into LDS by direct loads, rows [0, D/2) and then z_c in K
+  // buffer `kbuf`, rows [D/2, D) in V buffer 1 - kbuf, each row's 16-byte
+  // chunk c at position c ^ swz_k(row) (the epilogue's operand reads of one
+  // instruction then fall in distinct bank groups).
+  constexpr int ST_NI = D * D * 2 / 1024;  // direct-load instructions of S_c^T
+  static_assert(D * D + 1024 <= KTILE_B && D * D <= TILE_B, "S_c^T halves and z_c fit the tile buffers");
+  auto issue_state = [&](int kbuf) {
+    const int64_t sidx = (chunk_id * p.B + b) * p.Hk + hk;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(p.st) + sidx * D * D), (short)0, D * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.zc + sidx * D), (short)0, D * 4, 0x00020000);
+    char* lo = lds + kbuf * KTILE_B;
+    char* hi = lds + 2 * KTILE_B + (1 - kbuf) * TILE_B;
+#pragma unroll
+    for (int i = 0; i < (ST_NI + NW) / NW; ++i) {
+      const int u = wave + NW * i;
+      if (u < ST_NI) {
+        const int row0 = 64 * u / CPR;  // first row of this instruction (all its rows in one half)
+        const int row = row0 + lane / CPR, c = lane % CPR;
+        char* dst = row0 < D / 2 ? lo + row0 * ROWB : hi + (row0 - D / 2) * ROWB;
+        buffer_load_lds16(rs, (lds_void*)dst, uint32_t(row * ROWB + ((c ^ swz_k<D>(row)) * 16)));
+      } else if (u == ST_NI) {
+        buffer_load_lds16(rz, (lds_void*)(lo + D * D), uint32_t(lane * 16));  // lanes past z_c read zeros
       }
     }
   };
@@ -677,10 +721,10 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 
   auto main_loop = [&](auto fastc) {
     constexpr bool FAST = decltype(fastc)::value;
-    // prologue: K_0, V_0, K_1 in flight; S^T of tile 0
-    issue(0, false, 0);
-    issue(0, true, 0);
-    if (ntiles > 1) issue(1, false, 1);
+    // prologue: K_0, V_0, K_1 in flight (issued at the start for the first
+    // pass); S^T of tile 0
+    if (!first_issued) issue_first();
+    first_issued = false;
     wait_and_sync();
     f32x16 S[2][QB];
     qk(0, S);
@@ -777,25 +821,51 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   }
 
   // -------------------------------------------------------------- epilogue --
+  // bf16 output rows leave through LDS: a lane holds 4-channel pieces of one
+  // query row (O^T layout), so storing them directly would touch 32 rows per
+  // instruction.  Each wavefront writes its rows into its own LDS area
+  // (32 * QB rows of 2 D bytes, the 16-byte chunk c of local row rl at
+  // position c ^ swz_k(rl)) and stores whole rows, 1 KB per instruction.
+  static_assert(NW * 32 * QB * ROWB <= 2 * KTILE_B + 2 * TILE_B, "output staging fits the tile buffers");
+  char* const ob = lds + wave * (32 * QB * ROWB);
+  auto stage_piece = [&](int rl, int chunk, float y0, float y1, float y2, float y3) {
+    uint2 w;
+    w.x = pack_bf16x2(y0, y1);
+    w.y = pack_bf16x2(y2, y3);
+    *reinterpret_cast<uint2*>(ob + rl * ROWB + ((chunk ^ swz_k<D>(rl)) * 16) + g * 8) = w;
+  };
+  auto store_rows = [&]() {
+    constexpr int RPI_O = 1024 / ROWB;  // rows per store instruction
+#pragma unroll
+    for (int j = 0; j < 32 * QB / RPI_O; ++j) {
+      const int rl = j * RPI_O + lane / CPR, c = lane % CPR;
+      const int64_t q = qw0 + rl;
+      const uint4 u = *reinterpret_cast<const uint4*>(ob + rl * ROWB + ((c ^ swz_k<D>(rl)) * 16));
+      if (q < q_end) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.o) + ((int64_t(b) * p.Lq + q) * p.Hq + h) * D + c * 8) = u;
+    }
+  };
+
   if (p.epi == kEpiPlain || p.epi == kEpiRing) {
+    // (the main loop ended on a barrier after its last LDS read: every area is free)
+    const bool merge_prev = p.epi == kEpiRing && p.has_prev;
+    const bool to_part = p.epi == kEpiRing && !p.final_out;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float lt = lsum[qb] + other_half(lsum[qb]);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const float lse_s = partial_lse(m2[qb], lt);
       const int64_t q = qw0 + 32 * qb + r;
-      if (q >= q_end) continue;
-      const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
-      const int64_t lrowi = (int64_t(b) * p.Hq + h) * p.Lq + q;
+      const bool live = q < q_end;
+      const int64_t qc = live ? q : q_begin;  // rows past the end compute on a valid row, store nothing
+      const int64_t orow = ((int64_t(b) * p.Lq + qc) * p.Hq + h) * D;
+      const int64_t lrowi = (int64_t(b) * p.Hq + h) * p.Lq + qc;
       float wa = 0.f, wb = inv, lse_out = lse_s;
-      const bool merge_prev = p.epi == kEpiRing && p.has_prev;
       if (merge_prev) {
         const MergeW w = merge_weights(part_lse[lrowi], lse_s);
         wa = w.wa;
         wb = w.wb * inv;
         lse_out = w.lse;
       }
-      const bool to_part = p.epi == kEpiRing && !p.final_out;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -810,120 +880,96 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
             y[2] = fmaf(wa, pv4.z, y[2]); y[3] = fmaf(wa, pv4.w, y[3]);
           }
           if (to_part) {
-            *reinterpret_cast<float4*>(part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
+            if (live) *reinterpret_cast<float4*>(part_o + orow + d) = make_float4(y[0], y[1], y[2], y[3]);
           } else {
-            uint2 w;
-            w.x = pack_bf16x2(y[0], y[1]);
-            w.y = pack_bf16x2(y[2], y[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = w;
+            stage_piece(32 * qb + r, 4 * db + i4, y[0], y[1], y[2], y[3]);
           }
         }
-      if (g == 0) {
+      if (g == 0 && live) {
         if (to_part) part_lse[lrowi] = lse_out;
         else if (p.lse) p.lse[lrowi] = lse_out;
       }
     }
+    if (!to_part) store_rows();
     return;
   }
 
   // chunk-hybrid: O_lin^T = S_c^T phi(Q)^T on the matrix cores (S_c^T and
   // phi(q) in bf16, float32 accumulation), den = phi(q)^T z_c in float32.
-  // phi takes the queries as stored: the bounded-score path scaled the
-  // registers by c2.
-  //
-  // S_c^T of the workgroup's (chunk, batch, kv head) is read from memory once
-  // per workgroup into LDS (the tile buffers are free after the main loop):
-  // row dout at 2 D dout bytes, its 16-byte chunk c at position
-  // c ^ swz_k(dout), so the rows one operand read touches fall in distinct
-  // bank groups.  Every wave then reads its A operands there.
-  const int64_t sidx = (chunk_id * p.B + b) * p.Hk + hk;
-  const char* st = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.st) + sidx * D * D);
-  const float* z = p.zc + sidx * D;
-  {
-    constexpr int SC_BYTES = D * D * 2;
-    static_assert(SC_BYTES <= 2 * KTILE_B + 2 * TILE_B, "S_c fits the tile buffers");
-    constexpr int NCH = D * CPR;             // 16-byte chunks of S_c^T
-    constexpr int PER = NCH / (64 * NW);     // per thread
-    constexpr int BATCH = PER < 8 ? PER : 8;
-    static_assert(PER * 64 * NW == NCH && PER % BATCH == 0, "S_c staging mapping");
+  // The tile buffers are free (the main loop ended on a barrier after its
+  // last LDS read): S_c^T and z_c go into K buffer 0 and V buffer 1 while Q
+  // is reloaded unscaled (the bounded-score path scaled the registers), one
+  // memory latency for the three.
+  issue_state(0);
+  load_q();
+  wait_and_sync();
+  const char* s_lo = lds;
+  const char* s_hi = lds + 2 * KTILE_B + TILE_B;
+  const float* z = reinterpret_cast<const float*>(s_lo + D * D);
+  float lse_h[QB];
+  if (qw0 < q_end) {  // (a wave past the end of the chunk's last block has no rows)
 #pragma unroll
-    for (int i0 = 0; i0 < PER; i0 += BATCH) {
-      uint4 buf[BATCH];
+    for (int qb = 0; qb < QB; ++qb) {
+      const float lt = lsum[qb] + other_half(lsum[qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse_s = partial_lse(m2[qb], lt);
+      bf16x8 Fq[KS];
+      float dn = 0.f;
+      auto features = [&](auto polyc) {  // the map chosen once, not per element
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int e = tid + 64 * NW * (i0 + i);
-        buf[i] = *reinterpret_cast<const uint4*>(st + (e / CPR) * ROWB + (e % CPR) * 16);
-      }
+        for (int ks = 0; ks < KS; ++ks) {
+          const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
+          const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
+          const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+          bf16x8 f;
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int e = tid + 64 * NW * (i0 + i), row = e / CPR, c = e % CPR;
-        *reinterpret_cast<uint4*>(lds + row * ROWB + ((c ^ swz_k<D>(row)) * 16)) = buf[i];
+          for (int j = 0; j < 8; ++j) {
+            const float x = feature_t<decltype(polyc)::value>(static_cast<float>(Qr[qb][ks][j]), p.phi_q);
+            dn = fmaf(x, zz[j], dn);
+            f[j] = static_cast<__bf16>(x);
+          }
+          Fq[ks] = f;
+        }
+      };
+      if (p.phi_q.poly) features(std::true_type{});
+      else features(std::false_type{});
+      const float den = dn + other_half(dn);
+      const float lse_l = den > 0.f ? logf(den) : -INFINITY;
+      const MergeW w = merge_weights(lse_s, lse_l);
+      const float inv_den = den > 0.f ? 1.f / den : 0.f;
+      const float ws = w.wa * inv, wl = w.wb * inv_den;
+      lse_h[qb] = w.lse;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x16 A;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) A[i] = 0.f;
+        const int dout = 32 * db + r;
+        const char* srow = 32 * db < D / 2 ? s_lo + dout * ROWB : s_hi + (dout - D / 2) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(srow + (((2 * ks + g) ^ swz_k<D>(dout)) * 16));
+          A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Fq[ks], A, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[db][qb][i] = ws * O[db][qb][i] + wl * A[i];
       }
     }
-    __syncthreads();
   }
-  if (qw0 >= q_end) return;  // a wave with no queries (the last tile of a chunk)
-  load_q();
+  __syncthreads();  // every wavefront is done with S_c^T: the areas are free for the rows
+  if (qw0 >= q_end) return;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = lsum[qb] + other_half(lsum[qb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float lse_s = partial_lse(m2[qb], lt);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        stage_piece(32 * qb + r, 4 * db + i4, O[db][qb][4 * i4], O[db][qb][4 * i4 + 1], O[db][qb][4 * i4 + 2],
+                    O[db][qb][4 * i4 + 3]);
     const int64_t q = qw0 + 32 * qb + r;
-    bf16x8 Fq[KS];
-    float dn = 0.f;
-    auto features = [&](auto polyc) {  // the map chosen once, not per element
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float4 za = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g);
-        const float4 zb = *reinterpret_cast<const float4*>(z + 16 * ks + 8 * g + 4);
-        const float zz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
-        bf16x8 f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = feature_t<decltype(polyc)::value>(static_cast<float>(Qr[qb][ks][j]), p.phi_q);
-          dn = fmaf(x, zz[j], dn);
-          f[j] = static_cast<__bf16>(x);
-        }
-        Fq[ks] = f;
-      }
-    };
-    if (p.phi_q.poly) features(std::true_type{});
-    else features(std::false_type{});
-    const float den = dn + other_half(dn);
-    const float lse_l = den > 0.f ? logf(den) : -INFINITY;
-    const MergeW w = merge_weights(lse_s, lse_l);
-    const float inv_den = den > 0.f ? 1.f / den : 0.f;
-    const float ws = w.wa * inv, wl = w.wb * inv_den;
-    const int64_t orow = ((int64_t(b) * p.Lq + q) * p.Hq + h) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      f32x16 A;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) A[i] = 0.f;
-      const int dout = 32 * db + r;
-      const char* srow = lds + dout * ROWB;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(srow + (((2 * ks + g) ^ swz_k<D>(dout)) * 16));
-        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Fq[ks], A, 0, 0, 0);
-      }
-      if (q < q_end) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d = 32 * db + 8 * i4 + 4 * g;
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = ws * O[db][qb][4 * i4 + e] + wl * A[4 * i4 + e];
-          uint2 u;
-          u.x = pack_bf16x2(y[0], y[1]);
-          u.y = pack_bf16x2(y[2], y[3]);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + orow + d) = u;
-        }
-      }
-    }
-    if (p.lse && g == 0 && q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = w.lse;
+    if (p.lse && g == 0 && q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = lse_h[qb];
   }
+  store_rows();
 }
 
 template <int D, int NW, int QB>
@@ -933,6 +979,7 @@ hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
   if (p.epi == kEpiHybrid) total = ((p.chunk + BM - 1) / BM) * p.n_chunks * p.Hq * p.B;
   else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B * (p.nsplit > 1 ? p.nsplit : 1);
   if (total == 0) return hipSuccess;
+  if (total > 0x7fffffff) return hipErrorInvalidConfiguration;  // (the kernel's work index is 32-bit)
   hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
   return hipGetLastError();
 }
