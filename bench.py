@@ -464,10 +464,9 @@ def bench_other(args):
         knorm = key_norm_bound(w.head_dim)  # the keys come out of the RMSNorm
 
         def step(i):
-            s.zero_(); z.zero_()
             V.vdit_attn_fwd(qr, kr, vd, mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=s, state_z=z,
-                            overlap_tokens=w.overlap_tokens, key_norm_max=knorm)
-        form = "one call over the whole sequence (state reset, delta + scan, chunk softmax + linear epilogue)"
+                            overlap_tokens=w.overlap_tokens, key_norm_max=knorm, state_zero=True)
+        form = "one call over the whole sequence from the zero state (delta + scan, chunk softmax + linear epilogue)"
     else:
         flops = WL.flops_full(w.tokens, w.tokens, w.heads, w.head_dim)
 

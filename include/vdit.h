@@ -178,8 +178,10 @@ typedef enum {
  *   (0 <= ctx_tokens <= overlap_tokens) are keys/values from before the
  *   first query, which a streaming caller carries over from its previous
  *   call.  state_s [B, n_kv_heads, D, D] and state_z [B, n_kv_heads, D]
- *   (float32) hold the incoming state (zero for a new sequence) and receive
- *   it with every key of the call folded in except the last overlap_tokens
+ *   (float32) hold the incoming state (zero for a new sequence; with the
+ *   flag VDIT_ATTN_STATE_ZERO the incoming state is taken as zero and the
+ *   two arrays are only written) and receive it with every key of the
+ *   call folded in except the last overlap_tokens
  *   (the next call's context), so calling once per chunk equals one call
  *   over the whole sequence.  Needs `workspace` of
  *   vdit_attn_workspace_bytes().
@@ -263,6 +265,9 @@ typedef struct {
 /* vdit_attn_args.flags */
 #define VDIT_ATTN_RING_FOLD 1u /* RING: fold the chunks one launch at a time, in
                                   order, even where one launch could take them all */
+#define VDIT_ATTN_STATE_ZERO 2u /* CHUNK_HYBRID: the incoming state is zero (the
+                                   first call of a sequence): state_s and state_z
+                                   are written, never read */
 
 /* Bytes of device workspace vdit_attn_fwd needs (RING, CHUNK_HYBRID) or can
  * use (FULL, ROLLING: the key split) for these arguments on the current

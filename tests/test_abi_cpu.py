@@ -170,8 +170,9 @@ def test_attn_validation_errors(lib):
         st = lib.vdit_attn_fwd(ctypes.byref(a), None)
         assert st == V.VDIT_ERR_INVALID_ARG and "key_norm_max" in lib.vdit_last_error().decode()
     a.key_norm_max = 0.0
-    # flags: unknown bits, and the ring-only fold flag outside RING
-    for flags, word in ((2, "unknown"), (V.VDIT_ATTN_RING_FOLD, "RING")):
+    # flags: unknown bits, the ring-only fold flag outside RING and the
+    # hybrid-only zero-state flag outside CHUNK_HYBRID
+    for flags, word in ((4, "unknown"), (V.VDIT_ATTN_RING_FOLD, "RING"), (V.VDIT_ATTN_STATE_ZERO, "CHUNK_HYBRID")):
         a.flags = flags
         st = lib.vdit_attn_fwd(ctypes.byref(a), None)
         assert st == V.VDIT_ERR_INVALID_ARG and word in lib.vdit_last_error().decode()

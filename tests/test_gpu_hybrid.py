@@ -145,6 +145,31 @@ def test_hybrid_small_both_partials_visible():
     assert rs <= STATE_REL, rs
 
 
+@pytest.mark.parametrize("dtype,Ov", [("bf16", 0), ("bf16", 48), ("f32", 0)])
+def test_hybrid_state_zero_flag(dtype, Ov):
+    """VDIT_ATTN_STATE_ZERO: the incoming state is taken as zero and not
+    read.  State arrays full of NaN with the flag give the same bits (O, LSE,
+    and the state written back) as zeroed arrays without it."""
+    D, L, C, Hq, Hk = 128, 700, 160, 4, 2
+    log(f"hybrid, zero incoming state by flag: {dtype} L={L} chunk={C} overlap={Ov}")
+    rng = np.random.default_rng(1611)
+    q = WL.draw((1, L, Hq, D), rng, dtype); k = WL.draw((1, L, Hk, D), rng, dtype); v = WL.draw((1, L, Hk, D), rng, dtype)
+    g = V.make_grid(7, 10, 10, (22, 21, 21))
+    qr, kr = V.vdit_rope_qk(to_dev(q), to_dev(k), g)
+    vd = to_dev(v)
+    s1 = torch.zeros((1, Hk, D, D), device="cuda"); z1 = torch.zeros((1, Hk, D), device="cuda")
+    s2 = torch.full_like(s1, float("nan")); z2 = torch.full_like(z1, float("nan"))
+    o1, l1 = V.vdit_attn_fwd(qr, kr, vd, mode="hybrid", chunk_tokens=C, state_s=s1, state_z=z1, overlap_tokens=Ov)
+    o2, l2 = V.vdit_attn_fwd(qr, kr, vd, mode="hybrid", chunk_tokens=C, state_s=s2, state_z=z2, overlap_tokens=Ov,
+                             state_zero=True)
+    torch.cuda.synchronize()
+    for a, b, name in ((o1, o2, "O"), (l1, l2, "LSE"), (s1, s2, "state s"), (z1, z2, "state z")):
+        assert torch.equal(a, b), f"{name} differs with the zero-state flag"
+    o_s, l_s, o_l, l_l = O.hybrid_partials(from_dev(qr), from_dev(kr), v.values, C, overlap=Ov)
+    wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
+    check(o2, wo, dtype, "O hybrid (zero-state flag)"); check_lse(l2, wl, dtype, "LSE hybrid (zero-state flag)")
+
+
 # ------------------------------------------------- polynomial feature maps --
 
 @pytest.mark.parametrize("dtype,D,L,C,Ov,Hq,Hk", [

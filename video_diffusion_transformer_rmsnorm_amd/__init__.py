@@ -23,6 +23,7 @@ VDIT_ROPE_NO_Q_NORM = 2
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
 ABI_VERSION = 4
 VDIT_ATTN_RING_FOLD = 1
+VDIT_ATTN_STATE_ZERO = 2
 
 # Every symbol include/vdit.h declares.
 EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_attn_workspace_bytes",
@@ -204,7 +205,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
                   frame: int = 0, chunk_tokens: int = 0, state_s=None, state_z=None, workspace=None,
                   n_kv_heads: Optional[int] = None, overlap_tokens: int = 0, ctx_tokens: int = 0,
                   key_norm_max: float = 0.0, phi_coef: Optional[Sequence[float]] = None,
-                  ring_fold: bool = False, stream=None, _noalloc: bool = False):
+                  ring_fold: bool = False, state_zero: bool = False, stream=None, _noalloc: bool = False):
     """One attention call.  Returns (o, lse) (lse None unless wanted).
 
     full:    k, v [B,Lkv,Hk,D].
@@ -220,6 +221,7 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     phi_coef: hybrid only: 8 floats, the cubics phi_q (a0..a3) and phi_k (b0..b3) that
              replace elu + 1 in the linear term.
     ring_fold: ring only: fold the chunks one launch at a time (VDIT_ATTN_RING_FOLD).
+    state_zero: hybrid only: the incoming state is zero and is not read (VDIT_ATTN_STATE_ZERO).
     """
     import torch
     if phi_coef is not None and len(phi_coef) != 8:
@@ -264,6 +266,8 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     a.key_norm_max = key_norm_max
     if ring_fold:
         a.flags |= VDIT_ATTN_RING_FOLD
+    if state_zero:
+        a.flags |= VDIT_ATTN_STATE_ZERO
     if phi_coef is not None:
         coef = (ctypes.c_float * 8)(*[float(c) for c in phi_coef])
         keep.append(coef)
@@ -309,5 +313,5 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-__all__ = ["VDIT_ATTN_RING_FOLD", "vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
+__all__ = ["VDIT_ATTN_RING_FOLD", "VDIT_ATTN_STATE_ZERO", "vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
            "VditGrid", "VditAttnArgs", "VditError", "lib", "EXPORTS", "LIB_PATH"]

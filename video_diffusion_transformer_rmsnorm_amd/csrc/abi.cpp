@@ -25,6 +25,7 @@ static_assert(offsetof(vdit_attn_args, flags) == offsetof(vdit::AttnArgs, flags)
 static_assert(offsetof(vdit_attn_args, phi_coef) == offsetof(vdit::AttnArgs, phi_coef),
               "vdit_attn_args layout mirror");
 static_assert(VDIT_ATTN_RING_FOLD == vdit::kAttnRingFold, "flag mirror");
+static_assert(VDIT_ATTN_STATE_ZERO == vdit::kAttnStateZero, "flag mirror");
 
 namespace {
 
@@ -382,6 +383,7 @@ vdit_status vdit_attn_fwd(const vdit_attn_args* args, hipStream_t stream) {
       hs.v = a.v;
       hs.s_in = a.state_s;
       hs.z_in = a.state_z;
+      hs.zero_in = (a.flags & vdit::kAttnStateZero) ? 1 : 0;
       hs.s_out = a.state_s;
       hs.z_out = a.state_z;
       hs.ds = reinterpret_cast<float*>(ws + lay.off_ds);

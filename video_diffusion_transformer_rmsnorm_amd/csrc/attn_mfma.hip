@@ -67,6 +67,9 @@
 #ifndef VDIT_ATTN_VEARLY
 #define VDIT_ATTN_VEARLY 4  // region A steps (from its end) over which the first V^T reads of region B are issued
 #endif
+#ifndef VDIT_ATTN_VEARLY64
+#define VDIT_ATTN_VEARLY64 2  // the same at D = 64 (its region A has half the steps)
+#endif
 #ifndef VDIT_ATTN_KPREF
 #define VDIT_ATTN_KPREF 3  // K operand reads issued ahead of their MFMA
 #endif
@@ -601,7 +604,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   };
   constexpr int VPB = 4 * DB;
   constexpr int VP = VDIT_ATTN_VPREF < VPB ? VDIT_ATTN_VPREF : VPB;
-  static_assert(VDIT_ATTN_VEARLY >= 1 && VDIT_ATTN_VEARLY <= 2 * KS, "early V^T reads within region A");
+  constexpr int VEARLY = D == 64 ? VDIT_ATTN_VEARLY64 : VDIT_ATTN_VEARLY;
+  static_assert(VEARLY >= 1 && VEARLY <= 2 * KS, "early V^T reads within region A");
   auto vread_buf = [&](int vbuf, int st) {
     const char* Vl = lds + 2 * KTILE_B + vbuf * TILE_B;
     const int kk = st / DB, db = st % DB;
@@ -643,7 +647,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
       // the first V^T operands of region B
 #pragma unroll
       for (int v = 0; v < VP; ++v)
-        if (st == NSTEP - VDIT_ATTN_VEARLY + v * VDIT_ATTN_VEARLY / VP) vpre[v] = vread_buf(vbuf, v);
+        if (st == NSTEP - VEARLY + v * VEARLY / VP) vpre[v] = vread_buf(vbuf, v);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll

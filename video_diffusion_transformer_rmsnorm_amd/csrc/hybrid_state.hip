@@ -254,8 +254,10 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
   const bool is_z = e >= D * D;
   const int zi = e - D * D;            // first z element (is_z)
   const int dout = e / D, din = e % D;  // first S^T element (!is_z): din .. din + 3
-  float run[4];
-  if (is_z) {
+  float run[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.zero_in) {
+    // a new sequence: the incoming state is zero and is not read
+  } else if (is_z) {
     const float4 z4 = *reinterpret_cast<const float4*>(p.z_in + bh * D + zi);
     run[0] = z4.x; run[1] = z4.y; run[2] = z4.z; run[3] = z4.w;
   } else {

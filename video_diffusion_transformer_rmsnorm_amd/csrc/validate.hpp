@@ -144,7 +144,8 @@ struct AttnArgs {
   const float* phi_coef;
 };
 
-constexpr uint32_t kAttnRingFold = 1u;  // VDIT_ATTN_RING_FOLD
+constexpr uint32_t kAttnRingFold = 1u;   // VDIT_ATTN_RING_FOLD
+constexpr uint32_t kAttnStateZero = 2u;  // VDIT_ATTN_STATE_ZERO
 
 constexpr int kMaxRingChunks = 64;
 
@@ -243,8 +244,10 @@ inline int64_t attn_keys(const AttnArgs& a) {
 
 // flags and the hybrid's polynomial feature maps
 inline CheckResult check_attn_options(const AttnArgs& a) {
-  if (a.flags & ~kAttnRingFold) return CheckResult::bad("unknown attention flags");
+  if (a.flags & ~(kAttnRingFold | kAttnStateZero)) return CheckResult::bad("unknown attention flags");
   if ((a.flags & kAttnRingFold) && a.mode != 1) return CheckResult::bad("VDIT_ATTN_RING_FOLD belongs to RING");
+  if ((a.flags & kAttnStateZero) && a.mode != 3)
+    return CheckResult::bad("VDIT_ATTN_STATE_ZERO belongs to CHUNK_HYBRID");
   if (a.phi_coef) {
     if (a.mode != 3) return CheckResult::bad("phi_coef belongs to CHUNK_HYBRID (NULL otherwise)");
     for (int i = 0; i < 8; ++i)

@@ -163,6 +163,7 @@ struct HybridStateLaunch {
   const float* z_in;   // [B, Hk, D]
   float* s_out;        // may equal s_in
   float* z_out;
+  int32_t zero_in;     // 1: the incoming state is zero (s_in, z_in not read)
   float* ds;           // [n_chunks][nsplit][B][Hk][D][D] transposed (d_out, d_in)
   float* dz;           // [n_chunks][nsplit][B][Hk][D]
   void* sc;            // per-chunk state, transposed, bf16 or float32
