@@ -564,10 +564,11 @@ def traffic_from(run_root: str, kernels=(("attn", "attn_mfma_kernel"), ("rope", 
 
 def hybrid_state_bytes(w) -> dict:
     """Algorithmic HBM bytes of the chunk-hybrid's linear-attention state
-    kernels for workload w (bf16, B = 1): the delta pass reads K and V of every
-    token and writes one float32 dS^T, dz per (chunk, token split, kv head);
-    the scan reads those and the incoming state and writes S_c^T (bf16) and
-    z_c (float32) per chunk and the outgoing state."""
+    kernels for workload w (bf16, B = 1), as the benchmark's step runs them
+    (from the zero state, VDIT_ATTN_STATE_ZERO): the delta pass reads K and V
+    of every token and writes one float32 dS^T, dz per (chunk, token split, kv
+    head); the scan reads those and writes S_c^T (bf16) and z_c (float32) per
+    chunk and the outgoing state."""
     D, Hk, L = w.head_dim, w.kv_heads, w.tokens
     nch = -(-L // w.chunk_tokens)
     units = nch * Hk
@@ -575,7 +576,7 @@ def hybrid_state_bytes(w) -> dict:
     deltas = nch * ns * Hk * (D * D + D) * 4
     state = Hk * (D * D + D) * 4
     return {"delta": 2 * L * Hk * D * 2 + deltas,
-            "scan": deltas + state + nch * Hk * (D * D * 2 + D * 4) + state,
+            "scan": deltas + nch * Hk * (D * D * 2 + D * 4) + state,
             "token_splits": ns}
 
 
