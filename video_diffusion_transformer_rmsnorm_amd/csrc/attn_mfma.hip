@@ -144,8 +144,12 @@ __host__ __device__ constexpr bool pv_pairs_in_time(int npb, int db) {
 // QB blocks of 32 queries per wavefront.  QB = 1: two wavefronts per SIMD
 // (<= 256 registers each); QB = 2: one wavefront per SIMD with 512 registers,
 // every K / V^T operand read from LDS feeding two MFMAs (half the LDS traffic
-// per FLOP).  Second launch bound: workgroups per CU.
-template <int D, int NW, int QB>
+// per FLOP).  HYB: the chunk-hybrid instance (its own epilogue, and
+// wavefronts without queries -- the tail of a chunk's last block -- skip the
+// matrix work of the main loop, so their SIMD time goes to the other
+// workgroup of the CU); the other modes use the plain/ring instance.  Second
+// launch bound: workgroups per CU.
+template <int D, int NW, int QB, bool HYB>
 __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_kernel(AttnLaunch p, int64_t total) {
   constexpr int BM = 32 * NW * QB;  // queries per workgroup
   constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   // (32-bit index arithmetic: the launch keeps total below 2^31; a 64-bit
   // division is a long scalar sequence ahead of the first memory request)
   const uint32_t lid = uint32_t(xcd_remap(blockIdx.x, total));
-  const bool hybrid = p.epi == kEpiHybrid;
+  constexpr bool hybrid = HYB;
   int64_t q_begin, q_end, chunk_id = 0;
   int h, b;
   KvSeg sg;  // the keys/values this workgroup attends to
@@ -723,6 +727,25 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     }
   };
 
+  // A hybrid wavefront with no queries keeps only its share of the tile
+  // loads and the barriers of the main loop (same count and order).
+  const bool idle = HYB && qw0 >= q_end;
+  auto idle_loop = [&]() {
+    if (!first_issued) issue_first();
+    first_issued = false;
+    wait_and_sync();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int P0 = t & 1;
+      if (t + 2 < ntiles) issue(t + 2, false, P0);
+      if (t + 1 < ntiles) issue(t + 1, true, 1 - P0);
+      debug_sync();
+      debug_sync();
+      debug_sync();
+      wait_and_sync();
+    }
+  };
+
   auto main_loop = [&](auto fastc) {
     constexpr bool FAST = decltype(fastc)::value;
     // prologue: K_0, V_0, K_1 in flight (issued at the start for the first
@@ -774,7 +797,8 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   };
   if (ntiles > 0) {
     if constexpr (NW >= VDIT_ATTN_BOUND_MIN_NW) {
-      if (fast) main_loop(std::true_type{});
+      if (idle) idle_loop();
+      else if (fast) main_loop(std::true_type{});
       else main_loop(std::false_type{});
       // With a true bound every p of a bounded-score row lies in
       // [2^-32, 2^32] (up to rounding), so its row sum lies in [2^-64, 2^64]
@@ -816,11 +840,13 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
 #pragma unroll
               for (int i = 0; i < 16; ++i) O[db][qb][i] = 0.f;
           }
-          main_loop(std::false_type{});
+          if (idle) idle_loop();
+          else main_loop(std::false_type{});
         }
       }
     } else {
-      main_loop(std::false_type{});
+      if (idle) idle_loop();
+      else main_loop(std::false_type{});
     }
   }
 
@@ -849,7 +875,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     }
   };
 
-  if (p.epi == kEpiPlain || p.epi == kEpiRing) {
+  if constexpr (!HYB) {
     // (the main loop ended on a barrier after its last LDS read: every area is free)
     const bool merge_prev = p.epi == kEpiRing && p.has_prev;
     const bool to_part = p.epi == kEpiRing && !p.final_out;
@@ -896,7 +922,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     }
     if (!to_part) store_rows();
     return;
-  }
+  } else {
 
   // chunk-hybrid: O_lin^T = S_c^T phi(Q)^T on the matrix cores (S_c^T and
   // phi(q) in bf16, float32 accumulation), den = phi(q)^T z_c in float32.
@@ -974,17 +1000,24 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
     if (p.lse && g == 0 && q < q_end) p.lse[(int64_t(b) * p.Hq + h) * p.Lq + q] = lse_h[qb];
   }
   store_rows();
+  }  // HYB
 }
 
 template <int D, int NW, int QB>
 hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
+  const bool hyb = p.epi == kEpiHybrid;
   constexpr int BM = NW * 32 * QB;
   int64_t total;
   if (p.epi == kEpiHybrid) total = ((p.chunk + BM - 1) / BM) * p.n_chunks * p.Hq * p.B;
   else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B * (p.nsplit > 1 ? p.nsplit : 1);
   if (total == 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;  // (the kernel's work index is 32-bit)
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p, total);
+  if (hyb)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB, true>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p,
+                       total);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB, false>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p,
+                       total);
   return hipGetLastError();
 }
 
