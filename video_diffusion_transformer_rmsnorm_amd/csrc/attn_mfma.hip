@@ -46,6 +46,12 @@
 //    instruction immediates (the loop is unrolled by two over the buffer
 //    parity).  Workgroup ids are remapped so each XCD walks a contiguous
 //    range of (head, query-tile) work.
+//  * Output rows leave through LDS: each wavefront stages its bf16 rows
+//    (O^T pieces of 4 channels per lane) in its own LDS area and stores
+//    whole rows, 1 KB per store instruction.  The chunk-hybrid epilogue
+//    loads S_c^T and z_c into LDS by direct loads alongside the query
+//    reload; it runs in its own kernel instance, in which wavefronts without
+//    queries keep only their tile loads and barriers.
 #include <atomic>
 #include <type_traits>
 
