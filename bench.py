@@ -85,11 +85,17 @@ def _head(t, h):
     return t[:, :, h:h + 1]
 
 
+ROW_BLOCK = 2048  # query rows per oracle attention call (bounds its score matrix to ~0.5 GB)
+
+
 def _task_full(h):
     import oracle as O
     c = _CPU
     wq, wk = O.rope_qk(_head(c["q"], h), _head(c["k"], h), c["grid"], c["pairs"])
-    O.attention(wq[:, c["rows"]], wk, _head(c["v"], h))
+    v = _head(c["v"], h)
+    rows = c["rows"]
+    for i in range(0, len(rows), ROW_BLOCK):
+        O.attention(wq[:, rows[i:i + ROW_BLOCK]], wk, v)
 
 
 def _task_ring(h):
@@ -131,7 +137,7 @@ def _task_hybrid(h):
     O.lse_merge(o_s, l_s, o_l, l_l)
 
 
-def cpu_baseline(w, rows: int = 8192, seed: int = 99):
+def cpu_baseline(w, rows: int = 32760, seed: int = 99):
     """Time the oracle on a bounded sample of workload w; returns the
     cpu_baseline object (value in the benchmark line's unit, TFLOP/s of the
     sample's attention matmuls)."""
@@ -142,11 +148,11 @@ def cpu_baseline(w, rows: int = 8192, seed: int = 99):
     _CPU.update(q=q.values, k=k.values, v=v.values, grid=w.grid, pairs=w.pairs, w=w)
     heads = list(range(w.heads))
     if w.mode == "full":
-        r = WL.sample_rows(w.tokens, rows, seed)
+        r = np.arange(w.tokens) if rows >= w.tokens else WL.sample_rows(w.tokens, rows, seed)
         _CPU["rows"] = r
         fn, flops = _task_full, WL.flops_full(len(r), w.tokens, w.heads, w.head_dim)
-        sample = (f"{len(r)} of {w.tokens} query rows x {w.heads} heads vs all {w.tokens} keys, "
-                  "plus RMSNorm+RoPE of every token of those heads")
+        sample = (f"{len(r)} of {w.tokens} query rows x {w.heads} heads vs all {w.tokens} keys "
+                  f"(oracle attention on blocks of {ROW_BLOCK} rows), plus RMSNorm+RoPE of every token")
     elif w.mode == "ring":
         q0, nq = w.q_range
         r = WL.sample_rows(nq, min(rows, 4096), seed)
@@ -616,8 +622,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=8192,
-                    help="query rows of the oracle's timed sample (full and ring workloads)")
+    ap.add_argument("--cpu-rows", type=int, default=32760,
+                    help="query rows of the oracle's timed sample (full: all rows at the default; ring: at most 4096)")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the RoPE-over-rotated-buffers and reference-peak measurements (profiler passes)")
