@@ -199,7 +199,12 @@ hipError_t launch_rope(const RopeLaunch& p, hipStream_t s) {
   if (rows == 0 || (!p.q_in && !p.k_in)) return hipSuccess;
   const int rows_per_tok = (p.q_in ? p.Hq : 0) + (p.k_in ? p.Hk : 0);
   const int tasks_per_tok = rows_per_tok * (p.D / 8);
+  // about 1536 row pieces per workgroup, but at least ~4 workgroups per CU
+  // when the call is small: each thread's pieces are loaded one after the
+  // other, so a small call needs the parallelism to hide the load latency
   int tok = (1536 + tasks_per_tok - 1) / tasks_per_tok;
+  const int64_t min_blocks = 4 * int64_t(device_cus());
+  if (rows / tok < min_blocks) tok = int(rows / min_blocks);
   if (tok < 1) tok = 1;
   if (tok > kMaxRopeTok) tok = kMaxRopeTok;
   const int64_t blocks = (rows + tok - 1) / tok;
