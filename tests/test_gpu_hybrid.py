@@ -63,6 +63,7 @@ def _hybrid_full(w, scale, inputs, B=1, key_norm_max=0.0, phi_coef=None):
     wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
     check(o, wo, "bf16", f"O hybrid, scale {scale:.4f} (all rows)")
     check_lse(lse, wl, "bf16", f"LSE hybrid, scale {scale:.4f}")
+    _check_per_chunk(o, wo, C, "O hybrid per chunk")
     ws_, wz = _state_reference(k64, v.values, w.tokens - Ov, phi_coef)
     rs = np.linalg.norm(from_dev(sd) - ws_) / np.linalg.norm(ws_)
     rz = np.linalg.norm(from_dev(zd) - wz) / np.linalg.norm(wz)
@@ -71,6 +72,19 @@ def _hybrid_full(w, scale, inputs, B=1, key_norm_max=0.0, phi_coef=None):
     weights = _softmax_weight_per_chunk(l_s, l_l, w.tokens, C)
     log("  mean softmax weight per chunk: " + " ".join(f"{x:.3f}" for x in weights))
     return weights
+
+
+def _check_per_chunk(o, wo, C, what, rel=1e-2):
+    """The relative-error guard chunk by chunk, so that a mistake confined to
+    one chunk is not diluted by the others."""
+    g = from_dev(o)
+    worst = 0.0
+    for c0 in range(0, wo.shape[1], C):
+        d = g[:, c0:c0 + C] - wo[:, c0:c0 + C]
+        r = float(np.linalg.norm(d) / np.linalg.norm(wo[:, c0:c0 + C]))
+        assert r <= rel, f"{what}: chunk at {c0}: relative error {r:.3e}"
+        worst = max(worst, r)
+    log(f"  {what}: worst chunk relF {worst:.3e}")
 
 
 def _balanced(weights, lo=0.2, hi=0.97):
