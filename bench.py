@@ -434,6 +434,15 @@ def bench_other(args):
         wall1, each1 = _time_steps(step_one, args.steps, args.warmup)
         extra["one_launch_form"] = {"ms_per_step": round(wall1, 4), "step_ms_median": round(each1[len(each1) // 2], 4),
                                     "TFLOPs": round(flops / (wall1 * 1e-3) / 1e12, 2)}
+        # vdit_lse_merge alone on the two chunks' bf16 partials (read 2 x O +
+        # 2 x LSE, write O + LSE)
+        parts = [V.vdit_attn_fwd(qq, kc_, vc_, key_norm_max=knorm) for kc_, vc_ in zip(kcs, vcs)]
+        mo, ml = torch.empty_like(parts[0][0]), torch.empty_like(parts[0][1])
+        wall_m, each_m = _time_steps(lambda i: V.vdit_lse_merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1],
+                                                                o_out=mo, lse_out=ml), args.steps, args.warmup)
+        mbytes = 3 * mo.numel() * mo.element_size() + 3 * ml.numel() * 4
+        extra["lse_merge"] = {"ms_median": round(each_m[len(each_m) // 2], 4), "bytes": mbytes,
+                              "GBps": round(mbytes / (each_m[len(each_m) // 2] * 1e-3) / 1e9, 1)}
         form = "fold: one launch per chunk, LSE merge fused into the epilogue"
     elif w.mode == "rolling":
         kc = torch.zeros((1, w.n_slots, w.tokens, w.kv_heads, w.head_dim), dtype=qd.dtype, device=dev)
@@ -447,11 +456,10 @@ def bench_other(args):
         q_norm = False if w.kv_norm else None
         qbuf = torch.empty_like(qd[:1])
 
-        def step(i):
+        def frame_step(f):
             # one decode step of stream frame f: rotate q (KV-norm: without
             # its norm), normalise and rotate k straight into the cache slot,
             # values into their slot (normalised under KV-norm), then attend
-            f = w.n_slots + i
             j, slot = f % w.n_frames, f % w.n_slots
             V.vdit_rope_qk(qd[j:j + 1], kd[j:j + 1], grid, q_out=qbuf, k_out=kc[:, slot], t_offset=t_step * f,
                            q_norm=q_norm)
@@ -461,6 +469,15 @@ def bench_other(args):
                 vc[:, slot].copy_(vd[j:j + 1])
             V.vdit_attn_fwd(qbuf, mode="rolling", k_cache=kc, v_cache=vc, frame=f,
                             key_norm_max=key_norm_bound(w.head_dim))
+
+        def step(i):  # steady state: the window is full
+            frame_step(w.n_slots + i)
+
+        def stream():
+            # the whole stream of n_frames frames from an empty cache (the first
+            # n_slots - 1 frames attend to fewer frames)
+            for f in range(w.n_frames):
+                frame_step(f)
         form = "decode step: rope(q), rope(k) into the cache slot, v into its slot, windowed attention"
     elif w.mode == "hybrid":
         s = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device=dev)
@@ -481,6 +498,17 @@ def bench_other(args):
             V.vdit_attn_fwd(qr, kr, vd)
         form = "rope + full attention"
     wall, each = _time_steps(step, args.steps, args.warmup)
+    if w.mode == "rolling":
+        stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for a, b in ev:
+            a.record(); stream(); b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[1]
+        sflops = sum(WL.flops_full(w.tokens, w.tokens * min(f + 1, w.n_slots), w.heads, w.head_dim)
+                     for f in range(w.n_frames))
+        extra["stream"] = {"frames": w.n_frames, "ms_median_of_3": round(ms, 3),
+                           "ms_per_frame": round(ms / w.n_frames, 4), "TFLOPs": round(sflops / (ms * 1e-3) / 1e12, 1)}
     line = {"metric": METRIC, "value": round(flops / (wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall, 4),
             "step_ms_median": round(each[len(each) // 2], 4), "step_ms_min": round(each[0], 4),
