@@ -85,8 +85,8 @@ def test_understated_key_norm_bound_still_correct(D):
     ~20 sqrt(D) while a bound of sqrt(D) is claimed, and every score gains the
     same 20 |u|^2 (softmax is unchanged by it, the bounded path overflows).
     The overflowing rows are detected by their row sums and recomputed on the
-    running maximum; FULL (256- and 128-query shapes), RING in one launch and
-    ROLLING all match the oracle."""
+    running maximum; FULL (256- and 128-query shapes), RING in one launch,
+    CHUNK_HYBRID and ROLLING all match the oracle."""
     H = 8
     pairs = (22, 21, 21) if D == 128 else (12, 10, 10)
     log(f"understated key_norm_max: D={D}")
@@ -111,6 +111,17 @@ def test_understated_key_norm_bound_still_correct(D):
         check_lse(from_dev(lse)[:, :, rows], wl, "bf16", f"LSE FULL L={L}")
         check(from_dev(r)[:, rows], wo, "bf16", f"O RING L={L} (sampled rows)")
         check_lse(from_dev(rl)[:, :, rows], wl, "bf16", f"LSE RING L={L}")
+    # chunk hybrid (its own kernel instance): chunks of 1170, the last one
+    # 811 tokens, whose last 128-query block has 43 queries (three wavefronts
+    # without queries take the loads-and-barriers loop, in both passes)
+    C = 1170
+    sd = torch.zeros((1, H, D, D), device="cuda"); zd = torch.zeros((1, H, D), device="cuda")
+    hq, hl = V.vdit_attn_fwd(qr, kr, vd, mode="hybrid", chunk_tokens=C, state_s=sd, state_z=zd, key_norm_max=knm)
+    torch.cuda.synchronize()
+    o_s, l_s, o_l, l_l = O.hybrid_partials(q64, k64, v.values, C)
+    wo, wl = O.lse_merge(o_s, l_s, o_l, l_l)
+    check(hq, wo, "bf16", "O HYBRID (all rows)")
+    check_lse(hl, wl, "bf16", "LSE HYBRID")
     # rolling: 3 slots of 3000 tokens, frame 4
     kcache = kr[:, :9000].reshape(1, 3, 3000, H, D).contiguous()
     vcache = vd[:, :9000].reshape(1, 3, 3000, H, D).contiguous()
