@@ -207,7 +207,7 @@ def test_attention_matches_torch_sdpa_f64(Hq, Hk):
 
 
 def test_attention_probs_brute_force_and_against_attention():
-    # The softmax weight matrix: rows sum to one (the benchmark spec), each entry is
+    # The softmax weight matrix: rows sum to one, each entry is
     # e^{s_ij} / sum_k e^{s_ik} by loops (scale and GQA head map included),
     # P V is attention's output and ln of the row normaliser its LSE.
     r = RNG(15)
