@@ -169,22 +169,25 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
 
   // tile loads run one tile ahead in registers: tile j+1 is in flight while
   // tile j is on the matrix cores.  Rows past the split's end load row 0 of
-  // the tile (which exists) and are masked to zero: no branch per row.
+  // the tile (which exists) and are zeroed when the tile is written to LDS
+  // (not at the load, which would wait for the data right there); their
+  // key rows also get phi = 0 in the product below.
   constexpr int NCH = kMDeltaBN * CPR / 256;  // 16-byte chunks per thread per tile
   static_assert(NCH * 256 == kMDeltaBN * CPR, "tile chunks per thread");
   uint4 kpre[NCH], vpre[NCH];
+  // chunk c of a thread: row tid / CPR + c * (256 / CPR) of the tile, 16-byte
+  // chunk tid % CPR of the row
+  const int row0 = tid / CPR;
+  const int64_t lane_off = int64_t(row0) * tok_stride + (tid % CPR) * 8;
   auto gload = [&](int64_t j0) {
     const int nv = int(min<int64_t>(kMDeltaBN, t1 - j0));
+    const uint16_t* kb = kg + j0 * tok_stride;
+    const uint16_t* vb = vg + j0 * tok_stride;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int e = tid + 256 * c, row = e / CPR, ch = e % CPR;
-      const bool ok = row < nv;
-      const uint32_t m = ok ? 0xffffffffu : 0u;
-      const int64_t off = (j0 + (ok ? row : 0)) * tok_stride + ch * 8;
-      const uint4 kx = *reinterpret_cast<const uint4*>(kg + off);
-      const uint4 vx = *reinterpret_cast<const uint4*>(vg + off);
-      kpre[c] = make_uint4(kx.x & m, kx.y & m, kx.z & m, kx.w & m);
-      vpre[c] = make_uint4(vx.x & m, vx.y & m, vx.z & m, vx.w & m);
+      const int64_t off = row0 + c * (256 / CPR) < nv ? lane_off + c * (256 / CPR) * tok_stride : (tid % CPR) * 8;
+      kpre[c] = *reinterpret_cast<const uint4*>(kb + off);
+      vpre[c] = *reinterpret_cast<const uint4*>(vb + off);
     }
   };
   if (t0 < t1) gload(t0);
@@ -195,8 +198,9 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
     for (int c = 0; c < NCH; ++c) {
       const int e = tid + 256 * c, row = e / CPR, ch = e % CPR;
       const int at = row * ROWB + ((ch ^ dswz<D>(row)) * 16);
-      *reinterpret_cast<uint4*>(kt + at) = kpre[c];
-      *reinterpret_cast<uint4*>(vt + at) = vpre[c];
+      const uint32_t m = row < nv ? 0xffffffffu : 0u;
+      *reinterpret_cast<uint4*>(kt + at) = make_uint4(kpre[c].x & m, kpre[c].y & m, kpre[c].z & m, kpre[c].w & m);
+      *reinterpret_cast<uint4*>(vt + at) = make_uint4(vpre[c].x & m, vpre[c].y & m, vpre[c].z & m, vpre[c].w & m);
     }
     __syncthreads();
     if (j0 + kMDeltaBN < t1) gload(j0 + kMDeltaBN);
@@ -240,8 +244,7 @@ __global__ __launch_bounds__(256, 3) void hybrid_delta_mfma_kernel(HybridStateLa
 
 // Scan pass: each lane walks the chunks for four adjacent elements of one
 // (batch, kv head) state -- [D][D] dS^T elements, then the D of z -- with
-// 16-byte delta loads; four chunks' deltas are loaded before their prefixes
-// are stored, so the loads of a group do not wait on stores.
+// 16-byte delta loads, eight (chunk, split) slots in flight at a time.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
   constexpr int NE = D * D + D;  // elements per (batch, kv head): S^T, then z
@@ -279,29 +282,33 @@ __global__ __launch_bounds__(256) void hybrid_scan_kernel(HybridStateLaunch p) {
       *reinterpret_cast<float4*>(static_cast<float*>(p.sc) + cs * D * D + e) = make_float4(run[0], run[1], run[2], run[3]);
     }
   };
-  auto delta = [&](int64_t c) {
-    float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(dsrc + (c * p.nsplit + s) * dstep);
-      d.x += x.x; d.y += x.y; d.z += x.z; d.w += x.w;
-    }
-    return d;
-  };
+  // The (chunk, split) slots in order, eight loads in flight: a chunk's
+  // delta is the sum of its splits (in split order), and its prefix is
+  // stored before the delta is added.
+  const int64_t nsl = p.n_chunks * p.nsplit;
+  float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
   int64_t c = 0;
-  for (; c + 4 <= p.n_chunks; c += 4) {
-    float4 d[4];
+  for (int64_t j0 = 0; j0 < nsl; j0 += 8) {
+    float4 x[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) d[u] = delta(c + u);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      store(c + u);
-      run[0] += d[u].x; run[1] += d[u].y; run[2] += d[u].z; run[3] += d[u].w;
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = min(j0 + u, nsl - 1);  // past the end: the last slot again (in bounds, unused)
+      x[u] = *reinterpret_cast<const float4*>(dsrc + j * dstep);
     }
-  }
-  for (; c < p.n_chunks; ++c) {
-    const float4 d = delta(c);
-    store(c);
-    run[0] += d.x; run[1] += d.y; run[2] += d.z; run[3] += d.w;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < nsl) {
+        d.x += x[u].x; d.y += x[u].y; d.z += x[u].z; d.w += x[u].w;
+        if (++s == p.nsplit) {
+          store(c);
+          run[0] += d.x; run[1] += d.y; run[2] += d.z; run[3] += d.w;
+          d = make_float4(0.f, 0.f, 0.f, 0.f);
+          s = 0;
+          ++c;
+        }
+      }
+    }
   }
   if (is_z) {
     *reinterpret_cast<float4*>(p.z_out + bh * D + zi) = make_float4(run[0], run[1], run[2], run[3]);
