@@ -10,15 +10,19 @@
 // values inside attention) or for both; rms_norm_kernel normalises the values.
 //
 // Design (HBM-bound, one pass): a workgroup owns a few consecutive tokens.
-// It first computes cos/sin for each (token, pair) once -- the angle is
-// formed and reduced modulo 2*pi in float64 so large temporal offsets keep
-// float32 accuracy, then its sine and cosine are taken in float32 -- into
-// LDS, and every q and k head of those tokens reuses them.  Each lane then owns 8 channels (one 16-byte bf16 vector) of
+// Each thread first requests its first 16-byte piece of q or k, then the
+// workgroup computes cos/sin for each (token, pair) once -- the angle
+// (position times the pair's frequency, a power of a per-axis ratio that the
+// host forms in float64) is reduced modulo 2*pi in float64 so large temporal offsets keep float32
+// accuracy, then its sine and cosine are taken in float32 -- into LDS, and
+// every q and k head of those tokens reuses them.  Each lane then owns 8 channels (one 16-byte bf16 vector) of
 // one head row; the row's sum of squares is reduced across the D/8 lanes of
 // the row with cross-lane shuffles.  Loads and stores are 16-byte vectors
 // over contiguous memory, so each token's q (and k) block streams through
 // once.  In-place operation is safe: a lane reads its 8 channels before it
 // writes them.
+#include <cmath>
+
 #include "device_common.hpp"
 #include "vdit_internal.hpp"
 
@@ -39,24 +43,91 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   const int ntok = int(min<int64_t>(tok_per_block, rows_total - row0));
   if (ntok <= 0) return;
 
+  // (per-lane choices below pick between these values, not between fields
+  // of the argument block, which would be a load from a per-lane address)
+  const void* const q_in = p.q_in;
+  const void* const k_in = p.k_in;
+  void* const q_out = p.q_out;
+  void* const k_out = p.k_out;
+  const float* const q_gain = p.q_gain;
+  const float* const k_gain = p.k_gain;
+  const int Hq = p.Hq, Hk = p.Hk;
+  const bool norm_q = p.norm_q != 0, norm_k = p.norm_k != 0;
+  const bool has_q = q_in != nullptr, has_k = k_in != nullptr;
+  const int rows_q = has_q ? Hq : 0;
+  const int rows_per_tok = rows_q + (has_k ? Hk : 0);
+  const int tasks = ntok * rows_per_tok * TPR;
+  const float inv_d = 1.0f / float(D);
+
+  // piece t of the workgroup: 8 channels of one q or k head row.  Row index
+  // -> (token, row) without an integer division: rt < 2^16, so the float
+  // quotient, nudged by half a step, truncates exactly.
+  struct Piece {
+    int64_t off;
+    int tl, c;
+    bool is_q;
+  };
+  const float inv_rpt = 1.0f / float(rows_per_tok);
+  auto locate = [&](int t) {
+    Piece pc;
+    pc.c = t % TPR;
+    const int rt = t / TPR;
+    pc.tl = int((float(rt) + 0.5f) * inv_rpt);
+    const int r = rt - pc.tl * rows_per_tok;
+    pc.is_q = r < rows_q;
+    const int head = pc.is_q ? r : r - rows_q;
+    const int nh = pc.is_q ? Hq : Hk;
+    pc.off = ((row0 + pc.tl) * nh + head) * int64_t(D) + pc.c * 8;
+    return pc;
+  };
+  // the raw 16 (bf16) or 32 (float32) bytes of a piece
+  struct Raw {
+    uint4 a, b;
+  };
+  auto load_raw = [&](const Piece& pc) {
+    Raw w;
+    const void* src = pc.is_q ? q_in : k_in;
+    if constexpr (BF16) {
+      w.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + pc.off);
+      w.b = make_uint4(0, 0, 0, 0);
+    } else {
+      w.a = *reinterpret_cast<const uint4*>(static_cast<const float*>(src) + pc.off);
+      w.b = *reinterpret_cast<const uint4*>(static_cast<const float*>(src) + pc.off + 4);
+    }
+    return w;
+  };
+  // Each thread's first piece is requested before the angles are formed, so
+  // the memory latency passes under that arithmetic (its bytes are only
+  // looked at after the barrier below).
+  // (unconditional: a thread past the end reads an in-bounds piece it does
+  // not use, so no wait below has to allow for a load that may be missing)
+  const int tf = threadIdx.x;
+  const Piece pf = locate(min(tf, tasks - 1));
+  const Raw wf = load_raw(pf);
+  const double base_t = p.omega_base[0], base_h = p.omega_base[1], base_w = p.omega_base[2];
+
   // ---- angles: one (token, pair) per thread iteration ------------------
-  const double log2_theta = log2(double(p.theta));
   const int64_t HW = int64_t(p.H) * p.W;
   for (int e = threadIdx.x; e < ntok * P; e += kRopeThreads) {
     const int tl = e / P, pr = e - tl * P;
     const int64_t row = row0 + tl;
     const int64_t i = row % p.L;
     const int64_t n = p.token0 + i;
-    int axis, j, Pa;
-    if (pr < p.pairs_t) { axis = 0; j = pr; Pa = p.pairs_t; }
-    else if (pr < p.pairs_t + p.pairs_h) { axis = 1; j = pr - p.pairs_t; Pa = p.pairs_h; }
-    else { axis = 2; j = pr - p.pairs_t - p.pairs_h; Pa = p.pairs_w; }
     int64_t pos;
-    if (axis == 0) pos = n / HW + p.t_offset;
-    else if (axis == 1) pos = (n / p.W) % p.H;
-    else pos = n % p.W;
-    const double omega = exp2(-double(j) / double(Pa) * log2_theta);
-    double ang = double(pos) * omega;
+    int j;
+    double base;
+    if (pr < p.pairs_t) { pos = n / HW + p.t_offset; j = pr; base = base_t; }
+    else if (pr < p.pairs_t + p.pairs_h) { pos = (n / p.W) % p.H; j = pr - p.pairs_t; base = base_h; }
+    else { pos = n % p.W; j = pr - p.pairs_t - p.pairs_h; base = base_w; }
+    // frequency theta^(-j / P_axis) = base^j by squaring (j < 64): within
+    // ~64 float64 ulps, far below what the float32 sine and cosine resolve
+    double om = 1.0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      if ((j >> bit) & 1) om *= base;
+      base *= base;
+    }
+    double ang = double(pos) * om;
     const double two_pi = 6.283185307179586476925286766559;
     ang -= two_pi * rint(ang / two_pi);
     // the reduced angle lies in [-pi, pi]: float32 sine and cosine suffice
@@ -66,39 +137,17 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   }
   __syncthreads();
 
-  const bool has_q = p.q_in != nullptr, has_k = p.k_in != nullptr;
-  const int rows_q = has_q ? p.Hq : 0;
-  const int rows_per_tok = rows_q + (has_k ? p.Hk : 0);
-  const int tasks = ntok * rows_per_tok * TPR;
-  const float inv_d = 1.0f / float(D);
-
-  // row index -> (token, row) without an integer division: rt < 2^16, so
-  // the float quotient, nudged by half a step, truncates exactly
-  const float inv_rpt = 1.0f / float(rows_per_tok);
-  for (int t = threadIdx.x; t < tasks; t += kRopeThreads) {
-    const int c = t % TPR;
-    const int rt = t / TPR;
-    const int tl = int((float(rt) + 0.5f) * inv_rpt);
-    const int r = rt - tl * rows_per_tok;
-    const int64_t row = row0 + tl;
-    const bool is_q = r < rows_q;
-    const int head = is_q ? r : r - rows_q;
-    const int nh = is_q ? p.Hq : p.Hk;
-    const int64_t off = (row * nh + head) * int64_t(D) + c * 8;
-    const void* src = is_q ? p.q_in : p.k_in;
-    void* dst = is_q ? p.q_out : p.k_out;
-    const float* gain = is_q ? p.q_gain : p.k_gain;
-
+  auto process = [&](const Piece& pc, const Raw& w) {
     float x[8];
     if constexpr (BF16) {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
-      unpack8(u, x);
+      unpack8(w.a, x);
     } else {
-      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
-      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off + 4);
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      x[0] = __uint_as_float(w.a.x); x[1] = __uint_as_float(w.a.y);
+      x[2] = __uint_as_float(w.a.z); x[3] = __uint_as_float(w.a.w);
+      x[4] = __uint_as_float(w.b.x); x[5] = __uint_as_float(w.b.y);
+      x[6] = __uint_as_float(w.b.z); x[7] = __uint_as_float(w.b.w);
     }
-    if (is_q ? p.norm_q : p.norm_k) {
+    if (pc.is_q ? norm_q : norm_k) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
@@ -108,26 +157,35 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= rinv;
     }
+    const float* gain = pc.is_q ? q_gain : k_gain;
     if (gain) {
-      const float4 ga = *reinterpret_cast<const float4*>(gain + c * 8);
-      const float4 gb = *reinterpret_cast<const float4*>(gain + c * 8 + 4);
+      const float4 ga = *reinterpret_cast<const float4*>(gain + pc.c * 8);
+      const float4 gb = *reinterpret_cast<const float4*>(gain + pc.c * 8 + 4);
       x[0] *= ga.x; x[1] *= ga.y; x[2] *= ga.z; x[3] *= ga.w;
       x[4] *= gb.x; x[5] *= gb.y; x[6] *= gb.z; x[7] *= gb.w;
     }
     float y[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float2 a = cs[tl * P + c * 4 + e];
+      const float2 a = cs[pc.tl * P + pc.c * 4 + e];
       const float x0 = x[2 * e], x1 = x[2 * e + 1];
       y[2 * e] = x0 * a.x - x1 * a.y;
       y[2 * e + 1] = x0 * a.y + x1 * a.x;
     }
+    void* dst = pc.is_q ? q_out : k_out;
     if constexpr (BF16) {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + off) = pack8(y);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + pc.off) = pack8(y);
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(dst) + off) = make_float4(y[0], y[1], y[2], y[3]);
-      *reinterpret_cast<float4*>(static_cast<float*>(dst) + off + 4) = make_float4(y[4], y[5], y[6], y[7]);
+      *reinterpret_cast<float4*>(static_cast<float*>(dst) + pc.off) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4*>(static_cast<float*>(dst) + pc.off + 4) = make_float4(y[4], y[5], y[6], y[7]);
     }
+  };
+  // (tasks and the block size are multiples of TPR, so the lanes of one row
+  // take the same iterations and the shuffles stay inside the row)
+  if (tf < tasks) process(pf, wf);
+  for (int t = tf + kRopeThreads; t < tasks; t += kRopeThreads) {
+    const Piece pc = locate(t);
+    process(pc, load_raw(pc));
   }
 }
 
@@ -209,12 +267,17 @@ hipError_t launch_rope(const RopeLaunch& p, hipStream_t s) {
   if (tok > kMaxRopeTok) tok = kMaxRopeTok;
   const int64_t blocks = (rows + tok - 1) / tok;
   dim3 grid(static_cast<unsigned>(blocks));
+  // per-axis frequency ratios theta^(-1 / P_axis), in float64, once per call
+  RopeLaunch q = p;
+  const double log2_theta = std::log2(double(p.theta));
+  const int pa[3] = {p.pairs_t, p.pairs_h, p.pairs_w};
+  for (int a = 0; a < 3; ++a) q.omega_base[a] = pa[a] > 0 ? std::exp2(-log2_theta / double(pa[a])) : 1.0;
   if (p.dtype == 0) {
-    if (p.D == 128) hipLaunchKernelGGL((rope_qk_kernel<128, true>), grid, dim3(kRopeThreads), 0, s, p, tok);
-    else hipLaunchKernelGGL((rope_qk_kernel<64, true>), grid, dim3(kRopeThreads), 0, s, p, tok);
+    if (p.D == 128) hipLaunchKernelGGL((rope_qk_kernel<128, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    else hipLaunchKernelGGL((rope_qk_kernel<64, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((rope_qk_kernel<128, false>), grid, dim3(kRopeThreads), 0, s, p, tok);
-    else hipLaunchKernelGGL((rope_qk_kernel<64, false>), grid, dim3(kRopeThreads), 0, s, p, tok);
+    if (p.D == 128) hipLaunchKernelGGL((rope_qk_kernel<128, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    else hipLaunchKernelGGL((rope_qk_kernel<64, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
   }
   return hipGetLastError();
 }

@@ -128,6 +128,7 @@ struct RopeLaunch {
   int32_t norm_q;  // RMSNorm the q rows before rotating them
   int32_t norm_k;  // RMSNorm the k rows before rotating them
   int32_t dtype;
+  double omega_base[3];  // theta^(-1 / P_axis) per axis t, h, w (filled by launch_rope)
 };
 hipError_t launch_rope(const RopeLaunch& p, hipStream_t s);
 
