@@ -153,10 +153,14 @@ __host__ __device__ constexpr bool pv_pairs_in_time(int npb, int db) {
 // per FLOP).  HYB: the chunk-hybrid instance (its own epilogue, and
 // wavefronts without queries -- the tail of a chunk's last block -- skip the
 // matrix work of the main loop, so their SIMD time goes to the other
-// workgroup of the CU); the other modes use the plain/ring instance.  Second
-// launch bound: workgroups per CU.
-template <int D, int NW, int QB, bool HYB>
-__global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_kernel(AttnLaunch p, int64_t total) {
+// workgroup of the CU); the other modes use the plain/ring instance.  OCC:
+// wavefronts per SIMD the registers are sized for (2, or 3 for the D = 64
+// 4-wavefront shape on calls that fit one round at three workgroups per CU:
+// at most 168 registers, a few spilled).  Second launch bound: workgroups
+// per CU.
+template <int D, int NW, int QB, bool HYB, int OCC = 2>
+__global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / NW) void attn_mfma_kernel(AttnLaunch p,
+                                                                                                         int64_t total) {
   constexpr int BM = 32 * NW * QB;  // queries per workgroup
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
@@ -1009,7 +1013,7 @@ __global__ __launch_bounds__(64 * NW, (QB == 1 ? 8 : 4) / NW) void attn_mfma_ker
   }  // HYB
 }
 
-template <int D, int NW, int QB>
+template <int D, int NW, int QB, int OCC = 2>
 hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
   const bool hyb = p.epi == kEpiHybrid;
   constexpr int BM = NW * 32 * QB;
@@ -1018,12 +1022,18 @@ hipError_t launch_cfg(const AttnLaunch& p, hipStream_t s) {
   else total = ((p.Lq + BM - 1) / BM) * p.Hq * p.B * (p.nsplit > 1 ? p.nsplit : 1);
   if (total == 0) return hipSuccess;
   if (total > 0x7fffffff) return hipErrorInvalidConfiguration;  // (the kernel's work index is 32-bit)
-  if (hyb)
+  if constexpr (OCC != 2) {
+    static_assert(D == 64 && NW == 4 && QB == 1, "three wavefronts per SIMD: the D = 64 4-wavefront shape only");
+    if (hyb) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB, false, OCC>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0,
+                       s, p, total);
+  } else if (hyb) {
     hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB, true>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p,
                        total);
-  else
+  } else {
     hipLaunchKernelGGL((attn_mfma_kernel<D, NW, QB, false>), dim3(static_cast<unsigned>(total)), dim3(64 * NW), 0, s, p,
                        total);
+  }
   return hipGetLastError();
 }
 
@@ -1102,6 +1112,12 @@ hipError_t launch_attn_bf16(const AttnLaunch& p, hipStream_t s) {
   if constexpr (VDIT_ATTN_BIG_QB == 2)
     if (wg256 >= 512) return launch_cfg<64, 4, 2>(p, s);
   if (wide) return launch_cfg<64, 8, 1>(p, s);
+  // more than one round of 4-wavefront workgroups at two per CU, but one
+  // round at three: the registers sized for three (the XL decode frame's 696
+  // workgroups: 1.36 rounds -> 1, 7% faster; larger calls, with several
+  // rounds either way, run faster at two)
+  const int64_t cus = device_cus();
+  if (p.epi != kEpiHybrid && wg128 > 2 * cus && wg128 <= 3 * cus) return launch_cfg<64, 4, 1, 3>(p, s);
   return wg128 >= 512 ? launch_cfg<64, 4, 1>(p, s) : launch_cfg<64, 2, 1>(p, s);
 }
 
