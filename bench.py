@@ -291,7 +291,7 @@ def bench_full(args):
         "rope_GBps": round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(), "kernel": "attn_mfma_kernel<128,8,1>",
+                     "traffic": measured_traffic(), "kernel": "attn_mfma_kernel<128,8,1,false,2>",
                      "algorithmic_flops_per_launch": flops},
     }
     del qr, kr, o, lse
