@@ -457,16 +457,13 @@ def bench_other(args):
         qbuf = torch.empty_like(qd[:1])
 
         def frame_step(f):
-            # one decode step of stream frame f: rotate q (KV-norm: without
-            # its norm), normalise and rotate k straight into the cache slot,
-            # values into their slot (normalised under KV-norm), then attend
+            # one decode step of stream frame f, in one launch: rotate q
+            # (KV-norm: without its norm), normalise and rotate k straight
+            # into the cache slot, values into their slot (normalised under
+            # KV-norm); then attend
             j, slot = f % w.n_frames, f % w.n_slots
-            V.vdit_rope_qk(qd[j:j + 1], kd[j:j + 1], grid, q_out=qbuf, k_out=kc[:, slot], t_offset=t_step * f,
-                           q_norm=q_norm)
-            if w.kv_norm:
-                V.vdit_rms_norm(vd[j:j + 1], out=vc[:, slot])
-            else:
-                vc[:, slot].copy_(vd[j:j + 1])
+            V.vdit_rope_qkv(qd[j:j + 1], kd[j:j + 1], vd[j:j + 1], grid, q_out=qbuf, k_out=kc[:, slot],
+                            v_out=vc[:, slot], t_offset=t_step * f, q_norm=q_norm, v_norm=w.kv_norm)
             V.vdit_attn_fwd(qbuf, mode="rolling", k_cache=kc, v_cache=vc, frame=f,
                             key_norm_max=key_norm_bound(w.head_dim))
 
@@ -478,7 +475,8 @@ def bench_other(args):
             # n_slots - 1 frames attend to fewer frames)
             for f in range(w.n_frames):
                 frame_step(f)
-        form = "decode step: rope(q), rope(k) into the cache slot, v into its slot, windowed attention"
+        form = ("decode step: one launch for rope(q), rope(k) into the cache slot and v (normalised under "
+                "KV-norm) into its slot, then windowed attention")
     elif w.mode == "hybrid":
         s = torch.zeros((1, w.kv_heads, w.head_dim, w.head_dim), device=dev)
         z = torch.zeros((1, w.kv_heads, w.head_dim), device=dev)

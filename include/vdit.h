@@ -67,7 +67,10 @@ typedef struct {
 /* vdit_rope_qk flags */
 #define VDIT_ROPE_NO_NORM 1u   /* skip the RMSNorm of q and k, rotate only */
 #define VDIT_ROPE_NO_Q_NORM 2u /* skip it for q only: k is normalised, q rotated
-                                  only (KV-norm; normalise v with vdit_rms_norm) */
+                                  only (KV-norm; normalise v with vdit_rms_norm,
+                                  or in the same launch with vdit_rope_qkv) */
+#define VDIT_ROPE_V_NORM 4u    /* vdit_rope_qkv only: RMS-normalise the values
+                                  (with v_gain) instead of copying them */
 
 /*
  * vdit_rope_qk -- fused per-head RMSNorm + 3D-RoPE of queries and keys.
@@ -96,6 +99,33 @@ vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* 
                          int32_t head_dim, vdit_dtype dtype, const vdit_grid* grid,
                          int64_t token0, int64_t t_offset, const float* q_gain,
                          const float* k_gain, float eps, uint32_t flags, hipStream_t stream);
+
+/*
+ * vdit_rope_qkv -- vdit_rope_qk plus the values of the same tokens in the
+ * same launch: a decode step's three input transforms at once.
+ *
+ * q and k are treated exactly as by vdit_rope_qk (same flags, same results
+ * bit for bit).  The values are not rotated: every v row is copied to v_out
+ * unchanged, or, with VDIT_ROPE_V_NORM, normalised as by vdit_rms_norm,
+ * y = x / sqrt(mean_d(x_d^2) + eps) * v_gain (KV-norm: FlashDecoder Sec. 3.2
+ * "Base Architecture" normalises keys and values inside attention; the same
+ * bits as vdit_rms_norm).  A rolling-cache slot of a B = 1 cache is a valid
+ * k_out and v_out, so one call fills a decode frame's two slots.
+ *
+ * v_in, v_out: [B, L, n_kv_heads, head_dim] of dtype, both set or both
+ * NULL (then this is vdit_rope_qk); v_out may equal v_in (in place) and must
+ * not overlap any other tensor of the call.  v_gain: [head_dim] float32 or
+ * NULL (gain 1), 16-byte aligned.  The other arguments as for vdit_rope_qk.
+ * One workgroup holds a token's rows: the head rows of the tensors given
+ * (n_heads for q, n_kv_heads each for k and v) times head_dim must not
+ * exceed 16384 (VDIT_ERR_UNSUPPORTED beyond; the same limit as
+ * vdit_rope_qk's).  VDIT_ROPE_V_NORM passed to vdit_rope_qk is an error.
+ */
+vdit_status vdit_rope_qkv(const void* q_in, const void* k_in, const void* v_in, void* q_out, void* k_out,
+                          void* v_out, int32_t B, int64_t L, int32_t n_heads, int32_t n_kv_heads,
+                          int32_t head_dim, vdit_dtype dtype, const vdit_grid* grid, int64_t token0,
+                          int64_t t_offset, const float* q_gain, const float* k_gain, const float* v_gain,
+                          float eps, uint32_t flags, hipStream_t stream);
 
 /*
  * vdit_rms_norm -- per-head RMSNorm without rotation, for the values of

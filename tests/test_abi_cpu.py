@@ -105,6 +105,38 @@ def test_rope_validation_errors_return_before_any_gpu_call(lib):
     assert st == V.VDIT_ERR_INVALID_ARG and "flags" in msg
 
 
+def test_rope_qkv_validation_errors_return_before_any_gpu_call(lib):
+    grid = V.make_grid(21, 30, 52, (22, 21, 21))
+    a, b, c = 1 << 24, 1 << 26, 1 << 28  # never dereferenced: validation fails first
+    nk = 100 * 12 * 128 * 2  # bytes of one [1, 100, 12, 128] bf16 tensor
+
+    def qkv(q_in, k_in, v_in, q_out, k_out, v_out, Hq=12, Hk=12, v_gain=None, flags=0):
+        return _status(lib, lib.vdit_rope_qkv, q_in, k_in, v_in, q_out, k_out, v_out, 1, 100, Hq, Hk, 128, 0,
+                       ctypes.byref(grid), 0, 0, None, None, v_gain, 1e-6, flags, None)
+    st, msg = qkv(a, b, c, a, b, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "v_in and v_out" in msg
+    st, msg = qkv(a, b, c, a, b, b + nk - 64)  # the values' output runs into the keys' output
+    assert st == V.VDIT_ERR_INVALID_ARG and "v_out overlaps" in msg
+    st, msg = qkv(a, b, c, a, b, a + 1024)  # ... into the queries
+    assert st == V.VDIT_ERR_INVALID_ARG and "v_out overlaps" in msg
+    st, msg = qkv(a, b, c, c + 4096, b, 1 << 30)  # the queries' output over the values' input
+    assert st == V.VDIT_ERR_INVALID_ARG and "overlaps v_in" in msg
+    st, msg = qkv(a, b, c, a, b, c + 512)  # values partly in place
+    assert st == V.VDIT_ERR_INVALID_ARG and "v_out partially overlaps v_in" in msg
+    st, msg = qkv(a, b, c, a, b, c, v_gain=a + 4)
+    assert st == V.VDIT_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = qkv(a, b, c, a, b, c, Hq=64, Hk=64)  # (64 + 64 + 64) x 128 rows of a token > 16384
+    assert st == V.VDIT_ERR_UNSUPPORTED and "heads per token" in msg
+    st, msg = qkv(None, None, c, None, None, c, Hk=0)
+    assert st == V.VDIT_ERR_INVALID_ARG and "n_kv_heads" in msg
+    st, msg = qkv(a, b, c, a, b, c, flags=8)
+    assert st == V.VDIT_ERR_INVALID_ARG and "flags" in msg
+    # the values' flag belongs to vdit_rope_qkv
+    st, msg = _status(lib, lib.vdit_rope_qk, a, b, a, b, 1, 100, 12, 12, 128, 0,
+                      ctypes.byref(grid), 0, 0, None, None, 1e-6, V.VDIT_ROPE_V_NORM, None)
+    assert st == V.VDIT_ERR_INVALID_ARG and "vdit_rope_qkv" in msg
+
+
 def test_rms_norm_validation_errors_return_before_any_gpu_call(lib):
     fake = 1 << 20  # never dereferenced: validation fails first
     st, msg = _status(lib, lib.vdit_rms_norm, fake, fake, 1, 100, 3, 96, 0, None, 1e-6, None)

@@ -108,6 +108,50 @@ def test_rope_without_query_norm(dtype):
     check(qo, wq, dtype, "q rotated only"); check(ko, wk, dtype, "k normalised and rotated")
 
 
+@pytest.mark.parametrize("dtype,D,pairs", [("bf16", 64, (12, 10, 10)), ("bf16", 128, (22, 21, 21)),
+                                           ("f32", 64, (12, 10, 10))])
+def test_rope_qkv_values_in_the_same_launch(dtype, D, pairs):
+    """vdit_rope_qkv: q and k as vdit_rope_qk gives them and the values
+    copied, or normalised as vdit_rms_norm gives them (the same bits), also
+    written straight into a rolling-cache slot and in place; ragged token
+    count, grouped-query heads, gains; q, k, v against the oracle."""
+    grid = (4, 9, 10)
+    B, L, Hq, Hk = 2, 337, 6, 2
+    log(f"rope qkv {dtype} D={D} B={B} L={L} Hq={Hq} Hk={Hk}")
+    q = raw((B, L, Hq, D), 41, dtype); k = raw((B, L, Hk, D), 42, dtype); v = raw((B, L, Hk, D), 43, dtype)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    g = V.make_grid(*grid, pairs)
+    gv = (1.0 + 0.1 * np.random.default_rng(44).standard_normal(D)).astype(np.float32)
+    gk = (1.0 + 0.1 * np.random.default_rng(45).standard_normal(D)).astype(np.float32)
+    gvd, gkd = torch.from_numpy(gv).cuda(), torch.from_numpy(gk).cuda()
+    # values copied: q and k exactly as vdit_rope_qk
+    q1, k1, v1 = V.vdit_rope_qkv(qd, kd, vd, g, token0=11, t_offset=5, k_gain=gkd)
+    q2, k2 = V.vdit_rope_qk(qd, kd, g, token0=11, t_offset=5, k_gain=gkd)
+    # KV-norm: q rotated only, k normalised and rotated, values normalised
+    q3, k3, v3 = V.vdit_rope_qkv(qd, kd, vd, g, token0=11, t_offset=5, q_norm=False, v_norm=True, v_gain=gvd)
+    q4, k4 = V.vdit_rope_qk(qd, kd, g, token0=11, t_offset=5, q_norm=False)
+    v4 = V.vdit_rms_norm(vd, gain=gvd)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(k1, k2), "q, k differ from vdit_rope_qk"
+    assert torch.equal(v1, vd), "copied values differ"
+    assert torch.equal(q3, q4) and torch.equal(k3, k4), "q, k differ from vdit_rope_qk (KV-norm)"
+    assert torch.equal(v3, v4), "normalised values differ from vdit_rms_norm"
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs, token0=11, t_offset=5, q_norm=False)
+    check(q3, wq, dtype, "q rotated only"); check(k3, wk, dtype, "k normalised and rotated")
+    check(v3, O.rmsnorm(v.values, 1e-6, gv), dtype, "v normalised with gain")
+    # a decode frame's two cache slots (B = 1), and values in place
+    kc = torch.zeros((1, 3, L, Hk, D), dtype=kd.dtype, device="cuda"); vc = torch.zeros_like(kc)
+    qo = torch.empty_like(qd[:1])
+    V.vdit_rope_qkv(qd[:1], kd[:1], vd[:1], g, q_out=qo, k_out=kc[:, 2], v_out=vc[:, 2], v_norm=True)
+    vin = vd[1:].clone()
+    V.vdit_rope_qkv(None, None, vin, g, v_out=vin, v_norm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, 2], V.vdit_rope_qk(None, kd[:1], g)[1]), "k in the slot"
+    assert torch.equal(vc[:, 2], V.vdit_rms_norm(vd[:1])), "v in the slot"
+    assert torch.equal(vc[:, :2], torch.zeros_like(vc[:, :2])) and torch.equal(kc[:, :2], torch.zeros_like(kc[:, :2]))
+    assert torch.equal(vin, V.vdit_rms_norm(vd[1:])), "v normalised in place"
+
+
 def test_rope_full_size_wan13b():
     w = WL.WORKLOADS[2]
     log("rope full size 32760 x 12 x 128 bf16")
@@ -256,6 +300,35 @@ def test_full_attention_bounded_and_online_softmax(D, Lq):
     for o, lse, tag in ((o_b, lse_b, "bounded"), (o_o, lse_o, "online")):
         check(from_dev(o)[:, rows], wo, "bf16", f"O ({tag}, sampled rows)")
         check_lse(from_dev(lse)[:, :, rows], wl, "bf16", f"LSE ({tag}, sampled rows)")
+
+
+def test_d64_workgroups_sized_for_three_per_cu():
+    """D = 64, 32 query heads on 8 KV heads x ceil(2500 / 128) = 640
+    workgroups of 128 queries: more than one round at two per CU on a
+    256-CU part but one round at three, so the instance whose registers are
+    sized for three wavefronts per SIMD runs.  Ragged query and key tails;
+    query rows 1000..1299 scaled by 8 so that wavefronts with and without
+    the bounded-score path share workgroups; every row against the oracle,
+    with the computed key bound and with the online maximum alone."""
+    D, Lq, Lkv, Hq, Hk = 64, 2500, 700, 32, 8
+    log(f"D=64 call of one round at three workgroups per CU: Lq={Lq} Lkv={Lkv} Hq={Hq} Hk={Hk}")
+    rng = np.random.default_rng(91)
+    q64 = rng.standard_normal((1, Lq, Hq, D))
+    q64[:, 1000:1300] *= 8.0
+    k64 = rng.standard_normal((1, Lkv, Hk, D)); v64 = rng.standard_normal((1, Lkv, Hk, D))
+
+    def bf16(x64):
+        bits = WL.f32_to_bf16_bits(x64.astype(np.float32))
+        return WL.Tensor(WL.bf16_bits_to_f64(bits), bits, "bf16")
+    q, k, v = bf16(q64), bf16(k64), bf16(v64)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o_b, lse_b = V.vdit_attn_fwd(qd, kd, vd)
+    o_o, lse_o = V.vdit_attn_fwd(qd, kd, vd, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    wo, wl = O.attention(q.values, k.values, v.values)
+    for o, lse, tag in ((o_b, lse_b, "bounded"), (o_o, lse_o, "online")):
+        check(o, wo, "bf16", f"O ({tag})")
+        check_lse(lse, wl, "bf16", f"LSE ({tag})")
 
 
 @pytest.mark.parametrize("D", [128, 64])

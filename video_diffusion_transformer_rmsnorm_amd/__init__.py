@@ -20,13 +20,14 @@ VDIT_OK, VDIT_ERR_INVALID_ARG, VDIT_ERR_UNSUPPORTED, VDIT_ERR_HIP = 0, 1, 2, 3
 VDIT_BF16, VDIT_F32 = 0, 1
 VDIT_ROPE_NO_NORM = 1
 VDIT_ROPE_NO_Q_NORM = 2
+VDIT_ROPE_V_NORM = 4
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
 ABI_VERSION = 4
 VDIT_ATTN_RING_FOLD = 1
 VDIT_ATTN_STATE_ZERO = 2
 
 # Every symbol include/vdit.h declares.
-EXPORTS = ("vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_attn_workspace_bytes",
+EXPORTS = ("vdit_rope_qk", "vdit_rope_qkv", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_attn_workspace_bytes",
            "vdit_lse_merge", "vdit_last_error", "vdit_abi_version")
 
 
@@ -83,6 +84,9 @@ def load(path: str) -> ctypes.CDLL:
     h.vdit_rope_qk.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, ctypes.POINTER(VditGrid),
                                i64, i64, vp, vp, f32, u32, vp]
     h.vdit_rope_qk.restype = ctypes.c_int
+    h.vdit_rope_qkv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, ctypes.POINTER(VditGrid),
+                                i64, i64, vp, vp, vp, f32, u32, vp]
+    h.vdit_rope_qkv.restype = ctypes.c_int
     h.vdit_rms_norm.argtypes = [vp, vp, i32, i64, i32, i32, i32, vp, f32, vp]
     h.vdit_rms_norm.restype = ctypes.c_int
     h.vdit_attn_fwd.argtypes = [ctypes.POINTER(VditAttnArgs), vp]
@@ -164,6 +168,38 @@ def vdit_rope_qk(q, k, grid: VditGrid, q_out=None, k_out=None, token0: int = 0, 
                               _dtype_code(ref), ctypes.byref(grid), token0, t_offset,
                               _ptr(q_gain), _ptr(k_gain), eps, flags, _stream(stream)))
     return q_out, k_out
+
+
+def vdit_rope_qkv(q, k, v, grid: VditGrid, q_out=None, k_out=None, v_out=None, token0: int = 0,
+                  t_offset: int = 0, q_gain=None, k_gain=None, v_gain=None, eps: float = 1e-6,
+                  norm: bool = True, q_norm: Optional[bool] = None, v_norm: bool = False, stream=None):
+    """vdit_rope_qk of q and k plus the values v [B,L,Hk,D] in the same launch:
+    v is copied to v_out, or RMS-normalised with v_gain when v_norm is set;
+    never rotated.  Outputs default to new tensors.  Returns (q_out, k_out,
+    v_out)."""
+    import torch
+    ref = q if q is not None else (k if k is not None else v)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_out, "q_out"), (k_out, "k_out"), (v_out, "v_out"),
+                 (q_gain, "q_gain"), (k_gain, "k_gain"), (v_gain, "v_gain")):
+        _dev(t, n)
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    if k is not None and k_out is None:
+        k_out = torch.empty_like(k)
+    if v is not None and v_out is None:
+        v_out = torch.empty_like(v)
+    B, L, _, D = ref.shape
+    Hq = q.shape[2] if q is not None else 0
+    Hk = k.shape[2] if k is not None else (v.shape[2] if v is not None else 0)
+    flags = 0 if norm else VDIT_ROPE_NO_NORM
+    if norm and q_norm is False:
+        flags |= VDIT_ROPE_NO_Q_NORM
+    if v_norm:
+        flags |= VDIT_ROPE_V_NORM
+    _check(lib().vdit_rope_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(q_out), _ptr(k_out), _ptr(v_out), B, L, Hq, Hk, D,
+                               _dtype_code(ref), ctypes.byref(grid), token0, t_offset,
+                               _ptr(q_gain), _ptr(k_gain), _ptr(v_gain), eps, flags, _stream(stream)))
+    return q_out, k_out, v_out
 
 
 def vdit_rms_norm(x, out=None, gain=None, eps: float = 1e-6, stream=None):
@@ -313,5 +349,5 @@ def default_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
 
 
-__all__ = ["VDIT_ATTN_RING_FOLD", "VDIT_ATTN_STATE_ZERO", "vdit_rope_qk", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
+__all__ = ["VDIT_ATTN_RING_FOLD", "VDIT_ATTN_STATE_ZERO", "VDIT_ROPE_V_NORM", "vdit_rope_qk", "vdit_rope_qkv", "vdit_rms_norm", "vdit_attn_fwd", "vdit_attn_fwd_noalloc", "vdit_lse_merge", "vdit_attn_workspace_bytes", "make_grid",
            "VditGrid", "VditAttnArgs", "VditError", "lib", "EXPORTS", "LIB_PATH"]

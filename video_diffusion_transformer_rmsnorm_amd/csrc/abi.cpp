@@ -170,21 +170,20 @@ const char* vdit_last_error(void) { return g_last_error.c_str(); }
 
 int32_t vdit_abi_version(void) { return VDIT_ABI_VERSION; }
 
-vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* k_out, int32_t B,
-                         int64_t L, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
-                         vdit_dtype dtype, const vdit_grid* grid, int64_t token0, int64_t t_offset,
-                         const float* q_gain, const float* k_gain, float eps, uint32_t flags,
-                         hipStream_t stream) {
+vdit_status vdit_rope_qkv(const void* q_in, const void* k_in, const void* v_in, void* q_out, void* k_out,
+                          void* v_out, int32_t B, int64_t L, int32_t n_heads, int32_t n_kv_heads,
+                          int32_t head_dim, vdit_dtype dtype, const vdit_grid* grid, int64_t token0,
+                          int64_t t_offset, const float* q_gain, const float* k_gain, const float* v_gain,
+                          float eps, uint32_t flags, hipStream_t stream) {
   static_assert(sizeof(vdit_grid) == sizeof(vdit::GridArgs), "vdit_grid layout mirror");
   const auto* g = reinterpret_cast<const vdit::GridArgs*>(grid);
   if (auto r = vdit::check_rope(q_in, k_in, q_out, k_out, B, L, n_heads, n_kv_heads, head_dim,
-                                int(dtype), g, token0, eps);
+                                int(dtype), g, token0, eps, v_in, v_out);
       !r)
     return from_check(r);
-  if ((q_gain && (reinterpret_cast<uintptr_t>(q_gain) & 15)) ||
-      (k_gain && (reinterpret_cast<uintptr_t>(k_gain) & 15)))
-    return fail(VDIT_ERR_INVALID_ARG, "gain pointers must be 16-byte aligned");
-  if (flags & ~uint32_t(VDIT_ROPE_NO_NORM | VDIT_ROPE_NO_Q_NORM))
+  for (const float* gp : {q_gain, k_gain, v_gain})
+    if (gp && (reinterpret_cast<uintptr_t>(gp) & 15)) return fail(VDIT_ERR_INVALID_ARG, "gain pointers must be 16-byte aligned");
+  if (flags & ~uint32_t(VDIT_ROPE_NO_NORM | VDIT_ROPE_NO_Q_NORM | VDIT_ROPE_V_NORM))
     return fail(VDIT_ERR_INVALID_ARG, "unknown rope flags");
   vdit::RopeLaunch p;
   p.q_in = q_in;
@@ -193,6 +192,9 @@ vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* 
   p.k_out = k_out;
   p.q_gain = q_gain;
   p.k_gain = k_gain;
+  p.v_in = v_in;
+  p.v_out = v_out;
+  p.v_gain = v_gain;
   p.L = L;
   p.token0 = token0;
   p.t_offset = t_offset;
@@ -210,8 +212,19 @@ vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* 
   p.eps = eps;
   p.norm_k = (flags & VDIT_ROPE_NO_NORM) ? 0 : 1;
   p.norm_q = (flags & (VDIT_ROPE_NO_NORM | VDIT_ROPE_NO_Q_NORM)) ? 0 : 1;
+  p.norm_v = (flags & VDIT_ROPE_V_NORM) ? 1 : 0;
   p.dtype = int32_t(dtype);
-  return from_hip(vdit::launch_rope(p, stream), "vdit_rope_qk launch");
+  return from_hip(vdit::launch_rope(p, stream), "rope launch");
+}
+
+vdit_status vdit_rope_qk(const void* q_in, const void* k_in, void* q_out, void* k_out, int32_t B,
+                         int64_t L, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                         vdit_dtype dtype, const vdit_grid* grid, int64_t token0, int64_t t_offset,
+                         const float* q_gain, const float* k_gain, float eps, uint32_t flags,
+                         hipStream_t stream) {
+  if (flags & VDIT_ROPE_V_NORM) return fail(VDIT_ERR_INVALID_ARG, "VDIT_ROPE_V_NORM belongs to vdit_rope_qkv");
+  return vdit_rope_qkv(q_in, k_in, nullptr, q_out, k_out, nullptr, B, L, n_heads, n_kv_heads, head_dim, dtype,
+                       grid, token0, t_offset, q_gain, k_gain, nullptr, eps, flags, stream);
 }
 
 vdit_status vdit_rms_norm(const void* x_in, void* x_out, int32_t B, int64_t L, int32_t n_heads,

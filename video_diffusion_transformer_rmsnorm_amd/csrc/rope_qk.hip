@@ -30,9 +30,19 @@ namespace vdit {
 namespace {
 
 constexpr int kRopeThreads = 256;
+
+// One of three values by a piece's kind (q, k or v), chosen on values: a
+// choice between captured references would select their addresses and keep
+// the captured locals in scratch memory.
+template <class T>
+__device__ __forceinline__ T by_kind(bool is_k, bool is_v, T q, T k, T v) {
+  return is_v ? v : (is_k ? k : q);
+}
 constexpr int kMaxRopeTok = 32;
 
-template <int D, bool BF16>
+// HAS_V: the instance that also passes values through (vdit_rope_qkv); the
+// q/k-only instance carries none of that code.
+template <int D, bool BF16, bool HAS_V>
 __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int tok_per_block) {
   constexpr int P = D / 2;
   constexpr int TPR = D / 8;  // lanes per head row
@@ -47,25 +57,30 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   // of the argument block, which would be a load from a per-lane address)
   const void* const q_in = p.q_in;
   const void* const k_in = p.k_in;
+  const void* const v_in = p.v_in;
   void* const q_out = p.q_out;
   void* const k_out = p.k_out;
+  void* const v_out = p.v_out;
   const float* const q_gain = p.q_gain;
   const float* const k_gain = p.k_gain;
+  const float* const v_gain = p.v_gain;
   const int Hq = p.Hq, Hk = p.Hk;
-  const bool norm_q = p.norm_q != 0, norm_k = p.norm_k != 0;
-  const bool has_q = q_in != nullptr, has_k = k_in != nullptr;
+  const bool norm_q = p.norm_q != 0, norm_k = p.norm_k != 0, norm_v = p.norm_v != 0;
+  const bool has_q = q_in != nullptr, has_k = k_in != nullptr, has_v = HAS_V && v_in != nullptr;
   const int rows_q = has_q ? Hq : 0;
-  const int rows_per_tok = rows_q + (has_k ? Hk : 0);
+  const int rows_qk = rows_q + (has_k ? Hk : 0);
+  const int rows_per_tok = rows_qk + (has_v ? Hk : 0);
   const int tasks = ntok * rows_per_tok * TPR;
   const float inv_d = 1.0f / float(D);
 
-  // piece t of the workgroup: 8 channels of one q or k head row.  Row index
-  // -> (token, row) without an integer division: rt < 2^16, so the float
-  // quotient, nudged by half a step, truncates exactly.
+  // piece t of the workgroup: 8 channels of one q, k or v head row (a
+  // token's rows in that order).  Row index -> (token, row) without an
+  // integer division: rt < 2^16, so the float quotient, nudged by half a
+  // step, truncates exactly.
   struct Piece {
     int64_t off;
     int tl, c;
-    bool is_q;
+    bool is_k, is_v;  // else a q row
   };
   const float inv_rpt = 1.0f / float(rows_per_tok);
   auto locate = [&](int t) {
@@ -74,9 +89,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
     const int rt = t / TPR;
     pc.tl = int((float(rt) + 0.5f) * inv_rpt);
     const int r = rt - pc.tl * rows_per_tok;
-    pc.is_q = r < rows_q;
-    const int head = pc.is_q ? r : r - rows_q;
-    const int nh = pc.is_q ? Hq : Hk;
+    pc.is_v = HAS_V && r >= rows_qk;
+    pc.is_k = !pc.is_v && r >= rows_q;
+    const int head = r - by_kind(pc.is_k, pc.is_v, 0, rows_q, rows_qk);
+    const int nh = by_kind(pc.is_k, pc.is_v, Hq, Hk, Hk);
     pc.off = ((row0 + pc.tl) * nh + head) * int64_t(D) + pc.c * 8;
     return pc;
   };
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   };
   auto load_raw = [&](const Piece& pc) {
     Raw w;
-    const void* src = pc.is_q ? q_in : k_in;
+    const void* src = by_kind(pc.is_k, pc.is_v, q_in, k_in, v_in);
     if constexpr (BF16) {
       w.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + pc.off);
       w.b = make_uint4(0, 0, 0, 0);
@@ -147,7 +163,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
       x[4] = __uint_as_float(w.b.x); x[5] = __uint_as_float(w.b.y);
       x[6] = __uint_as_float(w.b.z); x[7] = __uint_as_float(w.b.w);
     }
-    if (pc.is_q ? norm_q : norm_k) {
+    if (by_kind(pc.is_k, pc.is_v, norm_q, norm_k, norm_v)) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= rinv;
     }
-    const float* gain = pc.is_q ? q_gain : k_gain;
+    const float* gain = by_kind(pc.is_k, pc.is_v, q_gain, k_gain, v_gain);
     if (gain) {
       const float4 ga = *reinterpret_cast<const float4*>(gain + pc.c * 8);
       const float4 gb = *reinterpret_cast<const float4*>(gain + pc.c * 8 + 4);
@@ -165,14 +181,19 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
       x[4] *= gb.x; x[5] *= gb.y; x[6] *= gb.z; x[7] *= gb.w;
     }
     float y[8];
+    if (pc.is_v) {  // values are not rotated
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float2 a = cs[pc.tl * P + pc.c * 4 + e];
-      const float x0 = x[2 * e], x1 = x[2 * e + 1];
-      y[2 * e] = x0 * a.x - x1 * a.y;
-      y[2 * e + 1] = x0 * a.y + x1 * a.x;
+      for (int e = 0; e < 8; ++e) y[e] = x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 a = cs[pc.tl * P + pc.c * 4 + e];
+        const float x0 = x[2 * e], x1 = x[2 * e + 1];
+        y[2 * e] = x0 * a.x - x1 * a.y;
+        y[2 * e + 1] = x0 * a.y + x1 * a.x;
+      }
     }
-    void* dst = pc.is_q ? q_out : k_out;
+    void* dst = by_kind(pc.is_k, pc.is_v, q_out, k_out, v_out);
     if constexpr (BF16) {
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst) + pc.off) = pack8(y);
     } else {
@@ -254,8 +275,8 @@ hipError_t launch_rms_norm(const RmsNormLaunch& p, hipStream_t s) {
 
 hipError_t launch_rope(const RopeLaunch& p, hipStream_t s) {
   const int64_t rows = int64_t(p.B) * p.L;
-  if (rows == 0 || (!p.q_in && !p.k_in)) return hipSuccess;
-  const int rows_per_tok = (p.q_in ? p.Hq : 0) + (p.k_in ? p.Hk : 0);
+  if (rows == 0 || (!p.q_in && !p.k_in && !p.v_in)) return hipSuccess;
+  const int rows_per_tok = (p.q_in ? p.Hq : 0) + (p.k_in ? p.Hk : 0) + (p.v_in ? p.Hk : 0);
   const int tasks_per_tok = rows_per_tok * (p.D / 8);
   // about 1536 row pieces per workgroup, but at least ~4 workgroups per CU
   // when the call is small: each thread's pieces are loaded one after the
@@ -272,12 +293,23 @@ hipError_t launch_rope(const RopeLaunch& p, hipStream_t s) {
   const double log2_theta = std::log2(double(p.theta));
   const int pa[3] = {p.pairs_t, p.pairs_h, p.pairs_w};
   for (int a = 0; a < 3; ++a) q.omega_base[a] = pa[a] > 0 ? std::exp2(-log2_theta / double(pa[a])) : 1.0;
+  const bool v = p.v_in != nullptr;
   if (p.dtype == 0) {
-    if (p.D == 128) hipLaunchKernelGGL((rope_qk_kernel<128, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
-    else hipLaunchKernelGGL((rope_qk_kernel<64, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    if (p.D == 128) {
+      if (v) hipLaunchKernelGGL((rope_qk_kernel<128, true, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
+      else hipLaunchKernelGGL((rope_qk_kernel<128, true, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    } else {
+      if (v) hipLaunchKernelGGL((rope_qk_kernel<64, true, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
+      else hipLaunchKernelGGL((rope_qk_kernel<64, true, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    }
   } else {
-    if (p.D == 128) hipLaunchKernelGGL((rope_qk_kernel<128, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
-    else hipLaunchKernelGGL((rope_qk_kernel<64, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    if (p.D == 128) {
+      if (v) hipLaunchKernelGGL((rope_qk_kernel<128, false, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
+      else hipLaunchKernelGGL((rope_qk_kernel<128, false, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    } else {
+      if (v) hipLaunchKernelGGL((rope_qk_kernel<64, false, true>), grid, dim3(kRopeThreads), 0, s, q, tok);
+      else hipLaunchKernelGGL((rope_qk_kernel<64, false, false>), grid, dim3(kRopeThreads), 0, s, q, tok);
+    }
   }
   return hipGetLastError();
 }

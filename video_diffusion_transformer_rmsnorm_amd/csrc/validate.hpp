@@ -55,10 +55,12 @@ struct GridArgs {
   float theta;
 };
 
+// v_in / v_out: the values that vdit_rope_qkv passes through (NULL for
+// vdit_rope_qk).
 inline CheckResult check_rope(const void* q_in, const void* k_in, const void* q_out,
                               const void* k_out, int32_t B, int64_t L, int32_t Hq, int32_t Hk,
                               int32_t D, int dtype, const GridArgs* g, int64_t token0,
-                              float eps) {
+                              float eps, const void* v_in = nullptr, const void* v_out = nullptr) {
   if (auto r = check_dtype(dtype); !r) return r;
   if (auto r = check_head_dim(D); !r) return r;
   if (!g) return CheckResult::bad("grid is NULL");
@@ -67,8 +69,11 @@ inline CheckResult check_rope(const void* q_in, const void* k_in, const void* q_
     return CheckResult::bad("q_in and q_out must both be set or both be NULL");
   if ((k_in == nullptr) != (k_out == nullptr))
     return CheckResult::bad("k_in and k_out must both be set or both be NULL");
+  if ((v_in == nullptr) != (v_out == nullptr))
+    return CheckResult::bad("v_in and v_out must both be set or both be NULL");
   if (q_in && Hq <= 0) return CheckResult::bad("n_heads must be positive when q is given");
   if (k_in && Hk <= 0) return CheckResult::bad("n_kv_heads must be positive when k is given");
+  if (v_in && Hk <= 0) return CheckResult::bad("n_kv_heads must be positive when v is given");
   if (g->T <= 0 || g->H <= 0 || g->W <= 0) return CheckResult::bad("grid T, H, W must be positive");
   if (g->pairs_t < 0 || g->pairs_h < 0 || g->pairs_w < 0)
     return CheckResult::bad("rotary pair counts must be non-negative");
@@ -77,23 +82,37 @@ inline CheckResult check_rope(const void* q_in, const void* k_in, const void* q_
   if (!(g->theta > 1.0f)) return CheckResult::bad("theta must be > 1");
   if (!(eps >= 0.0f)) return CheckResult::bad("eps must be >= 0");
   if (token0 < 0) return CheckResult::bad("token0 must be >= 0");
-  // one workgroup holds a token's q and k rows: at most 2048 16-byte pieces
-  // ((n_heads + n_kv_heads) * head_dim / 8), i.e. 128 heads of dim 128
-  if ((int64_t(q_in ? Hq : 0) + (k_in ? Hk : 0)) * (D / 8) > 2048)
-    return CheckResult::unsup("too many heads per token for the rotary kernel (n_heads + n_kv_heads <= 16384 / head_dim)");
+  // one workgroup holds a token's q, k (and v) rows: at most 2048 16-byte
+  // pieces ((n_heads + n_kv_heads [+ n_kv_heads]) * head_dim / 8), i.e. 128
+  // heads of dim 128
+  if ((int64_t(q_in ? Hq : 0) + (k_in ? Hk : 0) + (v_in ? Hk : 0)) * (D / 8) > 2048)
+    return CheckResult::unsup(
+        "too many heads per token for the rotary kernel (n_heads + n_kv_heads, plus n_kv_heads with values, "
+        "<= 16384 / head_dim)");
   const int64_t cells = int64_t(g->T) * g->H * g->W;
   if (token0 + L > cells) return CheckResult::bad("token0 + L exceeds the T*H*W grid");
-  for (const void* p : {q_in, k_in, q_out, k_out})
+  for (const void* p : {q_in, k_in, q_out, k_out, v_in, v_out})
     if (p && !aligned16(p)) return CheckResult::bad("tensor pointers must be 16-byte aligned");
   const size_t es = esize(dtype);
   const size_t nq = q_in ? size_t(B) * size_t(L) * size_t(Hq) * size_t(D) * es : 0;
   const size_t nk = k_in ? size_t(B) * size_t(L) * size_t(Hk) * size_t(D) * es : 0;
+  const size_t nv = v_in ? size_t(B) * size_t(L) * size_t(Hk) * size_t(D) * es : 0;
   if (q_in && q_out != q_in && overlaps(q_in, nq, q_out, nq))
     return CheckResult::bad("q_out partially overlaps q_in");
   if (k_in && k_out != k_in && overlaps(k_in, nk, k_out, nk))
     return CheckResult::bad("k_out partially overlaps k_in");
   if (q_out && k_out && overlaps(q_out, nq, k_out, nk))
     return CheckResult::bad("q_out overlaps k_out");
+  if (v_in) {
+    // the values' output may only be the values' input itself (in place):
+    // any other overlap with a tensor of the call is rejected
+    if (v_out != v_in && overlaps(v_in, nv, v_out, nv)) return CheckResult::bad("v_out partially overlaps v_in");
+    if ((q_in && overlaps(v_out, nv, q_in, nq)) || (q_out && overlaps(v_out, nv, q_out, nq)) ||
+        (k_in && overlaps(v_out, nv, k_in, nk)) || (k_out && overlaps(v_out, nv, k_out, nk)))
+      return CheckResult::bad("v_out overlaps q or k");
+    if ((q_out && overlaps(q_out, nq, v_in, nv)) || (k_out && overlaps(k_out, nk, v_in, nv)))
+      return CheckResult::bad("q_out or k_out overlaps v_in");
+  }
   return CheckResult::good();
 }
 

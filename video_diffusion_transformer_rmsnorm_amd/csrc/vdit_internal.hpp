@@ -117,6 +117,10 @@ struct RopeLaunch {
   void* k_out;
   const float* q_gain;
   const float* k_gain;
+  const void* v_in = nullptr;    // values: copied, or RMS-normalised (norm_v), not rotated
+  void* v_out = nullptr;
+  const float* v_gain = nullptr;
+  int32_t norm_v = 0;
   int64_t L;
   int64_t token0;
   int64_t t_offset;
