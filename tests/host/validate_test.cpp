@@ -32,6 +32,17 @@ int main() {
   EXPECT(check_rope(P(0x1000), nullptr, P(0x1010), nullptr, 1, 10, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "partial overlap");
   EXPECT(check_rope(P(0x1000), nullptr, nullptr, nullptr, 1, 10, 12, 12, 128, 0, &g, 0, 1e-6f).code == Check::invalid, "q_out missing");
   EXPECT(check_rope(P(0x1000), nullptr, P(0x1000), nullptr, 1, 10, 12, 12, 128, 0, &g, 0, -1.f).code == Check::invalid, "negative eps");
+  // the values of vdit_rope_qkv (q, k at 1 GiB, 2 GiB; v at 3 GiB; one tensor is 1 x 32760 x 12 x 128 bf16)
+  EXPECT(bool(check_rope(P(1ull << 30), P(2ull << 30), P(1ull << 30), P(2ull << 30), 1, 32760, 12, 12, 128, 0, &g, 0,
+                         1e-6f, P(3ull << 30), P(3ull << 30))), "rope with values in place ok");
+  EXPECT(check_rope(P(1ull << 30), P(2ull << 30), P(1ull << 30), P(2ull << 30), 1, 32760, 12, 12, 128, 0, &g, 0,
+                    1e-6f, P(3ull << 30), nullptr).code == Check::invalid, "v_out missing");
+  EXPECT(check_rope(P(1ull << 30), P(2ull << 30), P(1ull << 30), P(2ull << 30), 1, 32760, 12, 12, 128, 0, &g, 0,
+                    1e-6f, P(3ull << 30), P((2ull << 30) + 4096)).code == Check::invalid, "v_out over k_out");
+  EXPECT(check_rope(P(1ull << 30), P(2ull << 30), P(1ull << 30), P((3ull << 30) + 64), 1, 32760, 12, 12, 128, 0, &g,
+                    0, 1e-6f, P(3ull << 30), P(4ull << 30)).code == Check::invalid, "k_out over v_in");
+  EXPECT(check_rope(P(1ull << 30), P(2ull << 30), P(1ull << 30), P(2ull << 30), 1, 10, 64, 64, 128, 0, &g, 0, 1e-6f,
+                    P(3ull << 30), P(3ull << 30)).code == Check::unsupported, "too many rows per token with values");
 
   // per-head RMSNorm (values of KV-norm attention)
   EXPECT(bool(check_rms_norm(P(0x1000), P(0x1000), 1, 3600, 3, 64, 0, nullptr, 1e-6f)), "rms norm in place ok");
