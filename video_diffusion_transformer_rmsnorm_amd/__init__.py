@@ -138,6 +138,23 @@ def _dev(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _expect(t, name, shape, dtype=None):
+    """t is None, or a tensor of exactly `shape` (and `dtype`).  The C ABI sees
+    only pointers and sizes, so tensors that disagree with the sizes it is
+    given would be read or written past their ends: such calls stop here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rank(t, name, n):
+    if t is not None and t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
 def make_grid(T: int, H: int, W: int, pairs: Sequence[int], theta: float = 10000.0) -> VditGrid:
     return VditGrid(T, H, W, pairs[0], pairs[1], pairs[2], theta)
 
@@ -152,15 +169,19 @@ def vdit_rope_qk(q, k, grid: VditGrid, q_out=None, k_out=None, token0: int = 0, 
     q_out=q / k_out=k for in-place.  Returns (q_out, k_out)."""
     import torch
     ref = q if q is not None else k
+    _rank(q, "q", 4); _rank(k, "k", 4)
+    B, L, _, D = ref.shape
+    Hq = q.shape[2] if q is not None else 0
+    Hk = k.shape[2] if k is not None else 0
+    _expect(q, "q", (B, L, Hq, D), ref.dtype); _expect(q_out, "q_out", (B, L, Hq, D), ref.dtype)
+    _expect(k, "k", (B, L, Hk, D), ref.dtype); _expect(k_out, "k_out", (B, L, Hk, D), ref.dtype)
+    _expect(q_gain, "q_gain", (D,), torch.float32); _expect(k_gain, "k_gain", (D,), torch.float32)
     for t, n in ((q, "q"), (k, "k"), (q_out, "q_out"), (k_out, "k_out"), (q_gain, "q_gain"), (k_gain, "k_gain")):
         _dev(t, n)
     if q is not None and q_out is None:
         q_out = torch.empty_like(q)
     if k is not None and k_out is None:
         k_out = torch.empty_like(k)
-    B, L, _, D = ref.shape
-    Hq = q.shape[2] if q is not None else 0
-    Hk = k.shape[2] if k is not None else 0
     flags = 0 if norm else VDIT_ROPE_NO_NORM
     if norm and q_norm is False:
         flags |= VDIT_ROPE_NO_Q_NORM
@@ -179,6 +200,15 @@ def vdit_rope_qkv(q, k, v, grid: VditGrid, q_out=None, k_out=None, v_out=None, t
     v_out)."""
     import torch
     ref = q if q is not None else (k if k is not None else v)
+    _rank(q, "q", 4); _rank(k, "k", 4); _rank(v, "v", 4)
+    B, L, _, D = ref.shape
+    Hq = q.shape[2] if q is not None else 0
+    Hk = k.shape[2] if k is not None else (v.shape[2] if v is not None else 0)
+    _expect(q, "q", (B, L, Hq, D), ref.dtype); _expect(q_out, "q_out", (B, L, Hq, D), ref.dtype)
+    _expect(k, "k", (B, L, Hk, D), ref.dtype); _expect(k_out, "k_out", (B, L, Hk, D), ref.dtype)
+    _expect(v, "v", (B, L, Hk, D), ref.dtype); _expect(v_out, "v_out", (B, L, Hk, D), ref.dtype)
+    for g, n in ((q_gain, "q_gain"), (k_gain, "k_gain"), (v_gain, "v_gain")):
+        _expect(g, n, (D,), torch.float32)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_out, "q_out"), (k_out, "k_out"), (v_out, "v_out"),
                  (q_gain, "q_gain"), (k_gain, "k_gain"), (v_gain, "v_gain")):
         _dev(t, n)
@@ -188,9 +218,6 @@ def vdit_rope_qkv(q, k, v, grid: VditGrid, q_out=None, k_out=None, v_out=None, t
         k_out = torch.empty_like(k)
     if v is not None and v_out is None:
         v_out = torch.empty_like(v)
-    B, L, _, D = ref.shape
-    Hq = q.shape[2] if q is not None else 0
-    Hk = k.shape[2] if k is not None else (v.shape[2] if v is not None else 0)
     flags = 0 if norm else VDIT_ROPE_NO_NORM
     if norm and q_norm is False:
         flags |= VDIT_ROPE_NO_Q_NORM
@@ -207,11 +234,14 @@ def vdit_rms_norm(x, out=None, gain=None, eps: float = 1e-6, stream=None):
 
     out defaults to a new tensor; out=x normalises in place.  Returns out."""
     import torch
+    _rank(x, "x", 4)
+    B, L, H, D = x.shape
+    _expect(out, "out", x.shape, x.dtype)
+    _expect(gain, "gain", (D,), torch.float32)
     for t, n in ((x, "x"), (out, "out"), (gain, "gain")):
         _dev(t, n)
     if out is None:
         out = torch.empty_like(x)
-    B, L, H, D = x.shape
     _check(lib().vdit_rms_norm(_ptr(x), _ptr(out), B, L, H, D, _dtype_code(x), _ptr(gain), eps,
                                _stream(stream)))
     return out
@@ -262,10 +292,38 @@ def vdit_attn_fwd(q, k=None, v=None, mode: str = "full", o=None, lse=None, want_
     import torch
     if phi_coef is not None and len(phi_coef) != 8:
         raise ValueError("phi_coef: 4 coefficients of phi_q, then 4 of phi_k")
+    _rank(q, "q", 4)
+    B, Lq, Hq, D = q.shape
+    _expect(o, "o", q.shape, q.dtype)
+    _expect(lse, "lse", (B, Hq, Lq), torch.float32)
+    if mode == "ring":
+        if k_chunks is None or v_chunks is None or len(k_chunks) != len(v_chunks):
+            raise ValueError("ring: k_chunks and v_chunks must be lists of the same length")
+        for i, (kc, vc) in enumerate(zip(k_chunks, v_chunks)):
+            _rank(kc, f"k_chunks[{i}]", 4)
+            _expect(kc, f"k_chunks[{i}]", (B, kc.shape[1], k_chunks[0].shape[2], D), q.dtype)
+            _expect(vc, f"v_chunks[{i}]", kc.shape, q.dtype)
+        for i, (kc, vc) in enumerate(zip(k_chunks, v_chunks)):
+            _dev(kc, f"k_chunks[{i}]"); _dev(vc, f"v_chunks[{i}]")
+    elif mode == "rolling":
+        _rank(k_cache, "k_cache", 5)
+        if k_cache is None:
+            raise ValueError("rolling: k_cache and v_cache are required")
+        _expect(k_cache, "k_cache", (B, k_cache.shape[1], Lq, k_cache.shape[3], D), q.dtype)
+        _expect(v_cache, "v_cache", k_cache.shape, q.dtype)
+        _expect(k, "k", (B, Lq, k_cache.shape[3], D), q.dtype)
+        _expect(v, "v", (B, Lq, k_cache.shape[3], D), q.dtype)
+    elif k is not None:
+        _rank(k, "k", 4)
+        _expect(k, "k", (B, k.shape[1], k.shape[2], D), q.dtype)
+        _expect(v, "v", k.shape, q.dtype)
+        if mode == "hybrid":
+            Hk = k.shape[2]
+            _expect(state_s, "state_s", (B, Hk, D, D), torch.float32)
+            _expect(state_z, "state_z", (B, Hk, D), torch.float32)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (k_cache, "k_cache"),
                  (v_cache, "v_cache"), (state_s, "state_s"), (state_z, "state_z"), (workspace, "workspace")):
         _dev(t, n)
-    B, Lq, Hq, D = q.shape
     if o is None:
         o = torch.empty_like(q)
     if lse is None and want_lse:
@@ -335,7 +393,14 @@ def vdit_attn_fwd_noalloc(q, k=None, v=None, mode: str = "full", o=None, lse=Non
 def vdit_lse_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, out_dtype=None, stream=None):
     """Merge two attention partials; returns (o_out, lse_out)."""
     import torch
+    _rank(o_a, "o_a", 4)
     B, L, H, D = o_a.shape
+    _expect(o_b, "o_b", o_a.shape, o_a.dtype)
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b"), (lse_out, "lse_out")):
+        _expect(t, n, (B, H, L), torch.float32)
+    _expect(o_out, "o_out", o_a.shape)
+    for t, n in ((o_a, "o_a"), (lse_a, "lse_a"), (o_b, "o_b"), (lse_b, "lse_b"), (o_out, "o_out"), (lse_out, "lse_out")):
+        _dev(t, n)
     if o_out is None:
         o_out = torch.empty(o_a.shape, dtype=out_dtype or o_a.dtype, device=o_a.device)
     if lse_out is None:
