@@ -7,8 +7,10 @@
  *
  * Reads <dir>/meta.txt ("L Hq Hk D T H W pairs_t pairs_h pairs_w split"),
  * <dir>/q.bin, k.bin, v.bin (bfloat16 bit patterns, [1, L, H, D]); runs
- * RMSNorm + 3D-RoPE of q and k, FULL attention, and RING attention over the
- * two key chunks [0, split) and [split, L); writes qr.bin, kr.bin (bf16),
+ * RMSNorm + 3D-RoPE of q and k (vdit_rope_qk, and vdit_rope_qkv with the
+ * values normalised in the same launch, whose q and k must equal the first
+ * call's bit for bit), FULL attention, and RING attention over the two key
+ * chunks [0, split) and [split, L); writes qr.bin, kr.bin, vn.bin (bf16),
  * o_full.bin, o_ring.bin (bf16), lse_full.bin, lse_ring.bin (float32).  It
  * also checks that an unsupported head dimension is refused with a message.
  * Exit status 0 on success.
@@ -117,6 +119,13 @@ int main(int argc, char** argv) {
   /* RMSNorm + 3D-RoPE */
   vdit_grid g = {T, H, W, pt, ph, pw, 10000.0f};
   VDIT_OK_(vdit_rope_qk(q, k, qr, kr, 1, L, Hq, Hk, D, VDIT_BF16, &g, 0, 0, NULL, NULL, 1e-6f, 0u, s));
+  /* the same, with the values normalised in the same launch */
+  void *q2, *k2, *vn;
+  HIP_OK(hipMalloc(&q2, nq * 2));
+  HIP_OK(hipMalloc(&k2, nk * 2));
+  HIP_OK(hipMalloc(&vn, nk * 2));
+  VDIT_OK_(vdit_rope_qkv(q, k, v, q2, k2, vn, 1, L, Hq, Hk, D, VDIT_BF16, &g, 0, 0, NULL, NULL, NULL, 1e-6f,
+                         VDIT_ROPE_V_NORM, s));
 
   /* FULL */
   vdit_attn_args a;
@@ -181,6 +190,27 @@ int main(int argc, char** argv) {
   }
 
   HIP_OK(hipStreamSynchronize(s));
+  /* vdit_rope_qkv's q and k are vdit_rope_qk's, bit for bit */
+  {
+    void* h1 = malloc(nq * 2);
+    void* h2 = malloc(nq * 2);
+    if (!h1 || !h2) {
+      fprintf(stderr, "out of host memory\n");
+      return 1;
+    }
+    HIP_OK(hipMemcpy(h1, qr, nq * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(h2, q2, nq * 2, hipMemcpyDeviceToHost));
+    int differ = memcmp(h1, h2, nq * 2) != 0;
+    HIP_OK(hipMemcpy(h1, kr, nk * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(h2, k2, nk * 2, hipMemcpyDeviceToHost));
+    differ |= memcmp(h1, h2, nk * 2) != 0;
+    free(h1);
+    free(h2);
+    if (differ) {
+      fprintf(stderr, "vdit_rope_qkv's q or k differ from vdit_rope_qk's\n");
+      return 1;
+    }
+  }
   int bad_io = 0;
   HIP_OK(hipMemcpy(ho, qr, nq * 2, hipMemcpyDeviceToHost));
   bad_io |= write_file(dir, "qr.bin", ho, nq * 2);
@@ -194,13 +224,15 @@ int main(int argc, char** argv) {
   bad_io |= write_file(dir, "o_ring.bin", ho, nq * 2);
   HIP_OK(hipMemcpy(hl, lse_ring, nl * 4, hipMemcpyDeviceToHost));
   bad_io |= write_file(dir, "lse_ring.bin", hl, nl * 4);
+  HIP_OK(hipMemcpy(hk, vn, nk * 2, hipMemcpyDeviceToHost));
+  bad_io |= write_file(dir, "vn.bin", hk, nk * 2);
   if (bad_io) {
     fprintf(stderr, "cannot write outputs\n");
     return 1;
   }
 
   HIP_OK(hipStreamDestroy(s));
-  void* bufs[] = {q, k, v, qr, kr, o_full, o_ring, lse_full, lse_ring, ws1, ws2};
+  void* bufs[] = {q, k, v, qr, kr, o_full, o_ring, lse_full, lse_ring, ws1, ws2, q2, k2, vn};
   for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i)
     if (bufs[i]) HIP_OK(hipFree(bufs[i]));
   free(hq);

@@ -970,7 +970,9 @@ def test_graph_capture_replays_equal_eager():
 def test_c_abi_consumer_program(tmp_path):
     # tests/host/c_consumer.c uses the library as a C program would (hipMalloc,
     # its own stream, workspace from vdit_attn_workspace_bytes, statuses):
-    # RMSNorm + 3D-RoPE, FULL and a two-chunk RING, checked against the oracle
+    # RMSNorm + 3D-RoPE (also with the values normalised in the same launch,
+    # whose q and k it compares with the first call's bit for bit), FULL and
+    # a two-chunk RING, checked against the oracle
     from video_diffusion_transformer_rmsnorm_amd import build as B
     if not os.path.exists(B.CONSUMER):
         pytest.fail(f"{B.CONSUMER} is not built (run __graft_entry__.build())")
@@ -994,6 +996,7 @@ def test_c_abi_consumer_program(tmp_path):
     check_lse(f32("lse_full.bin", (1, Hq, L)), wl, "bf16", "LSE full (C)")
     check(bf("o_ring.bin", (1, L, Hq, D)), wo, "bf16", "O ring (C)")
     check_lse(f32("lse_ring.bin", (1, Hq, L)), wl, "bf16", "LSE ring (C)")
+    check(bf("vn.bin", (1, L, Hk, D)), O.rmsnorm(v.values), "bf16", "v normalised by vdit_rope_qkv (C)")
 
 
 # ------------------------------------------------------------ randomised --
