@@ -194,21 +194,28 @@ def _up(t, dev):
 
 
 def _time_steps(step, steps: int, warmup: int):
-    """Run warmup + steps calls of step(i); returns (wall ms per step, sorted
-    per-step HIP-event ms on torch's current stream)."""
+    """Run warmup calls of step(i), then `steps` timed calls back to back,
+    nothing else on the stream between them; returns (wall ms per step of
+    those, sorted per-step HIP-event ms on torch's current stream from a
+    second pass of `steps` calls with an event pair around each).  The
+    events stay out of the first pass: on steps of ~0.1 ms their records
+    add ~10% to the wall clock."""
     import torch
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for i, e in enumerate(evs):
-        e[0].record(stream)
+    for i in range(steps):
         step(warmup + i)
-        e[1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, e in enumerate(evs):
+        e[0].record(stream)
+        step(warmup + steps + i)
+        e[1].record(stream)
+    torch.cuda.synchronize()
     return wall, sorted(a.elapsed_time(b) for a, b in evs)
 
 
@@ -413,6 +420,9 @@ def bench_other(args):
     del q, k, v
     grid = V.make_grid(*w.grid, w.pairs)
     extra = {}
+    # one scratch area for every attention call of the run, allocated once as
+    # a caller would (a workspace may be larger than a call needs)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     if w.mode == "ring":
         # the ring step as the shard receives it: per-chunk attention folded
         # into the running partial chunk by chunk (LSE merge in the epilogue);
@@ -427,10 +437,11 @@ def bench_other(args):
         knorm = key_norm_bound(w.head_dim)
 
         def step(i):
-            V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs, ring_fold=True, key_norm_max=knorm)
+            V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs, ring_fold=True, key_norm_max=knorm,
+                            workspace=ws)
 
         def step_one(i):
-            V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs, key_norm_max=knorm)
+            V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs, key_norm_max=knorm, workspace=ws)
         wall1, each1 = _time_steps(step_one, args.steps, args.warmup)
         extra["one_launch_form"] = {"ms_per_step": round(wall1, 4), "step_ms_median": round(each1[len(each1) // 2], 4),
                                     "TFLOPs": round(flops / (wall1 * 1e-3) / 1e12, 2)}
@@ -465,7 +476,7 @@ def bench_other(args):
             V.vdit_rope_qkv(qd[j:j + 1], kd[j:j + 1], vd[j:j + 1], grid, q_out=qbuf, k_out=kc[:, slot],
                             v_out=vc[:, slot], t_offset=t_step * f, q_norm=q_norm, v_norm=w.kv_norm)
             V.vdit_attn_fwd(qbuf, mode="rolling", k_cache=kc, v_cache=vc, frame=f,
-                            key_norm_max=key_norm_bound(w.head_dim))
+                            key_norm_max=key_norm_bound(w.head_dim), workspace=ws)
 
         def step(i):  # steady state: the window is full
             frame_step(w.n_slots + i)
@@ -485,7 +496,7 @@ def bench_other(args):
         knorm = key_norm_bound(w.head_dim)  # the keys come out of the RMSNorm
 
         def step(i):
-            V.vdit_attn_fwd(qr, kr, vd, mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=s, state_z=z,
+            V.vdit_attn_fwd(qr, kr, vd, mode="hybrid", chunk_tokens=w.chunk_tokens, state_s=s, state_z=z, workspace=ws,
                             overlap_tokens=w.overlap_tokens, key_norm_max=knorm, state_zero=True)
         form = "one call over the whole sequence from the zero state (delta + scan, chunk softmax + linear epilogue)"
     else:
