@@ -35,7 +35,9 @@
 extern "C" {
 #endif
 
-#define VDIT_ABI_VERSION 4
+/* 5: vdit_rope_qkv and VDIT_ROPE_V_NORM added (the earlier entry points and
+ * structs unchanged) */
+#define VDIT_ABI_VERSION 5
 
 typedef enum {
   VDIT_OK = 0,

@@ -22,7 +22,7 @@ VDIT_ROPE_NO_NORM = 1
 VDIT_ROPE_NO_Q_NORM = 2
 VDIT_ROPE_V_NORM = 4
 MODES = {"full": 0, "ring": 1, "rolling": 2, "hybrid": 3}
-ABI_VERSION = 4
+ABI_VERSION = 5
 VDIT_ATTN_RING_FOLD = 1
 VDIT_ATTN_STATE_ZERO = 2
 
