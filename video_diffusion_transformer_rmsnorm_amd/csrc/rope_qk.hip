@@ -7,20 +7,22 @@
 // head of q and k, y = x / sqrt(mean(x^2) + eps) * g, then each adjacent
 // channel pair is rotated by pos_axis * theta^(-j / P_axis).  The norm can be
 // left out for q alone (KV-norm, where the same section normalises keys and
-// values inside attention) or for both; rms_norm_kernel normalises the values.
+// values inside attention) or for both.  The values of the same tokens can
+// ride along (vdit_rope_qkv): copied, or normalised without rotation, in the
+// same launch; rms_norm_kernel normalises values on their own.
 //
 // Design (HBM-bound, one pass): a workgroup owns a few consecutive tokens.
-// Each thread first requests its first 16-byte piece of q or k, then the
+// Each thread first requests its first 16-byte piece of q, k or v, then the
 // workgroup computes cos/sin for each (token, pair) once -- the angle
 // (position times the pair's frequency, a power of a per-axis ratio that the
-// host forms in float64) is reduced modulo 2*pi in float64 so large temporal offsets keep float32
-// accuracy, then its sine and cosine are taken in float32 -- into LDS, and
-// every q and k head of those tokens reuses them.  Each lane then owns 8 channels (one 16-byte bf16 vector) of
-// one head row; the row's sum of squares is reduced across the D/8 lanes of
-// the row with cross-lane shuffles.  Loads and stores are 16-byte vectors
-// over contiguous memory, so each token's q (and k) block streams through
-// once.  In-place operation is safe: a lane reads its 8 channels before it
-// writes them.
+// host forms in float64) is reduced modulo 2*pi in float64 so large temporal
+// offsets keep float32 accuracy, then its sine and cosine are taken in
+// float32 -- into LDS, and every q and k head of those tokens reuses them.
+// Each lane then owns 8 channels (one 16-byte bf16 vector) of one head row;
+// the row's sum of squares is reduced across the D/8 lanes of the row with
+// cross-lane shuffles.  Loads and stores are 16-byte vectors over contiguous
+// memory, so each token's q, k (and v) blocks stream through once.  In-place
+// operation is safe: a lane reads its 8 channels before it writes them.
 #include <cmath>
 
 #include "device_common.hpp"
