@@ -98,3 +98,49 @@ def test_noalloc_rejects_oversized_and_caller_workspace():
     assert "workspace" in V.lib().vdit_last_error().decode()
     torch.cuda.synchronize()
     assert bool((o == 7.0).all())  # nothing was written
+
+
+def test_noalloc_step_recorded_in_a_graph():
+    """A caller that records its step into a HIP graph (the case the entry
+    point is for): RMSNorm + 3D-RoPE into persistent buffers, then the
+    no-allocation attention with its keys split in ranges whose partials
+    live in the library's scratch.  Replayed three times with eager calls of
+    another shape in between (they reuse the same scratch and leave other
+    contents in it); every replay equals the eager call bit for bit."""
+    log("noalloc: RoPE + key-split attention recorded in a graph, replayed 3 times")
+    H, D, L, Lkv = 4, 128, 1500, 1500  # 48 workgroups of 128 queries: the keys are split
+    grid, pairs = (1, 1, Lkv), (22, 21, 21)
+    q, k, v = raw((1, L, H, D), 951), raw((1, Lkv, H, D), 952), raw((1, Lkv, H, D), 953)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    g = V.make_grid(*grid, pairs)
+    qr, kr = torch.empty_like(qd), torch.empty_like(kd)
+    o_e, l_e = torch.empty_like(qd), torch.empty((1, H, L), dtype=torch.float32, device="cuda")
+    o_g, l_g = torch.empty_like(qd), torch.empty_like(l_e)
+
+    def step(o, lse):
+        V.vdit_rope_qk(qd, kd, g, q_out=qr, k_out=kr)
+        V.vdit_attn_fwd_noalloc(qr, kr, vd, o=o, lse=lse)
+
+    step(o_e, l_e)  # eager reference (also the library's first call on this device)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(o_g, l_g)  # warm-up on a side stream before the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(o_g, l_g)
+    other_q, other_k = torch.randn((1, 300, H, D), device="cuda").to(torch.bfloat16), torch.randn(
+        (1, 2000, H, D), device="cuda").to(torch.bfloat16)
+    for rep in range(3):
+        o_g.fill_(float("nan")); l_g.fill_(float("nan"))
+        V.vdit_attn_fwd_noalloc(other_q, other_k, other_k)  # eager, same scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same(o_g, o_e, f"O replay {rep}"); _same(l_g, l_e, f"LSE replay {rep}")
+    wq, wk = O.rope_qk(q.values, k.values, grid, pairs)
+    wo, wl = O.attention(wq, wk, v.values)
+    check(o_g, wo, "bf16", "O of the replayed graph"); check_lse(l_g, wl, "bf16", "LSE of the replayed graph")
