@@ -660,8 +660,10 @@ def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=Fa
 
     A step covers frame_grid = (T_step, H, W); step f's sub-frames take the
     absolute temporal positions T_step * f + s.  With kv_norm the keys are
-    normalised and rotated, the values normalised (vdit_rms_norm) and the
-    queries rotated only."""
+    normalised and rotated, the values normalised and the queries rotated
+    only.  prefill_slot: vdit_rope_qkv writes the step's keys and values
+    straight into their cache slots; else vdit_rope_qk and vdit_rms_norm give
+    them to the attention call, which inserts them."""
     F, L, H, D = qf.values.shape
     Hk = kf.values.shape[2]
     T = frame_grid[0]
@@ -673,16 +675,15 @@ def _rolling_run(qf, kf, vf, frame_grid, pairs, n_slots, frames, prefill_slot=Fa
     qn = False if kv_norm else None
     outs = {}
     for f in range(frames):
-        qr, _ = V.vdit_rope_qk(qdev[f:f + 1], None, g, t_offset=T * f, q_norm=qn)
         if prefill_slot:
+            # a decode step's inputs in one launch: q rotated, k normalised and
+            # rotated into its cache slot, v (normalised under KV-norm) into its
             slot = f % n_slots
-            V.vdit_rope_qk(None, kdev[f:f + 1], g, k_out=kc[:, slot], t_offset=T * f)
-            if kv_norm:
-                V.vdit_rms_norm(vdev[f:f + 1], out=vc[:, slot])
-            else:
-                vc[:, slot].copy_(vdev[f:f + 1])
+            qr, _, _ = V.vdit_rope_qkv(qdev[f:f + 1], kdev[f:f + 1], vdev[f:f + 1], g, k_out=kc[:, slot],
+                                       v_out=vc[:, slot], t_offset=T * f, q_norm=qn, v_norm=kv_norm)
             o, lse = V.vdit_attn_fwd(qr, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
         else:
+            qr, _ = V.vdit_rope_qk(qdev[f:f + 1], None, g, t_offset=T * f, q_norm=qn)
             _, kr = V.vdit_rope_qk(None, kdev[f:f + 1], g, t_offset=T * f)
             vr = V.vdit_rms_norm(vdev[f:f + 1]) if kv_norm else vdev[f:f + 1].contiguous()
             o, lse = V.vdit_attn_fwd(qr, kr, vr, mode="rolling", k_cache=kc, v_cache=vc, frame=f)
