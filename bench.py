@@ -193,16 +193,33 @@ def _up(t, dev):
     return torch.from_numpy(t.values.astype(np.float32)).to(dev)
 
 
-def _time_steps(step, steps: int, warmup: int):
+def _time_steps(step, steps, warmup, warm_ms: float = 100.0, timed_ms: float = 100.0):
     """Run warmup calls of step(i), then `steps` timed calls back to back,
     nothing else on the stream between them; returns (wall ms per step of
     those, sorted per-step HIP-event ms on torch's current stream from a
-    second pass of `steps` calls with an event pair around each).  The
-    events stay out of the first pass: on steps of ~0.1 ms their records
-    add ~10% to the wall clock."""
+    second pass of `steps` calls with an event pair around each, steps,
+    warmup).  The events stay out of the first pass: on steps of ~0.1 ms
+    their records add ~10% to the wall clock.
+
+    `steps` / `warmup` None: sized from the first five warm-up calls to at
+    least timed_ms of timed work (at least 50 steps) and warm_ms of warm-up
+    (at least 10 steps).  After an idle spell the clock takes milliseconds
+    to come up: with 10 warm-up steps of 0.1 ms the first 50 timed ones ran
+    15% slower than the next 50."""
     import torch
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
+    done = 0
+    if steps is None or warmup is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(5):
+            step(i)
+        torch.cuda.synchronize()
+        done = 5
+        per = max((time.perf_counter() - t0) * 1e3 / done, 1e-3)
+        warmup = max(10, done + math.ceil(warm_ms / per)) if warmup is None else warmup
+        steps = max(50, math.ceil(timed_ms / per)) if steps is None else steps
+    for i in range(done, warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -216,7 +233,7 @@ def _time_steps(step, steps: int, warmup: int):
         step(warmup + steps + i)
         e[1].record(stream)
     torch.cuda.synchronize()
-    return wall, sorted(a.elapsed_time(b) for a, b in evs)
+    return wall, sorted(a.elapsed_time(b) for a, b in evs), steps, max(warmup, done)
 
 
 def key_norm_bound(head_dim: int) -> float:
@@ -265,7 +282,7 @@ def bench_full(args):
 
     for i in range(args.warmup, args.warmup + args.steps):
         evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ms_step, _ = _time_steps(step, args.steps, args.warmup)
+    ms_step, _, _, _ = _time_steps(step, args.steps, args.warmup)
     rope_each = [e[0].elapsed_time(e[1]) for e in evs.values()]
     attn_each = sorted(e[1].elapsed_time(e[2]) for e in evs.values())
     rope_ms = sum(rope_each) / args.steps
@@ -322,7 +339,7 @@ def rope_rotated(w, qd, kd, grid, reps: int = 24):
         a, b, c, d = sets[i % nsets]
         V.vdit_rope_qk(a, b, grid, q_out=c, k_out=d)
 
-    _, each = _time_steps(step, reps, nsets)
+    _, each, _, _ = _time_steps(step, reps, nsets)
     ms = sum(each) / len(each)
     del sets
     torch.cuda.empty_cache()
@@ -442,14 +459,14 @@ def bench_other(args):
 
         def step_one(i):
             V.vdit_attn_fwd(qq, mode="ring", k_chunks=kcs, v_chunks=vcs, key_norm_max=knorm, workspace=ws)
-        wall1, each1 = _time_steps(step_one, args.steps, args.warmup)
+        wall1, each1, _, _ = _time_steps(step_one, args.steps, args.warmup)
         extra["one_launch_form"] = {"ms_per_step": round(wall1, 4), "step_ms_median": round(each1[len(each1) // 2], 4),
                                     "TFLOPs": round(flops / (wall1 * 1e-3) / 1e12, 2)}
         # vdit_lse_merge alone on the two chunks' bf16 partials (read 2 x O +
         # 2 x LSE, write O + LSE)
         parts = [V.vdit_attn_fwd(qq, kc_, vc_, key_norm_max=knorm) for kc_, vc_ in zip(kcs, vcs)]
         mo, ml = torch.empty_like(parts[0][0]), torch.empty_like(parts[0][1])
-        wall_m, each_m = _time_steps(lambda i: V.vdit_lse_merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1],
+        wall_m, each_m, _, _ = _time_steps(lambda i: V.vdit_lse_merge(parts[0][0], parts[0][1], parts[1][0], parts[1][1],
                                                                 o_out=mo, lse_out=ml), args.steps, args.warmup)
         mbytes = 3 * mo.numel() * mo.element_size() + 3 * ml.numel() * 4
         extra["lse_merge"] = {"ms_median": round(each_m[len(each_m) // 2], 4), "bytes": mbytes,
@@ -506,7 +523,7 @@ def bench_other(args):
             qr, kr = V.vdit_rope_qk(qd, kd, grid)
             V.vdit_attn_fwd(qr, kr, vd)
         form = "rope + full attention"
-    wall, each = _time_steps(step, args.steps, args.warmup)
+    wall, each, args.steps, args.warmup = _time_steps(step, args.steps, args.warmup)
     if w.mode == "rolling":
         stream()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
@@ -656,8 +673,12 @@ def kernel_stats_from(run_dir: str, workload: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50 on the 32760-token layer; on the other workloads "
+                         "as many as fill 100 ms, at least 50)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 10 on the 32760-token layer; on the other "
+                         "workloads as many as fill 100 ms, at least 10)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32760,
                     help="query rows of the oracle's timed sample (full: all rows at the default; ring: at most 4096)")
@@ -694,6 +715,9 @@ def main():
     w = WL.WORKLOADS[args.workload]
     base = None if args.no_cpu_baseline or w.mode == "full" and w.dtype != "bf16" else \
         cpu_baseline(w, args.cpu_rows)
+    if args.workload == 2:
+        args.steps = 50 if args.steps is None else args.steps
+        args.warmup = 10 if args.warmup is None else args.warmup
     out = bench_full(args) if args.workload == 2 else bench_other(args)
     out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
