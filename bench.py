@@ -626,24 +626,29 @@ def hybrid_state_bytes(w) -> dict:
     """Algorithmic HBM bytes of the chunk-hybrid's linear-attention state
     kernels for workload w (bf16, B = 1), as the benchmark's step runs them
     (from the zero state, VDIT_ATTN_STATE_ZERO): the delta pass reads K and V
-    of every token and writes one float32 dS^T, dz per (chunk, token split, kv
-    head); the scan reads those and writes S_c^T (bf16) and z_c (float32) per
-    chunk and the outgoing state."""
+    of every token that enters the state (all but the last overlap_tokens,
+    which the next call receives as context) and writes one float32 dS^T, dz
+    per (chunk, token split, kv head); the scan reads those and writes S_c^T
+    (bf16) and z_c (float32) per chunk and the outgoing state."""
     D, Hk, L = w.head_dim, w.kv_heads, w.tokens
+    Ls = L - (w.overlap_tokens or 0)
     nch = -(-L // w.chunk_tokens)
     units = nch * Hk
     ns = max(1, min(8, -(-512 // units), w.chunk_tokens // 64))
     deltas = nch * ns * Hk * (D * D + D) * 4
     state = Hk * (D * D + D) * 4
-    return {"delta": 2 * L * Hk * D * 2 + deltas,
+    return {"delta": 2 * Ls * Hk * D * 2 + deltas,
             "scan": deltas + nch * Hk * (D * D * 2 + D * 4) + state,
             "token_splits": ns}
 
 
-def kernel_stats_from(run_dir: str, workload: int):
+def kernel_stats_from(run_dir: str, workload: int, steps=None, warmup=None):
     """Per-kernel average durations of a rocprofv3 --kernel-trace --stats run of
     `bench.py --workload N` (run_kernel_stats.csv), with the algorithmic
-    rates of the attention and linear-state kernels."""
+    rates of the attention and linear-state kernels; for the decode and
+    hybrid workloads, given the run's --steps and --warmup, also the
+    averages over the timed steps' dispatches alone (run_kernel_trace.csv),
+    from which the rates are then taken."""
     import workloads as WL
     w = WL.WORKLOADS[workload]
     rows = _csv_rows(run_dir, "kernel_stats.csv")
@@ -652,9 +657,32 @@ def kernel_stats_from(run_dir: str, workload: int):
         out["kernels"][r["Name"]] = {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
                                       "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
 
+    if w.mode in ("rolling", "hybrid") and steps and warmup is not None:
+        # a decode or hybrid step launches each of its kernels once; the
+        # setup (cache fill, input rotation) and the stream runs after the
+        # timed pass use other kernel names or come later, so dispatches
+        # [warmup, warmup + steps) of each kernel are the timed pass's
+        per = {}
+        for r in sorted(_csv_rows(run_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+            per.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        win = {}
+        for name, d in per.items():
+            if len(d) >= warmup + steps:
+                t = d[warmup:warmup + steps]
+                win[name] = {"dispatches": f"{warmup}..{warmup + steps - 1}", "avg_ns": round(sum(t) / len(t), 1),
+                             "median_ns": sorted(t)[len(t) // 2]}
+        out["timed_window"] = win
+    win = out.get("timed_window", {})
+
     def avg(sub):
-        v = [x["avg_ns"] for k, x in out["kernels"].items() if sub in k]
+        v = [x["avg_ns"] for k, x in win.items() if sub in k] or \
+            [x["avg_ns"] for k, x in out["kernels"].items() if sub in k]
         return v[0] if v else None
+    if w.mode == "rolling":
+        a = avg("attn_mfma_kernel")
+        if a:
+            out["attn_TFLOPs"] = round(WL.flops_full(w.tokens, w.tokens * w.n_slots, w.heads, w.head_dim)
+                                       / a / 1e3, 1)
     if w.mode == "hybrid":
         b = hybrid_state_bytes(w)
         for name, sub in (("delta", "hybrid_delta"), ("scan", "hybrid_scan")):
@@ -702,7 +730,8 @@ def main():
         print(json.dumps(t), flush=True)
         return
     if args.kernel_stats_from:
-        print(json.dumps(kernel_stats_from(args.kernel_stats_from, args.workload)), flush=True)
+        print(json.dumps(kernel_stats_from(args.kernel_stats_from, args.workload, args.steps, args.warmup)),
+              flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
