@@ -14,8 +14,10 @@ attention kernel alone, timed with HIP events on the stream it runs on;
 is touched, over a process pool of the host's cores, one head per task).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                                 (K, W default to 50, 10)
   python bench.py --workload N   (the other workloads, one JSON line each,
-                                  with their own cpu_baseline)
+                                  with their own cpu_baseline; K and W
+                                  default to at least 100 ms of steps each)
   python bench.py --calibrate-copy | --traffic-from DIR | --kernel-stats-from DIR
 """
 from __future__ import annotations
