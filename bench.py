@@ -385,18 +385,60 @@ def mfma_peak(reps: int = 3, iters: int = 20000):
     return res
 
 
+def valu_rates(reps: int = 3, iters: int = 20000):
+    """Cost of v_exp_f32 in v_sub_f32 issue slots, from the probe kernel
+    (libvdit_probes.so): eight independent chains per thread at eight
+    wavefronts per SIMD, so that the time is the VALU issue; also an
+    exponential and a subtraction per step, to see whether the two overlap.
+    None if the probe is not built."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBES_LIB):
+        return None
+    lib = ctypes.CDLL(PROBES_LIB)
+    if not hasattr(lib, "vdit_probe_valu_rate"):
+        return None
+    lib.vdit_probe_valu_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 8 * cus  # 32 wavefronts per CU: eight per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = {}
+    for kind in (1, 0, 2):
+        best = None
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.vdit_probe_valu_rate(kind, out.data_ptr(), iters, blocks, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                return None
+            t = e0.elapsed_time(e1)
+            best = t if best is None or t < best else best
+        ms[kind] = best
+    per_simd = blocks * 4 * iters * 8 / (4 * cus)  # chain steps per SIMD
+    return {"sub_ns_per_wave_instr_per_simd": round(ms[1] * 1e6 / per_simd, 4),
+            "exp_in_sub_slots": round(ms[0] / ms[1], 3),
+            "exp_plus_sub_in_sub_slots": round(ms[2] / ms[1], 3)}
+
+
 def measured_peaks(attn_tflops: float, rope_gbps: float, reps: int = 10):
     """Reference rates measured on the same device after the timed region: the
     matrix-core probe (the ceiling of any bf16 MFMA kernel at this clock and
     power), a bf16 library GEMM (8192^3, hipBLASLt), and a 1 GiB device copy
     as the sustained HBM rate, with the attention and RoPE rates as
-    fractions of them (context for the nominal peaks in `roofline`)."""
+    fractions of them (context for the nominal peaks in `roofline`); and the
+    cost of the softmax's exponential in plain VALU issue slots."""
     import torch
     out = {}
     mp = mfma_peak()
     if mp:
         out.update({"mfma_probe_" + k: v for k, v in mp.items()})
         out["attn_frac_of_mfma_probe"] = round(attn_tflops / mp["random_operands_TFLOPs"], 4)
+    vr = valu_rates()
+    if vr:
+        out.update({"valu_probe_" + k: v for k, v in vr.items()})
     n = 8192
     a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
     b = torch.randn((n, n), device="cuda").to(torch.bfloat16)

@@ -11,6 +11,12 @@
 // the next of eight operand pairs (random data keeps switching the
 // multipliers, like attention on real-valued inputs); otherwise one pair is
 // reused.  FLOPs = blocks * 4 wavefronts * iters * 8 MFMAs * 32768.
+//
+// A second probe gives the cost of the exponential the softmax issues per
+// score relative to a plain float32 operation: eight independent chains per
+// thread of v_exp_f32 (x <- 2^-x, which stays in (0, 1]), of v_sub_f32
+// (x <- 1 - x), or of one of each per step, at eight wavefronts per SIMD so
+// that the chains' latency is hidden and the time is the VALU issue.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -49,7 +55,37 @@ __global__ __launch_bounds__(256, 2) void mfma_peak_kernel(const uint4* seed, fl
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+template <int KIND>  // 0: exponentials, 1: subtractions, 2: one of each per step
+__global__ __launch_bounds__(256) void valu_rate_kernel(float* out, int iters) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.001f * float(threadIdx.x + j);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (KIND == 0) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+      else if constexpr (KIND == 1) x[j] = 1.0f - x[j];
+      else x[j] = 1.0f - __builtin_amdgcn_exp2f(-x[j]);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
+
+// out: blocks * 256 floats on the device.  kind 0: v_exp_f32 chains, 1:
+// v_sub_f32 chains, 2: one of each per step; blocks * 4 wavefronts * iters *
+// 8 chain steps in all.  Launches on `stream`.
+extern "C" int vdit_probe_valu_rate(int kind, float* out, int iters, int blocks, hipStream_t stream) {
+  if (!out || iters <= 0 || blocks <= 0 || kind < 0 || kind > 2) return int(hipErrorInvalidValue);
+  if (kind == 0) hipLaunchKernelGGL(valu_rate_kernel<0>, dim3(blocks), dim3(256), 0, stream, out, iters);
+  else if (kind == 1) hipLaunchKernelGGL(valu_rate_kernel<1>, dim3(blocks), dim3(256), 0, stream, out, iters);
+  else hipLaunchKernelGGL(valu_rate_kernel<2>, dim3(blocks), dim3(256), 0, stream, out, iters);
+  return int(hipGetLastError());
+}
 
 // seed: 16 * 64 uint4 (bf16 operand data) on the device; out: blocks * 256
 // floats.  Launches `blocks` workgroups of 4 wavefronts on `stream`.
