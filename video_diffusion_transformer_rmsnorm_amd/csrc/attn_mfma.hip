@@ -82,6 +82,9 @@
 #ifndef VDIT_ATTN_VPREF
 #define VDIT_ATTN_VPREF 2  // V^T operand read pairs issued ahead of their MFMA
 #endif
+#ifndef VDIT_WIDE_ONE_ROUND
+#define VDIT_WIDE_ONE_ROUND 1  // 8-wavefront workgroups for calls of one nearly full round
+#endif
 #ifndef VDIT_DEBUG_SYNC
 #define VDIT_DEBUG_SYNC 0  // 1: self-check build, every pipeline stage ends on a full wait + barrier
 #endif
@@ -1062,6 +1065,9 @@ namespace {
 // time).  The wide shape is ~3% faster per FLOP: take it when at most 6% of
 // its CU-rounds would sit idle.
 bool prefer_wide(int64_t wg256, int cus) {
+  // one nearly full round (a key-split decode frame: 256 workgroups on 256
+  // CUs) has no ragged last round for the narrow shape to fill
+  if (VDIT_WIDE_ONE_ROUND && wg256 <= int64_t(cus) && wg256 * 100 >= 94 * int64_t(cus)) return true;
   if (wg256 < 2 * int64_t(cus)) return false;
   const int64_t rounds = (wg256 + cus - 1) / cus;
   const int64_t idle = rounds * cus - wg256;  // CU-rounds left empty
