@@ -116,12 +116,18 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   };
   // Each thread's first piece is requested before the angles are formed, so
   // the memory latency passes under that arithmetic (its bytes are only
-  // looked at after the barrier below).
-  // (unconditional: a thread past the end reads an in-bounds piece it does
-  // not use, so no wait below has to allow for a load that may be missing)
-  const int tf = threadIdx.x;
+  // looked at after the barrier below); in a workgroup of at most two pieces
+  // per thread (a decode frame's one-token workgroups) the second piece goes
+  // out with it, so the two latencies overlap.  (Unconditional within the
+  // workgroup: a thread past the end reads an in-bounds piece it does not
+  // use, so no wait below has to allow for a load that may be missing.)
+  const int tf = threadIdx.x, ts = tf + kRopeThreads;
+  const bool two = tasks <= 2 * kRopeThreads;  // workgroup-uniform
   const Piece pf = locate(min(tf, tasks - 1));
   const Raw wf = load_raw(pf);
+  const Piece ps = locate(min(ts, tasks - 1));
+  Raw ws;
+  if (two) ws = load_raw(ps);
   const double base_t = p.omega_base[0], base_h = p.omega_base[1], base_w = p.omega_base[2];
 
   // ---- angles: one (token, pair) per thread iteration ------------------
@@ -206,7 +212,11 @@ __global__ __launch_bounds__(kRopeThreads) void rope_qk_kernel(RopeLaunch p, int
   // (tasks and the block size are multiples of TPR, so the lanes of one row
   // take the same iterations and the shuffles stay inside the row)
   if (tf < tasks) process(pf, wf);
-  for (int t = tf + kRopeThreads; t < tasks; t += kRopeThreads) {
+  if (two) {
+    if (ts < tasks) process(ps, ws);
+    return;
+  }
+  for (int t = ts; t < tasks; t += kRopeThreads) {
     const Piece pc = locate(t);
     process(pc, load_raw(pc));
   }
