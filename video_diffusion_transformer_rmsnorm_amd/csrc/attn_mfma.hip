@@ -70,6 +70,9 @@
 #ifndef VDIT_ATTN_DOT2
 #define VDIT_ATTN_DOT2 0  // row sums by v_dot2_f32_bf16 over the packed bf16 p (slower: a serial accumulate)
 #endif
+#ifndef VDIT_ATTN_MSUM
+#define VDIT_ATTN_MSUM 1  // D = 64: row sums of P on the matrix cores (16x16x32 against a 0/1 selector)
+#endif
 #ifndef VDIT_ATTN_VEARLY
 #define VDIT_ATTN_VEARLY 4  // region A steps (from its end) over which the first V^T reads of region B are issued
 #endif
@@ -389,6 +392,30 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
   float m2[QB], lsum[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m2[qb] = -INFINITY; lsum[qb] = 0.f; }
+  // Row sums on the matrix cores (D = 64, where the VALU is the busier
+  // pipe): each packed P register (16 keys of 32 queries, the B operand of
+  // the PV product) is read as the B operand of a 16x16x32 MFMA, whose lane
+  // l supplies keys 8 (l / 16) .. + 7 of column l % 16 -- query l % 32 of
+  // the P layout, so columns mix queries n and n + 16 in alternate 8-key
+  // groups.  The 0/1 selector A[m][k] = [bit 2 of m == bit 3 of k] sums, in
+  // output rows 4i..4i+3, exactly the groups of query (l % 16) + 16 (i & 1),
+  // which is lane l's own query: every register of the accumulator then
+  // holds the lane's whole row sum (both lane halves), over every tile.
+  constexpr bool MSUM = VDIT_ATTN_MSUM != 0 && D == 64;
+  f32x4 lacc[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 msel;
+  {
+    const __bf16 one = static_cast<__bf16>((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 1.0f : 0.0f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) msel[j] = one;
+  }
+  // the row's sum of p over its keys (both lane halves)
+  auto row_total = [&](int qb) -> float {
+    if constexpr (MSUM) return lacc[qb][0];
+    else return lsum[qb] + other_half(lsum[qb]);
+  };
   const float c2 = p.scale_log2;
 
   // Bounded scores (Cauchy-Schwarz): |s_ij| <= |q_i| |k_j| <= |q_i| Kmax,
@@ -538,6 +565,7 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
         const float alpha = fast_exp2(m2[qb] - mn);
         m2[qb] = mn;
         lsum[qb] *= alpha;
+        if constexpr (MSUM) lacc[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -607,6 +635,7 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
     const __bf16 b0 = static_cast<__bf16>(e0), b1 = static_cast<__bf16>(e1);
     P[kb2][qb][hh][j] = b0;
     P[kb2][qb][hh][j + 1] = b1;
+    if constexpr (MSUM) return;  // (the row sums come from the matrix cores)
 #if VDIT_ATTN_DOT2
     // the row sum of the rounded p that the PV product uses: one v_dot2 with
     // (1, 1) per packed pair
@@ -644,8 +673,10 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
 #pragma unroll
     for (int st = 0; st < KP; ++st)
       ka[st] = *reinterpret_cast<const bf16x8*>(Kl + (st >> 1) * 32 + (st & 1) * 32 * KROWB);
+    if constexpr (!MSUM) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) run[qb] = 0.f;
+      for (int qb = 0; qb < QB; ++qb) run[qb] = 0.f;
+    }
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       if (st + KP < NSTEP) {
@@ -696,6 +727,13 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
       for (int qb = 0; qb < QB; ++qb)
         O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[st]), P[kk >> 1][qb][kk & 1],
                                                             O[db][qb], 0, 0, 0);
+      if constexpr (MSUM) {
+        if (db == DB - 1) {  // after the P register's last PV product
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(msel, P[kk >> 1][qb][kk & 1], lacc[qb], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < NPB; ++k)
         if (st > 0 && bstep(k) == st - 1) exp_finish(NPA + k, P);
@@ -716,8 +754,10 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (!MSUM) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb] += run[qb];
+      for (int qb = 0; qb < QB; ++qb) lsum[qb] += run[qb];
+    }
     if constexpr (DOMAX) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = m[qb];
@@ -827,7 +867,7 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
         if (fast && qw0 < q_end) {  // (a wave past the block's end has no rows)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const float lt = lsum[qb] + other_half(lsum[qb]);
+            const float lt = row_total(qb);
             bad = bad || !(lt >= 0x1p-64f && lt <= 0x1p64f);
           }
         }
@@ -848,6 +888,7 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
           for (int qb = 0; qb < QB; ++qb) {
             m2[qb] = -INFINITY;
             lsum[qb] = 0.f;
+            lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -894,7 +935,7 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
     const bool to_part = p.epi == kEpiRing && !p.final_out;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float lt = lsum[qb] + other_half(lsum[qb]);
+      const float lt = row_total(qb);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const float lse_s = partial_lse(m2[qb], lt);
       const int64_t q = qw0 + 32 * qb + r;
@@ -953,7 +994,7 @@ __global__ __launch_bounds__(64 * NW, OCC == 3 ? 12 / NW : (QB == 1 ? 8 : 4) / N
   if (qw0 < q_end) {  // (a wave past the end of the chunk's last block has no rows)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float lt = lsum[qb] + other_half(lsum[qb]);
+      const float lt = row_total(qb);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const float lse_s = partial_lse(m2[qb], lt);
       bf16x8 Fq[KS];
