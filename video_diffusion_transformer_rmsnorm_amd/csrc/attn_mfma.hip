@@ -42,6 +42,12 @@
 //    in log2 units with a lazy rescale: the running max only moves when a
 //    row's tile max exceeds it by more than 8 (so p <= 2^8), which skips the
 //    output rescale on almost every tile.
+//  * Row sums at D = 64 (half the MFMA work per score, so the softmax VALU
+//    work weighs twice as much): each packed P register is also the B
+//    operand of a 16x16x32 MFMA against a constant 0/1 selector that sums
+//    exactly the lane's own query, so the row sums cost four small matrix
+//    products per tile instead of 32 VALU adds.  At D = 128 the matrix
+//    cores are the busier pipe and the adds stay.
 //  * All LDS addresses are precomputed per lane; tile and buffer offsets are
 //    instruction immediates (the loop is unrolled by two over the buffer
 //    parity).  Workgroup ids are remapped so each XCD walks a contiguous
