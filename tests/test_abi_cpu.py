@@ -265,6 +265,17 @@ def test_workspace_sizes(lib):
     assert V.vdit_attn_workspace_bytes(f) == bound(1, 16) + align(2 * 2040 * 16 * 64 * 4) + align(2 * 16 * 2040 * 4)
     f.Lq, f.n_heads, f.n_kv_heads, f.head_dim, f.Lkv = 32760, 12, 12, 128, 32760
     assert V.vdit_attn_workspace_bytes(f) == bound(1, 12)
+    # several rounds of 128-query workgroups ending on a nearly empty one
+    # (14400 queries x 24 heads: 2712 workgroups, 152 in the sixth round of
+    # 512): two key ranges
+    f.Lq, f.n_heads, f.n_kv_heads, f.head_dim, f.Lkv = 14400, 24, 3, 64, 28800
+    assert V.vdit_attn_workspace_bytes(f) == bound(1, 3) + align(2 * 14400 * 24 * 64 * 4) + align(2 * 24 * 14400 * 4)
+    # ... but not a call that three workgroups per CU fit in one round
+    # (3600 queries x 24 heads: 696 workgroups), nor one with fewer keys
+    f.Lq, f.Lkv = 3600, 7200
+    assert V.vdit_attn_workspace_bytes(f) == bound(1, 3)
+    f.Lq, f.Lkv = 14400, 4096
+    assert V.vdit_attn_workspace_bytes(f) == bound(1, 3)
     f.dtype = 1  # float32: neither the bound nor the split
     assert V.vdit_attn_workspace_bytes(f) == 0
     h.head_dim = 96

@@ -218,7 +218,11 @@ inline size_t ring_workspace_bytes(const AttnArgs& a) {
 
 // Key split of FULL / ROLLING bf16 attention.  When the 128-query
 // workgroups of a call would not give each of the device's `cus` compute
-// units two of them, the keys are cut into nsplit ranges of split_keys keys
+// units two of them -- or when a call of several rounds of them would end
+// on a round at most half full (more than three per CU in all, so a call
+// that the three-per-CU shape fits in one round keeps it; at least 8192
+// keys), in which case the keys are cut in two and the rounds double with
+// a fuller last one -- the keys are cut into nsplit ranges of split_keys keys
 // (a multiple of the 64-key tile, each range at least 256 keys, at most 8
 // ranges); every range yields a float32 partial (normalised O and its LSE)
 // and a merge pass combines them.
@@ -232,8 +236,14 @@ inline SplitPlan split_plan(int dtype, int64_t B, int64_t Lq, int64_t Hq, int64_
   if (dtype != 0 || B <= 0 || Lq <= 0 || Hq <= 0 || keys <= 0 || cus <= 0) return s;
   const int64_t wg = ((Lq + 127) / 128) * Hq * B;
   const int64_t target = 2 * int64_t(cus);
-  if (wg >= target) return s;
-  int64_t n = (target + wg - 1) / wg;
+  int64_t n;
+  if (wg >= target) {
+    const int64_t rem = wg % target;  // workgroups of the last round
+    if (wg <= 3 * int64_t(cus) || rem == 0 || 2 * rem > target || keys < 8192) return s;
+    n = 2;
+  } else {
+    n = (target + wg - 1) / wg;
+  }
   if (n > 8) n = 8;
   if (n > keys / 256) n = keys / 256;
   if (n < 2) return s;
