@@ -241,10 +241,12 @@ typedef enum {
  * clobbered.  RING (with more than one chunk) and CHUNK_HYBRID require it.
  * For FULL and ROLLING it is optional: bf16 calls with too few queries to
  * occupy the device (fewer than two 128-query blocks per compute unit)
- * split the keys into up to 8 ranges whose float32 partials live in the
- * workspace and are merged with the log-sum-exp combination of
- * vdit_lse_merge; without a large enough workspace they run unsplit (same
- * result up to rounding order).
+ * split the keys into up to 8 ranges, and calls of several rounds of such
+ * blocks whose last round would be at most half full (more than three
+ * blocks per compute unit, at least 8192 keys) into two; the ranges'
+ * float32 partials live in the workspace and are merged with the
+ * log-sum-exp combination of vdit_lse_merge.  Without a large enough
+ * workspace these calls run unsplit (same result up to rounding order).
  *
  * key_norm_max: 0, or a bound the caller guarantees on the Euclidean norm of
  * every key of the call.  bf16 calls bound each query's scores by
